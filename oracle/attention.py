@@ -1,0 +1,94 @@
+"""Decode attention through a block table (oracle; test infrastructure only).
+
+[L] = "Paged Attention: OS-Inspired Memory Management for KV Caches";
+[B] = "What is PagedAttention and how does it manage KV cache?".
+
+The pages fix the result exactly: reading keys and values block by block
+through the table gives attention identical to the contiguous layout ([L],
+"How PagedAttention works", step 4; "Key takeaways": paging is exact;
+"Memory sharing across requests": the same numbers, the same outputs). So the
+oracle is that definition written out: gather the sequence's tokens through
+its table into contiguous arrays, then ordinary softmax attention of the one
+new query over all L cached tokens, in fp64.
+
+Readings the pages leave open (they are silent on these points):
+  * grouped-query heads: query head h reads KV head h // (Hq / Hkv);
+  * the scale is the caller's (1/sqrt(D) in every workload); no bias, cap or
+    window;
+  * L = 0 gives a zero output.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .cache import gather
+
+
+def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
+    """Softmax attention of one query [D] over L keys/values [L, D], in fp64.
+
+    scores = scale * K q; weights = exp(scores - max) / sum; out = weights V.
+    Subtracting the maximum changes nothing mathematically and keeps exp finite.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    if K.shape[0] == 0:
+        return np.zeros(V.shape[1], dtype=np.float64)
+    scores = float(scale) * (K @ q)
+    w = np.exp(scores - scores.max())
+    return (w @ V) / w.sum()
+
+
+def decode(query, k_pool, v_pool, block_tables, context_lens, scale) -> np.ndarray:
+    """Paged decode: out[s, h] = attention of query[s, h] over the first
+    context_lens[s] tokens of KV head h // (Hq / Hkv), read through
+    block_tables[s]. Returns fp64 [S, Hq, D].
+    """
+    S, Hq, D = query.shape
+    NB, Hkv, B, Dk = k_pool.shape
+    if Dk != D or v_pool.shape != k_pool.shape:
+        raise ValueError("shape mismatch")
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    G = Hq // Hkv
+    out = np.zeros((S, Hq, D), dtype=np.float64)
+    for s in range(S):
+        L = int(context_lens[s])
+        if L < 0 or L > block_tables.shape[1] * B:
+            raise ValueError("context length outside [0, MB * B]")
+        if L == 0:
+            continue
+        Kc = gather(k_pool, block_tables[s], L, B).astype(np.float64)
+        Vc = gather(v_pool, block_tables[s], L, B).astype(np.float64)
+        for h in range(Hq):
+            g = h // G
+            out[s, h] = attend(query[s, h], Kc[g], Vc[g], scale)
+    return out
+
+
+def attend_partial(q, K, V, scale):
+    """Unnormalised state of attention over a subset of tokens:
+    m = max score, l = sum exp(score - m), acc = sum exp(score - m) V.
+    An empty subset gives (-inf, 0, 0)."""
+    q = np.asarray(q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    if K.shape[0] == 0:
+        return -np.inf, 0.0, np.zeros(V.shape[1])
+    scores = float(scale) * (K @ q)
+    m = scores.max()
+    w = np.exp(scores - m)
+    return m, w.sum(), w @ V
+
+
+def merge_partials(parts):
+    """Combine states of disjoint token subsets into the attention output:
+    with M = max m_p, out = sum e^(m_p - M) acc_p / sum e^(m_p - M) l_p."""
+    ms = np.array([p[0] for p in parts], dtype=np.float64)
+    M = ms.max()
+    if not np.isfinite(M):
+        return np.zeros_like(parts[0][2])
+    num = sum(np.exp(m - M) * acc for m, _, acc in parts if np.isfinite(m))
+    den = sum(np.exp(m - M) * l for m, l, _ in parts if np.isfinite(m))
+    return num / den

@@ -1,0 +1,86 @@
+"""Cache contents: gather through a table, token writes, block copies
+(oracle; test infrastructure only).
+
+[L] = "Paged Attention: OS-Inspired Memory Management for KV Caches";
+[B] = "What is PagedAttention and how does it manage KV cache?".
+
+Pool layout: [NB, Hkv, B, D]. Inside one physical block and one KV head the B
+tokens sit one after another, each a row of D values ([B], "How PagedAttention
+works": tokens are contiguous within a block).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .geometry import blocks_for
+
+
+def gather(pool: np.ndarray, table_row, L: int, B: int) -> np.ndarray:
+    """The sequence's first L tokens, in logical order, as [Hkv, L, D].
+
+    Reads the blocks the table names in table order ([L], "How PagedAttention
+    works", step 4: walk the table and load each block), lays them end to end
+    and keeps the first L token rows.
+    """
+    NB, Hkv, Bp, D = pool.shape
+    if Bp != B:
+        raise ValueError("block size mismatch")
+    n = blocks_for(L, B)
+    ids = np.asarray(table_row[:n], dtype=np.int64)
+    if len(ids) < n:
+        raise ValueError("table row shorter than the context needs")
+    if n and (ids.min() < 0 or ids.max() >= NB):
+        raise ValueError("table entry outside the pool")
+    out = np.empty((Hkv, n * B, D), dtype=pool.dtype)
+    for i, b in enumerate(ids):
+        out[:, i * B:(i + 1) * B, :] = pool[b]
+    return out[:, :L, :]
+
+
+def write_kv(k_pool, v_pool, key, value, slot_mapping):
+    """Store token i's key/value rows ([Hkv, D]) at slot_mapping[i] in both pools.
+
+    Returns new pools; the inputs are not modified. A negative slot means the
+    token is not stored, and so does a slot past the pool's last slot (the
+    library skips such writes rather than touch memory outside the pool).
+    Two tokens aimed at one slot is a caller error and is rejected here.
+    ([L], "How PagedAttention works", step 2: a new token goes into the next
+    free slot of the last block, no allocation.)
+    """
+    k_out, v_out = k_pool.copy(), v_pool.copy()
+    NB, Hkv, B, D = k_pool.shape
+    slots = np.asarray(slot_mapping, dtype=np.int64)
+    valid = [int(x) for x in slots if 0 <= x < NB * B]
+    if len(valid) != len(set(valid)):
+        raise ValueError("duplicate slots in one write")
+    for i, slot in enumerate(slots):
+        slot = int(slot)
+        if slot < 0 or slot >= NB * B:
+            continue
+        blk, off = divmod(slot, B)
+        k_out[blk, :, off, :] = key[i]
+        v_out[blk, :, off, :] = value[i]
+    return k_out, v_out
+
+
+def copy_blocks(k_pool, v_pool, pairs):
+    """For each (src, dst): physical block dst becomes a copy of block src, in
+    both pools, all heads and all B slots.
+
+    Every source is read as it was before the call. Destinations must be
+    distinct and must not be sources (caller error otherwise); a pair naming a
+    block outside the pool is skipped, as the library does.
+    ([L], "Memory sharing across requests": copy-on-write gives the writer a
+    private copy of a shared block.)
+    """
+    k_out, v_out = k_pool.copy(), v_pool.copy()
+    NB = k_pool.shape[0]
+    pairs = np.asarray(pairs, dtype=np.int64).reshape(-1, 2)
+    ok = [(int(s), int(d)) for s, d in pairs if 0 <= s < NB and 0 <= d < NB]
+    dsts = [d for _, d in ok]
+    if len(dsts) != len(set(dsts)) or set(dsts) & {s for s, _ in ok}:
+        raise ValueError("copy destinations must be distinct and not sources")
+    for src, dst in ok:
+        k_out[dst] = k_pool[src]
+        v_out[dst] = v_pool[src]
+    return k_out, v_out

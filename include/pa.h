@@ -1,0 +1,204 @@
+/*
+ * pa.h — paged KV-cache decode for AMD Instinct MI355X (CDNA4, gfx950).
+ *
+ * A C ABI over hand-written HIP kernels. It implements the data path that the
+ * pages on PagedAttention describe: keys and values live in fixed-size blocks
+ * of B tokens scattered across one physical pool; each sequence's block table
+ * maps its logical blocks to physical ones; new tokens are stored into their
+ * slots; shared blocks are copied before a sequence writes into them; and
+ * decode attention reads the cache through the table, giving the same result
+ * as attention over contiguous keys and values.
+ *
+ * Sources:
+ *   [L] "Paged Attention: OS-Inspired Memory Management for KV Caches"
+ *       (modernaiengineering.com, Lesson 13.6)
+ *   [B] "What is PagedAttention and how does it manage KV cache?" (n4n.ai)
+ *
+ * ---------------------------------------------------------------------------
+ * Layout (device memory unless stated otherwise; row-major, no padding)
+ *   k_pool, v_pool  fp16 [NB][Hkv][B][D]. One (block, KV head) tile is B*D
+ *                   contiguous fp16: tokens sit one after another inside a
+ *                   block ([B], "How PagedAttention works").
+ *   block_tables    int32 [S][MB]. Entry j of row s is the physical block that
+ *                   holds tokens j*B .. j*B+B-1 of sequence s ([L], "What
+ *                   PagedAttention is"). Entries past ceil(L/B) are ignored
+ *                   (conventionally -1).
+ *   context_lens    int32 [S]. L counts every cached token of the sequence,
+ *                   including the one being decoded, whose K/V must already be
+ *                   stored at position L-1.
+ *   slot            int64 pool-wide token slot = physical_block * B + offset.
+ *   query, out      fp16 [S][Hq][D]. Query head h reads KV head h / (Hq/Hkv).
+ *
+ * Ownership and threading
+ *   The caller owns every buffer, including the decode workspace. The library
+ *   never allocates, frees or synchronises. Its only state is a thread-local
+ *   error string, so calls from several threads are safe.
+ *
+ * Ordering
+ *   Every compute call validates its arguments on the host, enqueues its
+ *   kernels on `stream` (NULL = the null stream) and returns without waiting.
+ *   Calls on one stream run in order, so pa_write_kv then pa_decode on one
+ *   stream reads the new token.
+ *
+ * Errors
+ *   Host-checked problems (null pointers, bad sizes, misalignment, unsupported
+ *   D/B/group size, a short workspace, a failed launch) return a non-zero
+ *   pa_status and set pa_last_error(); nothing is enqueued then. Device-side
+ *   data (table entries, slots, lengths) is not checked on the host; kernels
+ *   clamp or skip bad entries so that no access leaves the caller's buffers,
+ *   but the results for such inputs are unspecified.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,        /* a required pointer is NULL */
+  PA_ERR_SHAPE = 2,       /* a size is negative/zero where it must be positive, or sizes disagree */
+  PA_ERR_ALIGN = 3,       /* a pointer is not aligned as documented */
+  PA_ERR_UNSUPPORTED = 4, /* valid but not implemented: D, B or group size */
+  PA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than pa_decode_workspace_bytes */
+  PA_ERR_HIP = 6          /* the HIP runtime reported an error at launch */
+} pa_status;
+
+/* Short constant name of a status code ("PA_OK", ...). Never NULL. */
+const char* pa_status_str(int status);
+
+/* Detail of the last non-OK status returned on this thread ("" if none). */
+const char* pa_last_error(void);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int pa_version(void);
+
+/*
+ * pa_slot_mapping — where new tokens go ([L], "How PagedAttention works",
+ * steps 2-3: a new token takes the next slot of the sequence's last block;
+ * listing paged_vs_contiguous.py: token t is at offset t % B of the physical
+ * block in table entry t / B).
+ *
+ *   slot_mapping[i] = block_tables[s][t / B] * B + t % B
+ *
+ * for token i of sequence s = seq_ids[i] at position t = positions[i]. With
+ * seq_ids == NULL token i belongs to sequence i (T <= S). With positions ==
+ * NULL the position is context_lens[s] - 1, the token being decoded.
+ * slot_mapping[i] = -1 when t < 0, t / B >= MB, s outside [0, S) or the table
+ * entry is outside [0, NB); pa_write_kv skips such tokens.
+ *
+ *   slot_mapping  device int64 [T], written
+ *   block_tables  device int32 [S][MB]
+ *   seq_ids       device int32 [T] or NULL
+ *   positions     device int32 [T] or NULL
+ *   context_lens  device int32 [S]; required when positions == NULL, else ignored
+ * T = 0 is a no-op. Requires B > 0, NB > 0, MB > 0, S >= 0.
+ */
+pa_status pa_slot_mapping(int64_t* slot_mapping, const int32_t* block_tables,
+                          const int32_t* seq_ids, const int32_t* positions,
+                          const int32_t* context_lens, int T, int S, int MB, int B, int NB,
+                          hipStream_t stream);
+
+/*
+ * pa_write_kv — store each new token's key and value rows into its slot
+ * ([L], "How PagedAttention works", step 2; no allocation happens here).
+ *
+ *   k_pool[slot / B][h][slot % B][:] = key[i][h][:]   (same for v_pool/value)
+ *
+ * for every token i with 0 <= slot_mapping[i] < NB * B; other tokens are
+ * skipped. A bit copy: stored values equal the inputs exactly.
+ *
+ *   key, value        device fp16 [T][Hkv][D], 16-byte aligned
+ *   k_pool, v_pool    device fp16 [NB][Hkv][B][D], 16-byte aligned
+ *   slot_mapping      device int64 [T]
+ * D must be a positive multiple of 8; T = 0 is a no-op. Two tokens with the
+ * same slot in one call is a caller error (which one lands is unspecified).
+ */
+pa_status pa_write_kv(const void* key, const void* value, void* k_pool, void* v_pool,
+                      const int64_t* slot_mapping, int T, int Hkv, int D, int B, int NB,
+                      hipStream_t stream);
+
+/*
+ * pa_copy_blocks — copy-on-write of whole blocks ([L], "Memory sharing across
+ * requests": a sequence about to write into a block that others share first
+ * gets a private copy of it).
+ *
+ *   k_pool[dst] = k_pool[src];  v_pool[dst] = v_pool[src]   (all heads, all B slots)
+ *
+ * for each pair (src, dst) = (block_mapping[2p], block_mapping[2p+1]).
+ * Pairs with src or dst outside [0, NB) are skipped. Destinations must be
+ * distinct and must not appear as sources in the same call (caller error
+ * otherwise).
+ *
+ *   k_pool, v_pool    device fp16 [NB][Hkv][B][D], 16-byte aligned
+ *   block_mapping     device int32 [n][2]
+ * D must be a positive multiple of 8; n = 0 is a no-op.
+ */
+pa_status pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_mapping, int n,
+                         int Hkv, int D, int B, int NB, hipStream_t stream);
+
+/*
+ * pa_decode_partition_size — the context partition (in tokens) pa_decode uses
+ * for these sizes: partition_size itself when positive, otherwise the
+ * library's choice (a multiple of B that gives enough workgroups to fill the
+ * GPU). Returns -1 for invalid arguments (B <= 0, partition_size < 0 or not a
+ * multiple of B).
+ */
+int pa_decode_partition_size(int S, int Hkv, int B, int max_context_len, int partition_size);
+
+/*
+ * pa_decode_workspace_bytes — device workspace pa_decode needs: partial
+ * results of every context partition, S * Hq * ceil(max_context_len / P)
+ * * (D + 2) * 4 bytes, or 0 when one partition covers every sequence.
+ * Returns 0 for invalid arguments as well; pa_decode then reports the error.
+ */
+size_t pa_decode_workspace_bytes(int S, int Hq, int Hkv, int D, int B, int max_context_len,
+                                 int partition_size);
+
+/*
+ * pa_decode — one decode step of attention through the block table ([L],
+ * "How PagedAttention works", step 4: walk the table, load each block's keys
+ * and values, and attend exactly as over contiguous memory).
+ *
+ *   out[s][h] = sum_t softmax_t(scale * q[s][h] . K_t) * V_t,  t = 0 .. L_s - 1
+ *
+ * where K_t, V_t are token t's rows for KV head h / (Hq/Hkv), read from
+ * physical block block_tables[s][t / B] at offset t % B. fp16 inputs, fp32
+ * arithmetic, fp16 output rounded to nearest even. L_s = 0 gives zeros.
+ * Slots past L_s in the last block and blocks the table does not name are
+ * never read into the result, whatever they hold (NaN and Inf included).
+ * The summation order depends only on logical token positions, so relabelling
+ * physical blocks or sharing them between sequences leaves every output bit
+ * unchanged.
+ *
+ *   out               device fp16 [S][Hq][D], 16-byte aligned, written
+ *   query             device fp16 [S][Hq][D], 16-byte aligned
+ *   k_pool, v_pool    device fp16 [NB][Hkv][B][D], 16-byte aligned
+ *   block_tables      device int32 [S][MB]
+ *   context_lens      device int32 [S], 0 <= L_s <= min(max_context_len, MB * B)
+ *   max_context_len   host bound on every L_s (sizes the launch)
+ *   scale             softmax scale, usually 1/sqrt(D)
+ *   partition_size    tokens per context partition: 0 = library choice, else a
+ *                     positive multiple of B
+ *   workspace         device buffer of at least pa_decode_workspace_bytes(...)
+ *                     bytes, 16-byte aligned; may be NULL when that is 0
+ * Supported: D = 128; B in {16, 32}; Hq / Hkv in {1, 2, 4, 8}. S = 0 is a no-op.
+ * L_s outside the stated range is a caller error: the kernels clamp to the
+ * table and the launch, so no access leaves the buffers.
+ */
+pa_status pa_decode(void* out, const void* query, const void* k_pool, const void* v_pool,
+                    const int32_t* block_tables, const int32_t* context_lens, int S, int Hq,
+                    int Hkv, int D, int B, int NB, int MB, int max_context_len, float scale,
+                    int partition_size, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

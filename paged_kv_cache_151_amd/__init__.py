@@ -1,0 +1,141 @@
+"""Python binding of libpa.so: paged KV-cache decode on MI355X (gfx950).
+
+Argument marshalling only. Every function passes device pointers of torch
+tensors, their sizes and torch's current HIP stream to the C entry point of the
+same name (declared in include/pa.h); all work runs in the library's kernels.
+Output tensors and the decode workspace are allocated here with torch when the
+caller does not pass them. There is no fallback: importing this package fails
+when libpa.so has not been built, and every call raises PaError on a non-OK
+status.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpa.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python paged_kv_cache_151_amd/build.py`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_p = ctypes.c_void_p
+_i = ctypes.c_int
+_lib.pa_status_str.restype = ctypes.c_char_p
+_lib.pa_status_str.argtypes = [_i]
+_lib.pa_last_error.restype = ctypes.c_char_p
+_lib.pa_last_error.argtypes = []
+_lib.pa_version.restype = _i
+_lib.pa_slot_mapping.restype = _i
+_lib.pa_slot_mapping.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
+_lib.pa_write_kv.restype = _i
+_lib.pa_write_kv.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
+_lib.pa_copy_blocks.restype = _i
+_lib.pa_copy_blocks.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _p]
+_lib.pa_decode_partition_size.restype = _i
+_lib.pa_decode_partition_size.argtypes = [_i, _i, _i, _i, _i]
+_lib.pa_decode_workspace_bytes.restype = ctypes.c_size_t
+_lib.pa_decode_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i]
+_lib.pa_decode.restype = _i
+_lib.pa_decode.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i,
+                           ctypes.c_float, _i, _p, ctypes.c_size_t, _p]
+
+PA_OK = 0
+
+
+class PaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        name = _lib.pa_status_str(status).decode()
+        detail = _lib.pa_last_error().decode()
+        super().__init__(f"{fn}: {name}: {detail}")
+
+
+def _check(fn: str, status: int):
+    if status != PA_OK:
+        raise PaError(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def pa_version() -> int:
+    return _lib.pa_version()
+
+
+def pa_slot_mapping(block_tables, block_size: int, num_blocks: int, context_lens=None,
+                    seq_ids=None, positions=None, out=None, stream=None):
+    """int64 slots for new tokens (see pa_slot_mapping in include/pa.h)."""
+    S, MB = block_tables.shape
+    T = positions.shape[0] if positions is not None else (
+        seq_ids.shape[0] if seq_ids is not None else S)
+    if out is None:
+        out = torch.empty(T, dtype=torch.int64, device=block_tables.device)
+    _check("pa_slot_mapping", _lib.pa_slot_mapping(
+        _ptr(out), _ptr(block_tables), _ptr(seq_ids), _ptr(positions), _ptr(context_lens),
+        T, S, MB, block_size, num_blocks, _stream(stream)))
+    return out
+
+
+def pa_write_kv(key, value, k_pool, v_pool, slot_mapping, stream=None):
+    """Scatter key/value [T, Hkv, D] into the pools [NB, Hkv, B, D] at their slots."""
+    T, Hkv, D = key.shape
+    NB, _, B, _ = k_pool.shape
+    _check("pa_write_kv", _lib.pa_write_kv(
+        _ptr(key), _ptr(value), _ptr(k_pool), _ptr(v_pool), _ptr(slot_mapping),
+        T, Hkv, D, B, NB, _stream(stream)))
+
+
+def pa_copy_blocks(k_pool, v_pool, block_mapping, stream=None):
+    """Copy whole blocks src -> dst for each row of block_mapping [n, 2] (int32)."""
+    NB, Hkv, B, D = k_pool.shape
+    n = block_mapping.shape[0]
+    _check("pa_copy_blocks", _lib.pa_copy_blocks(
+        _ptr(k_pool), _ptr(v_pool), _ptr(block_mapping), n, Hkv, D, B, NB, _stream(stream)))
+
+
+def pa_decode_partition_size(S, Hkv, B, max_context_len, partition_size=0) -> int:
+    return _lib.pa_decode_partition_size(S, Hkv, B, max_context_len, partition_size)
+
+
+def pa_decode_workspace_bytes(S, Hq, Hkv, D, B, max_context_len, partition_size=0) -> int:
+    return _lib.pa_decode_workspace_bytes(S, Hq, Hkv, D, B, max_context_len, partition_size)
+
+
+def pa_decode(query, k_pool, v_pool, block_tables, context_lens, max_context_len: int,
+              scale: float, partition_size: int = 0, out=None, workspace=None, stream=None):
+    """Paged decode attention; returns out fp16 [S, Hq, D]."""
+    S, Hq, D = query.shape
+    NB, Hkv, B, _ = k_pool.shape
+    MB = block_tables.shape[1]
+    if out is None:
+        out = torch.empty_like(query)
+    need = pa_decode_workspace_bytes(S, Hq, Hkv, D, B, max_context_len, partition_size)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("pa_decode", _lib.pa_decode(
+        _ptr(out), _ptr(query), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+        _ptr(context_lens), S, Hq, Hkv, D, B, NB, MB, int(max_context_len), float(scale),
+        int(partition_size), _ptr(workspace), ws_bytes, _stream(stream)))
+    return out
+
+
+__all__ = ["PaError", "lib", "LIB_PATH", "pa_version", "pa_slot_mapping", "pa_write_kv",
+           "pa_copy_blocks", "pa_decode_partition_size", "pa_decode_workspace_bytes",
+           "pa_decode"]

@@ -1,0 +1,216 @@
+// C ABI of the paged KV-cache library: host-side validation, launch sizing,
+// error reporting. Declared in include/pa.h.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <cmath>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+pa_status fail(pa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+pa_status ok() {
+  g_err[0] = '\0';
+  return PA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+pa_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_str(int status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_NULL: return "PA_ERR_NULL";
+    case PA_ERR_SHAPE: return "PA_ERR_SHAPE";
+    case PA_ERR_ALIGN: return "PA_ERR_ALIGN";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE";
+    case PA_ERR_HIP: return "PA_ERR_HIP";
+    default: return "PA_ERR_UNKNOWN";
+  }
+}
+
+const char* pa_last_error(void) { return g_err; }
+
+int pa_version(void) { return 100; }
+
+pa_status pa_slot_mapping(int64_t* slot_mapping, const int32_t* block_tables,
+                          const int32_t* seq_ids, const int32_t* positions,
+                          const int32_t* context_lens, int T, int S, int MB, int B, int NB,
+                          hipStream_t stream) {
+  if (T < 0 || S < 0) return fail(PA_ERR_SHAPE, "pa_slot_mapping: T=%d S=%d must be >= 0", T, S);
+  if (B <= 0 || NB <= 0 || MB <= 0)
+    return fail(PA_ERR_SHAPE, "pa_slot_mapping: B=%d NB=%d MB=%d must be > 0", B, NB, MB);
+  if (!seq_ids && T > S)
+    return fail(PA_ERR_SHAPE, "pa_slot_mapping: T=%d > S=%d needs seq_ids", T, S);
+  if ((int64_t)NB * B > ((int64_t)1 << 62))
+    return fail(PA_ERR_SHAPE, "pa_slot_mapping: pool too large");
+  if (T == 0) return ok();
+  if (!slot_mapping || !block_tables)
+    return fail(PA_ERR_NULL, "pa_slot_mapping: slot_mapping and block_tables are required");
+  if (!positions && !context_lens)
+    return fail(PA_ERR_NULL, "pa_slot_mapping: need positions or context_lens");
+  if (!aligned(slot_mapping, 8) || !aligned(block_tables, 4) || !aligned(seq_ids, 4) ||
+      !aligned(positions, 4) || !aligned(context_lens, 4))
+    return fail(PA_ERR_ALIGN, "pa_slot_mapping: misaligned index buffer");
+  return hip_status(pa::launch_slot_mapping(slot_mapping, block_tables, seq_ids, positions,
+                                            context_lens, T, S, MB, B, NB, stream),
+                    "pa_slot_mapping launch");
+}
+
+pa_status pa_write_kv(const void* key, const void* value, void* k_pool, void* v_pool,
+                      const int64_t* slot_mapping, int T, int Hkv, int D, int B, int NB,
+                      hipStream_t stream) {
+  if (T < 0) return fail(PA_ERR_SHAPE, "pa_write_kv: T=%d must be >= 0", T);
+  if (Hkv <= 0 || D <= 0 || B <= 0 || NB <= 0)
+    return fail(PA_ERR_SHAPE, "pa_write_kv: Hkv=%d D=%d B=%d NB=%d must be > 0", Hkv, D, B, NB);
+  if (D % 8) return fail(PA_ERR_UNSUPPORTED, "pa_write_kv: D=%d must be a multiple of 8", D);
+  if ((int64_t)T * Hkv * (D / 8) >= ((int64_t)1 << 40))
+    return fail(PA_ERR_SHAPE, "pa_write_kv: too many tokens");
+  if (T == 0) return ok();
+  if (!key || !value || !k_pool || !v_pool || !slot_mapping)
+    return fail(PA_ERR_NULL, "pa_write_kv: null pointer argument");
+  if (!aligned(key, 16) || !aligned(value, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16))
+    return fail(PA_ERR_ALIGN, "pa_write_kv: key/value/pools must be 16-byte aligned");
+  if (!aligned(slot_mapping, 8)) return fail(PA_ERR_ALIGN, "pa_write_kv: slot_mapping misaligned");
+  return hip_status(pa::launch_write_kv(key, value, k_pool, v_pool, slot_mapping, T, Hkv, D, B,
+                                        NB, stream),
+                    "pa_write_kv launch");
+}
+
+pa_status pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_mapping, int n,
+                         int Hkv, int D, int B, int NB, hipStream_t stream) {
+  if (n < 0) return fail(PA_ERR_SHAPE, "pa_copy_blocks: n=%d must be >= 0", n);
+  if (Hkv <= 0 || D <= 0 || B <= 0 || NB <= 0)
+    return fail(PA_ERR_SHAPE, "pa_copy_blocks: Hkv=%d D=%d B=%d NB=%d must be > 0", Hkv, D, B,
+                NB);
+  if (D % 8) return fail(PA_ERR_UNSUPPORTED, "pa_copy_blocks: D=%d must be a multiple of 8", D);
+  if (n == 0) return ok();
+  if (!k_pool || !v_pool || !block_mapping)
+    return fail(PA_ERR_NULL, "pa_copy_blocks: null pointer argument");
+  if (!aligned(k_pool, 16) || !aligned(v_pool, 16))
+    return fail(PA_ERR_ALIGN, "pa_copy_blocks: pools must be 16-byte aligned");
+  if (!aligned(block_mapping, 4)) return fail(PA_ERR_ALIGN, "pa_copy_blocks: mapping misaligned");
+  // the y grid dimension carries the pair index; split very long lists
+  const int kMaxY = 65535;
+  for (int off = 0; off < n; off += kMaxY) {
+    const int cnt = n - off < kMaxY ? n - off : kMaxY;
+    hipError_t e = pa::launch_copy_blocks(k_pool, v_pool, block_mapping + 2 * (int64_t)off, cnt,
+                                          Hkv, D, B, NB, stream);
+    if (e != hipSuccess) return hip_status(e, "pa_copy_blocks launch");
+  }
+  return ok();
+}
+
+int pa_decode_partition_size(int S, int Hkv, int B, int max_context_len, int partition_size) {
+  if (B <= 0 || partition_size < 0 || (partition_size > 0 && partition_size % B)) return -1;
+  if (partition_size > 0) return partition_size;
+  // Default: 32 blocks of 16 tokens (512), halved while the launch would give
+  // fewer than 4 workgroups per compute unit (256 CUs), down to 4 blocks.
+  int P = 32 * B < 512 ? 32 * B : 512;
+  if (P < B) P = B;
+  const int64_t units = (int64_t)(S > 0 ? S : 1) * (Hkv > 0 ? Hkv : 1);
+  const int maxL = max_context_len > 0 ? max_context_len : 1;
+  while (P > 4 * B && units * ceil_div(maxL, P) < 1024) P /= 2;
+  return P;
+}
+
+size_t pa_decode_workspace_bytes(int S, int Hq, int Hkv, int D, int B, int max_context_len,
+                                 int partition_size) {
+  const int P = pa_decode_partition_size(S, Hkv, B, max_context_len, partition_size);
+  if (P <= 0 || S <= 0 || Hq <= 0 || D <= 0 || max_context_len <= 0) return 0;
+  const int64_t Pmax = ceil_div(max_context_len, P);
+  if (Pmax <= 1) return 0;
+  return (size_t)S * Hq * Pmax * (D + 2) * sizeof(float);
+}
+
+pa_status pa_decode(void* out, const void* query, const void* k_pool, const void* v_pool,
+                    const int32_t* block_tables, const int32_t* context_lens, int S, int Hq,
+                    int Hkv, int D, int B, int NB, int MB, int max_context_len, float scale,
+                    int partition_size, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
+  if (S < 0) return fail(PA_ERR_SHAPE, "pa_decode: S=%d must be >= 0", S);
+  if (Hq <= 0 || Hkv <= 0 || D <= 0 || B <= 0 || NB <= 0 || MB <= 0)
+    return fail(PA_ERR_SHAPE, "pa_decode: Hq=%d Hkv=%d D=%d B=%d NB=%d MB=%d must be > 0", Hq,
+                Hkv, D, B, NB, MB);
+  if (Hq % Hkv) return fail(PA_ERR_SHAPE, "pa_decode: Hq=%d not a multiple of Hkv=%d", Hq, Hkv);
+  if ((int64_t)MB * B >= ((int64_t)1 << 31))
+    return fail(PA_ERR_SHAPE, "pa_decode: MB*B=%lld exceeds int32", (long long)MB * B);
+  if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)MB * B)
+    return fail(PA_ERR_SHAPE, "pa_decode: max_context_len=%d outside [0, MB*B=%lld]",
+                max_context_len, (long long)MB * B);
+  if (partition_size < 0 || (partition_size > 0 && partition_size % B))
+    return fail(PA_ERR_SHAPE, "pa_decode: partition_size=%d must be 0 or a multiple of B=%d",
+                partition_size, B);
+  const int G = Hq / Hkv;
+  if (D != pa::kHeadDim) return fail(PA_ERR_UNSUPPORTED, "pa_decode: D=%d (supported: 128)", D);
+  if (B != 16 && B != 32) return fail(PA_ERR_UNSUPPORTED, "pa_decode: B=%d (supported: 16, 32)", B);
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode: Hq/Hkv=%d (supported: 1, 2, 4, 8)", G);
+  if (!std::isfinite(scale)) return fail(PA_ERR_SHAPE, "pa_decode: scale is not finite");
+  if (S == 0) return ok();
+  if (!out || !query || !k_pool || !v_pool || !block_tables || !context_lens)
+    return fail(PA_ERR_NULL, "pa_decode: null pointer argument");
+  if (!aligned(out, 16) || !aligned(query, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16))
+    return fail(PA_ERR_ALIGN, "pa_decode: out/query/pools must be 16-byte aligned");
+  if (!aligned(block_tables, 4) || !aligned(context_lens, 4))
+    return fail(PA_ERR_ALIGN, "pa_decode: block_tables/context_lens misaligned");
+
+  const int P = pa_decode_partition_size(S, Hkv, B, max_context_len, partition_size);
+  const int Pmax = max_context_len > 0 ? ceil_div(max_context_len, P) : 1;
+  if (Pmax > pa::kMaxPartitions)
+    return fail(PA_ERR_SHAPE, "pa_decode: %d partitions exceed %d", Pmax, pa::kMaxPartitions);
+  const int64_t wgs = (int64_t)Pmax * S * Hkv;
+  if (wgs * pa::kDecodeWaves * 64 >= ((int64_t)1 << 32) || (int64_t)S * Hq >= ((int64_t)1 << 31))
+    return fail(PA_ERR_SHAPE, "pa_decode: launch too large (%lld workgroups)", (long long)wgs);
+  const size_t need = pa_decode_workspace_bytes(S, Hq, Hkv, D, B, max_context_len, P);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(PA_ERR_WORKSPACE, "pa_decode: workspace %zu bytes < %zu needed", workspace_bytes,
+                  need);
+    if (!aligned(workspace, 16)) return fail(PA_ERR_ALIGN, "pa_decode: workspace misaligned");
+  }
+
+  pa::DecodeArgs a;
+  a.out = static_cast<_Float16*>(out);
+  a.q = static_cast<const _Float16*>(query);
+  a.k_pool = static_cast<const _Float16*>(k_pool);
+  a.v_pool = static_cast<const _Float16*>(v_pool);
+  a.tables = block_tables;
+  a.lens = context_lens;
+  float* ws = static_cast<float*>(workspace);
+  a.part_acc = need > 0 ? ws : nullptr;
+  a.part_ml = need > 0 ? ws + (size_t)S * Hq * Pmax * D : nullptr;
+  a.S = S;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.NB = NB;
+  a.MB = MB;
+  a.P = P;
+  a.Pmax = Pmax;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  return hip_status(pa::launch_decode(a, B, G, stream), "pa_decode launch");
+}
+
+}  // extern "C"

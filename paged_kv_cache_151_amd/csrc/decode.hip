@@ -1,0 +1,379 @@
+// Paged decode attention for gfx950: split-context partition kernel plus a
+// log-sum-exp reduce across partitions.
+//
+// [L] "Paged Attention: OS-Inspired Memory Management for KV Caches",
+//     "How PagedAttention works", step 4: walk the block table, load each
+//     block's keys and values, attend exactly as over contiguous memory.
+// [B] "What is PagedAttention and how does it manage KV cache?",
+//     "How PagedAttention works": two-level indirection (table -> block,
+//     tokens contiguous inside the block) keeps the loads coalesced.
+//
+// Work decomposition. One workgroup of 4 waves per (sequence s, KV head g,
+// context partition p). A partition is P consecutive tokens (P a multiple of
+// B), so it covers whole blocks. Wave w takes the partition's blocks w, w+4,
+// w+8, ... . Inside a wave, lane = 16 * r + c: DPP row r (0..3) holds tokens
+// 4i + r of the block (i = 0 .. B/4-1) and lane c of the row holds dims
+// 8c .. 8c+7, so each 16-byte load of a row reads 256 contiguous bytes and a
+// wave-wide load reads 1 KiB of one contiguous 4 KiB (B = 16) K or V tile.
+//
+// q.K: 4 dot2 per lane, then a sum over the 16 lanes of the DPP row (four
+// DPP adds). Softmax: every lane keeps an online (max, sum) for the tokens of
+// its row, in the log2 domain (scores are pre-multiplied by scale * log2 e,
+// exponentials are exp2). P.V: fp32 FMA of p with the fp16 V row chunk. At the
+// end the 4 rows of a wave merge by cross-row shuffles, the 4 waves merge in
+// LDS; a single-partition sequence writes fp16 output directly, otherwise the
+// unnormalised partial (max, sum, acc[D]) goes to the workspace for the
+// reduce kernel.
+//
+// Exact masking: tokens at or past L only occur in a sequence's last block;
+// that block takes a masked path that selects (never multiplies) so NaN or
+// Inf in unused slots cannot reach the result. Arithmetic order depends only
+// on logical positions, so physical ids never change an output bit.
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kNegBig = -1.0e30f;   // "no token yet" running max; exp2 of it is 0
+
+__device__ __forceinline__ float dpp_row_sum(float x) {
+  // quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror:
+  // after the four steps every lane of the 16-lane row holds the row's sum.
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1,
+                                                             0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E,
+                                                             0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141,
+                                                             0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140,
+                                                             0xF, 0xF, false));
+  return x;
+}
+
+__device__ __forceinline__ float dot8(const uint4& a, const uint4& b) {
+  float s = 0.f;
+  s = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a.x), __builtin_bit_cast(half2_t, b.x), s, false);
+  s = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a.y), __builtin_bit_cast(half2_t, b.y), s, false);
+  s = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a.z), __builtin_bit_cast(half2_t, b.z), s, false);
+  s = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a.w), __builtin_bit_cast(half2_t, b.w), s, false);
+  return s;
+}
+
+__device__ __forceinline__ float lo_f(uint32_t u) {
+  return (float)__builtin_bit_cast(half2_t, u).x;
+}
+__device__ __forceinline__ float hi_f(uint32_t u) {
+  return (float)__builtin_bit_cast(half2_t, u).y;
+}
+
+// acc[0..7] += p * v (8 fp16 values in a uint4), fp32 FMA
+__device__ __forceinline__ void fma8(float* acc, float p, const uint4& v) {
+  acc[0] = __builtin_fmaf(p, lo_f(v.x), acc[0]);
+  acc[1] = __builtin_fmaf(p, hi_f(v.x), acc[1]);
+  acc[2] = __builtin_fmaf(p, lo_f(v.y), acc[2]);
+  acc[3] = __builtin_fmaf(p, hi_f(v.y), acc[3]);
+  acc[4] = __builtin_fmaf(p, lo_f(v.z), acc[4]);
+  acc[5] = __builtin_fmaf(p, hi_f(v.z), acc[5]);
+  acc[6] = __builtin_fmaf(p, lo_f(v.w), acc[6]);
+  acc[7] = __builtin_fmaf(p, hi_f(v.w), acc[7]);
+}
+
+template <int B>
+struct Tile {
+  static constexpr int R = B / 4;   // token rows per lane per block
+  uint4 k[R];
+  uint4 v[R];
+};
+
+template <int B>
+__device__ __forceinline__ void load_tile(Tile<B>& t, const _Float16* __restrict__ kp,
+                                          const _Float16* __restrict__ vp, int64_t base,
+                                          int lane_off) {
+#pragma unroll
+  for (int i = 0; i < Tile<B>::R; ++i) {
+    const int64_t o = base + i * (4 * kHeadDim) + lane_off;
+    t.k[i] = *reinterpret_cast<const uint4*>(kp + o);
+    t.v[i] = *reinterpret_cast<const uint4*>(vp + o);
+  }
+}
+
+// Online-softmax update of one lane's state for the block in `t`.
+// tok_base = logical position of the block's token 0 for this lane's row
+// (i.e. block_start + r); with MASK, tokens at or past `L` are excluded by
+// selection.
+template <int B, int G, bool MASK>
+__device__ __forceinline__ void process_tile(const Tile<B>& t, const uint4 (&q)[G],
+                                             float (&m)[G], float (&l)[G], float (&acc)[G][8],
+                                             float scale_log2, int tok_base, int L) {
+  constexpr int R = Tile<B>::R;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float sc[R];
+    float mx = m[h];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      sc[i] = dpp_row_sum(dot8(q[h], t.k[i])) * scale_log2;
+      if (MASK) {
+        const bool valid = (tok_base + 4 * i) < L;
+        sc[i] = valid ? sc[i] : kNegBig;
+      }
+      mx = __builtin_fmaxf(mx, sc[i]);
+    }
+    const float alpha = __builtin_amdgcn_exp2f(m[h] - mx);
+    m[h] = mx;
+    float lsum = l[h] * alpha;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) acc[h][d] *= alpha;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      float p = __builtin_amdgcn_exp2f(sc[i] - mx);
+      if (MASK) {
+        const bool valid = (tok_base + 4 * i) < L;
+        if (valid) {
+          lsum += p;
+          fma8(acc[h], p, t.v[i]);
+        }
+      } else {
+        lsum += p;
+        fma8(acc[h], p, t.v[i]);
+      }
+    }
+    l[h] = lsum;
+  }
+}
+
+// Merge state (mo, lo, acco) into (m, l, acc).
+__device__ __forceinline__ void merge_state(float& m, float& l, float* acc, float mo, float lo,
+                                            const float* acco) {
+  const float mx = __builtin_fmaxf(m, mo);
+  const float a = __builtin_amdgcn_exp2f(m - mx);
+  const float b = __builtin_amdgcn_exp2f(mo - mx);
+  m = mx;
+  l = l * a + lo * b;
+#pragma unroll
+  for (int d = 0; d < 8; ++d) acc[d] = acc[d] * a + acco[d] * b;
+}
+
+template <int B, int G>
+__global__ __launch_bounds__(kDecodeWaves * 64) void decode_partition_kernel(const DecodeArgs a) {
+  constexpr int NW = kDecodeWaves;
+  constexpr int D = kHeadDim;
+  __shared__ float s_acc[NW][G][D];
+  __shared__ float s_ml[NW][G][2];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane >> 4;
+  const int c = lane & 15;
+
+  // blockIdx -> (p, s, g) with g fastest: consecutive workgroups go to
+  // consecutive XCDs, so every workgroup of one KV head lands on the same XCD
+  // when Hkv is a multiple of 8 (shared prefix blocks stay in one L2).
+  int id = blockIdx.x;
+  const int g = id % a.Hkv;
+  id /= a.Hkv;
+  const int s = id % a.S;
+  const int p = id / a.S;
+
+  int L = a.lens[s];
+  L = L < 0 ? 0 : L;
+  L = L > a.MB * B ? a.MB * B : L;
+  L = L > a.Pmax * a.P ? a.Pmax * a.P : L;
+  const int tok0 = p * a.P;
+  const int hq0 = g * G;
+  if (tok0 >= L) {
+    if (p == 0) {  // empty sequence: zero output
+      for (int e = threadIdx.x; e < G * D; e += NW * 64) {
+        a.out[((int64_t)s * a.Hq + hq0 + e / D) * D + (e % D)] = (_Float16)0.f;
+      }
+    }
+    return;
+  }
+  const int nparts = (L + a.P - 1) / a.P;
+  const int tok1 = tok0 + a.P < L ? tok0 + a.P : L;
+  const int blk0 = tok0 / B;
+  const int nblk = (tok1 - tok0 + B - 1) / B;
+  const int n_full = (tok1 - tok0) / B;  // blocks with every slot valid
+
+  uint4 q[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    q[h] = *reinterpret_cast<const uint4*>(a.q + ((int64_t)s * a.Hq + hq0 + h) * D + 8 * c);
+  }
+  float m[G], l[G], acc[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = kNegBig;
+    l[h] = 0.f;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) acc[h][d] = 0.f;
+  }
+
+  const int32_t* trow = a.tables + (int64_t)s * a.MB + blk0;
+  const int lane_off = r * D + 8 * c;
+  const int64_t head_stride = (int64_t)B * D;
+
+  // Blocks are walked in chunks of 64: one lane holds one table entry of the
+  // chunk and v_readlane hands the wave its entry, so no table access sits
+  // inside the pipelined loop (a partition of at most 64 blocks, the default,
+  // is a single chunk). Inside a chunk the loads of the wave's next block are
+  // issued before the current block is computed. The loads are unconditional
+  // (past the wave's last block they re-read the current one, an L2 hit) so
+  // that the compiler's wait counts stay partial. Only the partition's final
+  // block can be partial; it takes the masked update. A table entry outside
+  // the pool is clamped to block 0 (no access leaves the pool; the result for
+  // such input is unspecified).
+  for (int cb = 0; cb < nblk; cb += 64) {
+    const int ce = cb + 64 < nblk ? cb + 64 : nblk;
+    const int tbl = cb + lane < ce ? trow[cb + lane] : -1;
+    auto locate = [&](int jj) -> int64_t {
+      const int phys = __builtin_amdgcn_readlane(tbl, jj - cb);
+      const int safe = (unsigned)phys < (unsigned)a.NB ? phys : 0;
+      return ((int64_t)safe * a.Hkv + g) * head_stride;
+    };
+    int j = cb + wave;
+    if (j >= ce) continue;
+    Tile<B> t0, t1;
+    load_tile<B>(t0, a.k_pool, a.v_pool, locate(j), lane_off);
+    while (true) {
+      int jn = j + NW;
+      load_tile<B>(t1, a.k_pool, a.v_pool, locate(jn < ce ? jn : j), lane_off);
+      if (j < n_full) {
+        process_tile<B, G, false>(t0, q, m, l, acc, a.scale_log2, 0, 0);
+      } else {
+        process_tile<B, G, true>(t0, q, m, l, acc, a.scale_log2, tok0 + j * B + r, L);
+      }
+      if (jn >= ce) break;
+      j = jn;
+      jn = j + NW;
+      load_tile<B>(t0, a.k_pool, a.v_pool, locate(jn < ce ? jn : j), lane_off);
+      if (j < n_full) {
+        process_tile<B, G, false>(t1, q, m, l, acc, a.scale_log2, 0, 0);
+      } else {
+        process_tile<B, G, true>(t1, q, m, l, acc, a.scale_log2, tok0 + j * B + r, L);
+      }
+      if (jn >= ce) break;
+      j = jn;
+    }
+  }
+
+  // merge the four rows of the wave (lanes c, c+16, c+32, c+48)
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+#pragma unroll
+    for (int x = 16; x <= 32; x *= 2) {
+      const float mo = __shfl_xor(m[h], x);
+      const float lo = __shfl_xor(l[h], x);
+      float ao[8];
+#pragma unroll
+      for (int d = 0; d < 8; ++d) ao[d] = __shfl_xor(acc[h][d], x);
+      merge_state(m[h], l[h], acc[h], mo, lo, ao);
+    }
+  }
+  if (r == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+      for (int d = 0; d < 8; ++d) s_acc[wave][h][8 * c + d] = acc[h][d];
+      if (c == 0) {
+        s_ml[wave][h][0] = m[h];
+        s_ml[wave][h][1] = l[h];
+      }
+    }
+  }
+  __syncthreads();
+
+  // combine the waves: thread e handles output element (h, d)
+  for (int e = threadIdx.x; e < G * D; e += NW * 64) {
+    const int h = e / D;
+    const int d = e % D;
+    float mx = s_ml[0][h][0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) mx = __builtin_fmaxf(mx, s_ml[w][h][0]);
+    float lsum = 0.f, num = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float f = __builtin_amdgcn_exp2f(s_ml[w][h][0] - mx);
+      lsum += f * s_ml[w][h][1];
+      num += f * s_acc[w][h][d];
+    }
+    const int hq = hq0 + h;
+    if (nparts == 1) {
+      const float o = lsum > 0.f ? num / lsum : 0.f;
+      a.out[((int64_t)s * a.Hq + hq) * D + d] = (_Float16)o;
+    } else {
+      const int64_t row = ((int64_t)s * a.Hq + hq) * a.Pmax + p;
+      a.part_acc[row * D + d] = num;
+      if (d == 0) {
+        a.part_ml[row * 2] = mx;
+        a.part_ml[row * 2 + 1] = lsum;
+      }
+    }
+  }
+}
+
+// One wave per (s, hq): out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
+// Sequences that fit one partition were finished by the partition kernel.
+__global__ __launch_bounds__(64) void decode_reduce_kernel(const DecodeArgs a, int B_MB) {
+  constexpr int D = kHeadDim;
+  const int hq = blockIdx.x % a.Hq;
+  const int s = blockIdx.x / a.Hq;
+  int L = a.lens[s];
+  L = L < 0 ? 0 : L;
+  L = L > B_MB ? B_MB : L;
+  int np = (L + a.P - 1) / a.P;
+  np = np > a.Pmax ? a.Pmax : np;
+  if (np <= 1) return;
+  const int64_t row0 = ((int64_t)s * a.Hq + hq) * a.Pmax;
+  float mx = kNegBig;
+  for (int p = 0; p < np; ++p) mx = __builtin_fmaxf(mx, a.part_ml[(row0 + p) * 2]);
+  float den = 0.f, n0 = 0.f, n1 = 0.f;
+  const int d = 2 * threadIdx.x;
+  for (int p = 0; p < np; ++p) {
+    const float f = __builtin_amdgcn_exp2f(a.part_ml[(row0 + p) * 2] - mx);
+    den += f * a.part_ml[(row0 + p) * 2 + 1];
+    const float2 v = *reinterpret_cast<const float2*>(a.part_acc + (row0 + p) * D + d);
+    n0 += f * v.x;
+    n1 += f * v.y;
+  }
+  _Float16* o = a.out + ((int64_t)s * a.Hq + hq) * D + d;
+  o[0] = (_Float16)(den > 0.f ? n0 / den : 0.f);
+  o[1] = (_Float16)(den > 0.f ? n1 / den : 0.f);
+}
+
+template <int B, int G>
+hipError_t launch_partition(const DecodeArgs& a, hipStream_t stream) {
+  const int64_t grid = (int64_t)a.Pmax * a.S * a.Hkv;
+  decode_partition_kernel<B, G><<<(unsigned)grid, kDecodeWaves * 64, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+template <int B>
+hipError_t launch_partition_g(const DecodeArgs& a, int G, hipStream_t stream) {
+  switch (G) {
+    case 1: return launch_partition<B, 1>(a, stream);
+    case 2: return launch_partition<B, 2>(a, stream);
+    case 4: return launch_partition<B, 4>(a, stream);
+    case 8: return launch_partition<B, 8>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, int B, int G, hipStream_t stream) {
+  hipError_t e;
+  switch (B) {
+    case 16: e = launch_partition_g<16>(a, G, stream); break;
+    case 32: e = launch_partition_g<32>(a, G, stream); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess || a.Pmax <= 1) return e;
+  const int64_t grid = (int64_t)a.S * a.Hq;
+  decode_reduce_kernel<<<(unsigned)grid, 64, 0, stream>>>(a, a.MB * B);
+  return hipGetLastError();
+}
+
+}  // namespace pa

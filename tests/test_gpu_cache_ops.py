@@ -1,0 +1,123 @@
+"""Bit-exact parity of slot translation, token writes and block copies (GPU vs
+the CPU oracle), over whole pools compared as uint16."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from conftest import load_golden
+from gpu_util import dev, host, pa_module, say, u16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pa():
+    return pa_module()
+
+
+def test_slot_mapping_decode_form_matches_oracle(pa):
+    c = W.seven_b_single_layer()
+    say("slot_mapping decode form, 7b_single_layer")
+    got = host(pa.pa_slot_mapping(dev(c.block_tables), c.B, c.NB, context_lens=dev(c.context_lens)))
+    ref = oracle.decode_slots(c.block_tables, c.context_lens, c.B, c.NB)
+    assert got.dtype == np.int64 and np.array_equal(got, ref)
+
+
+def test_slot_mapping_invalid_inputs_give_minus_one(pa):
+    tables = np.array([[3, 1, -1], [0, 2, 5], [7, -1, -1], [1, 9, 2]], dtype=np.int32)
+    lens = np.array([5, 12, 0, 6], dtype=np.int32)
+    say("slot_mapping invalid inputs")
+    got = host(pa.pa_slot_mapping(dev(tables), 4, 8, context_lens=dev(lens)))
+    ref = oracle.decode_slots(tables, lens, 4, 8)
+    assert np.array_equal(got, ref) and got.tolist() == [4, 23, -1, -1]
+    seq = np.array([0, 1, 1, 3, 4, -1, 2], dtype=np.int32)
+    pos = np.array([7, 11, 12, 5, 0, 0, 0], dtype=np.int32)
+    got = host(pa.pa_slot_mapping(dev(tables), 4, 8, seq_ids=dev(seq), positions=dev(pos)))
+    assert np.array_equal(got, oracle.token_slots(tables, seq, pos, 4, 8))
+
+
+def test_lifecycle_growth_slots(pa):
+    g = W.growth_example()
+    gold = load_golden("lifecycle.json")
+    say("slot_mapping growth walk 7-2-9-4")
+    got = host(pa.pa_slot_mapping(dev(g["table_after"]), g["B"], g["NB"],
+                                  seq_ids=dev(np.zeros(9, np.int32)),
+                                  positions=dev(g["positions"])))
+    assert got.tolist() == gold["derived_slots_positions_40_to_48"]
+
+
+def test_write_kv_bit_exact_whole_pool(pa):
+    c = W.seven_b_single_layer()
+    kp, vp = dev(c.k_pool), dev(c.v_pool)
+    say("write_kv 7b_single_layer")
+    slots = pa.pa_slot_mapping(dev(c.block_tables), c.B, c.NB, context_lens=dev(c.context_lens))
+    pa.pa_write_kv(dev(c.key_new), dev(c.value_new), kp, vp, slots)
+    rk, rv = oracle.write_kv(c.k_pool, c.v_pool, c.key_new, c.value_new, host(slots))
+    assert np.array_equal(u16(host(kp)), u16(rk))
+    assert np.array_equal(u16(host(vp)), u16(rv))
+
+
+def test_write_kv_skips_negative_and_out_of_pool_slots(pa):
+    rng = np.random.default_rng(21)
+    NB, H, B, D, T = 6, 3, 16, 128, 9
+    kpool = W.f16_normal(rng, (NB, H, B, D))
+    vpool = W.f16_normal(rng, (NB, H, B, D))
+    key = W.f16_normal(rng, (T, H, D))
+    val = W.f16_normal(rng, (T, H, D))
+    slots = np.array([5, -1, 95, 96, 1 << 40, 0, -7, 17, 48], dtype=np.int64)
+    kp, vp = dev(kpool), dev(vpool)
+    say("write_kv skip rules")
+    pa.pa_write_kv(dev(key), dev(val), kp, vp, dev(slots))
+    rk, rv = oracle.write_kv(kpool, vpool, key, val, slots)
+    assert np.array_equal(u16(host(kp)), u16(rk)) and np.array_equal(u16(host(vp)), u16(rv))
+
+
+@pytest.mark.parametrize("H,B,D", [(2, 16, 64), (8, 32, 128), (1, 4, 8)])
+def test_write_kv_other_shapes(pa, H, B, D):
+    rng = np.random.default_rng(H * 100 + B)
+    NB = 11
+    T = 23
+    kpool = W.f16_normal(rng, (NB, H, B, D))
+    vpool = W.f16_normal(rng, (NB, H, B, D))
+    key = W.f16_normal(rng, (T, H, D))
+    val = W.f16_normal(rng, (T, H, D))
+    slots = rng.permutation(NB * B)[:T].astype(np.int64)
+    kp, vp = dev(kpool), dev(vpool)
+    say(f"write_kv H={H} B={B} D={D}")
+    pa.pa_write_kv(dev(key), dev(val), kp, vp, dev(slots))
+    rk, rv = oracle.write_kv(kpool, vpool, key, val, slots)
+    assert np.array_equal(u16(host(kp)), u16(rk)) and np.array_equal(u16(host(vp)), u16(rv))
+
+
+def test_copy_blocks_shared_prefix_bit_exact(pa):
+    d = W.shared_prefix()
+    kp, vp = dev(d["k_pool"]), dev(d["v_pool"])
+    say("copy_blocks shared_prefix 64 pairs")
+    pa.pa_copy_blocks(kp, vp, dev(d["copy_pairs"]))
+    rk, rv = oracle.copy_blocks(d["k_pool"], d["v_pool"], d["copy_pairs"])
+    assert np.array_equal(u16(host(kp)), u16(rk)) and np.array_equal(u16(host(vp)), u16(rv))
+
+
+def test_copy_blocks_skips_out_of_pool_pairs_and_large_blocks(pa):
+    rng = np.random.default_rng(22)
+    NB, H, B, D = 9, 32, 32, 128          # 256 KiB blocks: several workgroups per pair
+    kpool = W.f16_normal(rng, (NB, H, B, D))
+    vpool = W.f16_normal(rng, (NB, H, B, D))
+    pairs = np.array([[0, 3], [1, 9], [-1, 4], [2, 5], [8, 7]], dtype=np.int32)
+    kp, vp = dev(kpool), dev(vpool)
+    say("copy_blocks skip rules, 256 KiB blocks")
+    pa.pa_copy_blocks(kp, vp, dev(pairs))
+    rk, rv = oracle.copy_blocks(kpool, vpool, pairs)
+    assert np.array_equal(u16(host(kp)), u16(rk)) and np.array_equal(u16(host(vp)), u16(rv))
+
+
+def test_calls_with_zero_work_are_no_ops(pa):
+    import torch
+    kp = torch.zeros((2, 1, 16, 128), dtype=torch.float16, device="cuda")
+    say("zero-work calls")
+    pa.pa_copy_blocks(kp, kp.clone(), torch.zeros((0, 2), dtype=torch.int32, device="cuda"))
+    pa.pa_write_kv(torch.zeros((0, 1, 128), dtype=torch.float16, device="cuda"),
+                   torch.zeros((0, 1, 128), dtype=torch.float16, device="cuda"), kp, kp.clone(),
+                   torch.zeros(0, dtype=torch.int64, device="cuda"))
+    assert not host(kp).any()

@@ -208,6 +208,11 @@ def chat_layer(layer: int, seed: int = CHAT_SEED, S: int = 128, with_pools: bool
     return case
 
 
+def chat_pool_seed(layer: int, seed: int = CHAT_SEED) -> int:
+    """Seed of the device-drawn pools of one chat layer."""
+    return seed * 1000 + layer
+
+
 def device_pools(NB: int, Hkv: int, B: int, D: int, seed: int, device="cuda"):
     """K and V pools drawn on the device: torch N(0, 1) in fp32 rounded to fp16.
 
@@ -284,10 +289,11 @@ def shared_prefix(seed: int = 4, n_seq: int = 64, prefix_len: int = 500, Hq: int
                 query=query, suffix_k=suffix_k, suffix_v=suffix_v, scale=1.0 / np.sqrt(D))
 
 
-def long_context(seed: int = 5) -> DecodeCase:
+def long_context(seed: int = 5, with_pools: bool = True) -> DecodeCase:
     """Batch 16 at 4096 tokens, 32 heads, B = 32, pool of exactly 2048 blocks,
-    fully shuffled."""
+    fully shuffled. The host pools take about 30 s to draw; with
+    `with_pools=False` they are left to `device_pools` (seed * 1000)."""
     rng = np.random.default_rng(seed)
     lengths = np.full(16, 4096, dtype=np.int32)
     return _finish_case("long_context_b16_4096", seed, rng, lengths, 32, 32, 32, HEAD_DIM,
-                        2048, (5, 4), None, True)
+                        2048, (5, 4), None, with_pools)

@@ -45,7 +45,52 @@ def parse():
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--cpu-sample-layers", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-reference-mb", type=int, default=0,
+                    help="after timing, run one pa_copy_blocks moving this many MiB per pool "
+                         "(a copy of known size for scaling traffic counters)")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pa_decode_chat_b128_traffic.json")
+DECODE_SOURCES = [os.path.join(ROOT, "paged_kv_cache_151_amd", "csrc", f)
+                  for f in ("decode.hip", "pa_internal.h")]
+
+
+def decode_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed counter summary, or None
+    when the decode kernel's source changed after the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("decode_source_sha256") != decode_source_hash():
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def copy_reference(pa, mb):
+    """One pa_copy_blocks call over a scratch pool: reads and writes exactly
+    mb MiB in each of two pools (K and V)."""
+    import torch
+    blk = 32 * 16 * 128 * 2                       # bytes of one block of one pool
+    n = max(1, (mb << 20) // blk)
+    kp = torch.empty((2 * n, 32, 16, 128), dtype=torch.float16, device="cuda")
+    vp = torch.empty_like(kp)
+    pairs = torch.stack([torch.arange(n), torch.arange(n) + n], 1).to(torch.int32).cuda()
+    torch.cuda.synchronize()
+    pa.pa_copy_blocks(kp, vp, pairs)
+    torch.cuda.synchronize()
+    log(f"copy reference: {n} blocks x {blk} B per pool, {2 * n * blk} B read, same written")
 
 
 def main():
@@ -129,6 +174,9 @@ def main():
     tok_s = S / (ms_per_step * 1e-3)
     achieved = float(np.mean(kv_bytes_layer)) / (decode_avg_ms * 1e-3) / 1e9
 
+    if args.copy_reference_mb > 0:
+        copy_reference(pa, args.copy_reference_mb)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(layers, args.cpu_sample_layers, kv_bytes_step, args.layers)
@@ -162,7 +210,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(),
             "kernel": "pa_decode (partition + reduce), average per layer call",
             "avg_launch_us": round(decode_avg_ms * 1e3, 2),
             "bytes_per_launch": int(np.mean(kv_bytes_layer)),

@@ -35,6 +35,7 @@ namespace pa {
 namespace {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kNegBig = -1.0e30f;   // "no token yet" running max; exp2 of it is 0
 
@@ -52,12 +53,16 @@ __device__ __forceinline__ float dpp_row_sum(float x) {
   return x;
 }
 
-__device__ __forceinline__ float dot8(const uint4& a, const uint4& b) {
+// Element values are passed by value before the bit cast: a bit cast applied
+// directly to an ext-vector element expression (a.y) reads element x.
+__device__ __forceinline__ half2_t as_h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
+
+__device__ __forceinline__ float dot8(const u32x4& a, const u32x4& b) {
   float s = 0.f;
-  s = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a.x), __builtin_bit_cast(half2_t, b.x), s, false);
-  s = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a.y), __builtin_bit_cast(half2_t, b.y), s, false);
-  s = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a.z), __builtin_bit_cast(half2_t, b.z), s, false);
-  s = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a.w), __builtin_bit_cast(half2_t, b.w), s, false);
+  s = __builtin_amdgcn_fdot2(as_h2(a.x), as_h2(b.x), s, false);
+  s = __builtin_amdgcn_fdot2(as_h2(a.y), as_h2(b.y), s, false);
+  s = __builtin_amdgcn_fdot2(as_h2(a.z), as_h2(b.z), s, false);
+  s = __builtin_amdgcn_fdot2(as_h2(a.w), as_h2(b.w), s, false);
   return s;
 }
 
@@ -69,7 +74,7 @@ __device__ __forceinline__ float hi_f(uint32_t u) {
 }
 
 // acc[0..7] += p * v (8 fp16 values in a uint4), fp32 FMA
-__device__ __forceinline__ void fma8(float* acc, float p, const uint4& v) {
+__device__ __forceinline__ void fma8(float* acc, float p, const u32x4& v) {
   acc[0] = __builtin_fmaf(p, lo_f(v.x), acc[0]);
   acc[1] = __builtin_fmaf(p, hi_f(v.x), acc[1]);
   acc[2] = __builtin_fmaf(p, lo_f(v.y), acc[2]);
@@ -80,40 +85,60 @@ __device__ __forceinline__ void fma8(float* acc, float p, const uint4& v) {
   acc[7] = __builtin_fmaf(p, hi_f(v.w), acc[7]);
 }
 
-template <int B>
+// One pipelined work unit is 16 tokens of one KV head: a 4 KiB K tile and a
+// 4 KiB V tile at D = 128. A block of B = 32 tokens is two units, so the
+// register footprint does not grow with B.
+constexpr int kUnit = 16;
+
 struct Tile {
-  static constexpr int R = B / 4;   // token rows per lane per block
-  uint4 k[R];
-  uint4 v[R];
+  u32x4 k[4];   // row r of the wave holds tokens 4i + r of the unit
+  u32x4 v[4];
 };
 
-template <int B>
-__device__ __forceinline__ void load_tile(Tile<B>& t, const _Float16* __restrict__ kp,
-                                          const _Float16* __restrict__ vp, int64_t base,
-                                          int lane_off) {
+// Tile loads go through a buffer resource built on the unit's tile base
+// (wave-uniform, so it lives in scalar registers); each lane supplies its
+// byte offset within the row group (vector offset) and the row group's
+// offset rides in the scalar offset. The resource's range `nbytes` is checked
+// by the hardware against the lane's offset: out-of-range lanes get zeros
+// and touch no memory. A range of 0 therefore turns the load into a no-op
+// that still counts as issued (the loop's wait counts stay uniform), and a
+// range of 256 * valid_tokens never drops a valid token's row (a valid
+// token t = 4i + r has vector offset below 256 (r + 1) <= 256 * valid). Every
+// offset lies inside the unit's 4 KiB tile either way. Word 3 is the
+// raw-buffer format for the gfx9 family; cache policy bit 1 is the
+// non-temporal hint.
+constexpr int kUnitBytes = kUnit * kHeadDim * 2;
+constexpr int kRsrcWord3 = 0x00020000;
+
+template <bool NT>
+__device__ __forceinline__ void load_tile(Tile& t, const _Float16* kb, const _Float16* vb,
+                                          int nbytes, unsigned lane_byte_off) {
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16*>(kb), 0, nbytes, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16*>(vb), 0, nbytes, kRsrcWord3);
 #pragma unroll
-  for (int i = 0; i < Tile<B>::R; ++i) {
-    const int64_t o = base + i * (4 * kHeadDim) + lane_off;
-    t.k[i] = *reinterpret_cast<const uint4*>(kp + o);
-    t.v[i] = *reinterpret_cast<const uint4*>(vp + o);
+  for (int i = 0; i < 4; ++i) {
+    const int so = i * (4 * kHeadDim * 2);   // row i of the tile: scalar offset
+    t.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, lane_byte_off, so, NT ? 2 : 0);
+    t.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, lane_byte_off, so, NT ? 2 : 0);
   }
 }
 
-// Online-softmax update of one lane's state for the block in `t`.
-// tok_base = logical position of the block's token 0 for this lane's row
-// (i.e. block_start + r); with MASK, tokens at or past `L` are excluded by
+// Online-softmax update of one lane's state for the unit in `t`.
+// tok_base = logical position of the unit's token 0 for this lane's row
+// (unit start + r); with MASK, tokens at or past `L` are excluded by
 // selection.
-template <int B, int G, bool MASK>
-__device__ __forceinline__ void process_tile(const Tile<B>& t, const uint4 (&q)[G],
-                                             float (&m)[G], float (&l)[G], float (&acc)[G][8],
-                                             float scale_log2, int tok_base, int L) {
-  constexpr int R = Tile<B>::R;
+template <int G, bool MASK>
+__device__ __forceinline__ void process_tile(const Tile& t, const u32x4 (&q)[G], float (&m)[G],
+                                             float (&l)[G], float (&acc)[G][8], float scale_log2,
+                                             int tok_base, int L) {
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    float sc[R];
+    float sc[4];
     float mx = m[h];
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
+    for (int i = 0; i < 4; ++i) {
       sc[i] = dpp_row_sum(dot8(q[h], t.k[i])) * scale_log2;
       if (MASK) {
         const bool valid = (tok_base + 4 * i) < L;
@@ -127,7 +152,7 @@ __device__ __forceinline__ void process_tile(const Tile<B>& t, const uint4 (&q)[
 #pragma unroll
     for (int d = 0; d < 8; ++d) acc[h][d] *= alpha;
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
+    for (int i = 0; i < 4; ++i) {
       float p = __builtin_amdgcn_exp2f(sc[i] - mx);
       if (MASK) {
         const bool valid = (tok_base + 4 * i) < L;
@@ -156,10 +181,14 @@ __device__ __forceinline__ void merge_state(float& m, float& l, float* acc, floa
   for (int d = 0; d < 8; ++d) acc[d] = acc[d] * a + acco[d] * b;
 }
 
-template <int B, int G>
-__global__ __launch_bounds__(kDecodeWaves * 64) void decode_partition_kernel(const DecodeArgs a) {
-  constexpr int NW = kDecodeWaves;
+template <int B, int G, int NW, int DEPTH, bool NT>
+__global__ __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu(PA_DECODE_MIN_WAVES_PER_EU)))
+void decode_partition_kernel(const DecodeArgs a) {
   constexpr int D = kHeadDim;
+  constexpr int UPB = B / kUnit;        // units per block
+  static_assert(B % kUnit == 0, "block size must be a multiple of 16");
+  static_assert(DEPTH == 1 || DEPTH == 2, "prefetch depth 1 or 2");
   __shared__ float s_acc[NW][G][D];
   __shared__ float s_ml[NW][G][2];
 
@@ -192,15 +221,16 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_partition_kernel(con
     return;
   }
   const int nparts = (L + a.P - 1) / a.P;
-  const int tok1 = tok0 + a.P < L ? tok0 + a.P : L;
+  const int len = (tok0 + a.P < L ? tok0 + a.P : L) - tok0;
   const int blk0 = tok0 / B;
-  const int nblk = (tok1 - tok0 + B - 1) / B;
-  const int n_full = (tok1 - tok0) / B;  // blocks with every slot valid
+  const int nblk = (len + B - 1) / B;
+  const int nunits = (len + kUnit - 1) / kUnit;
+  const int n_full = len / kUnit;        // units with every slot valid
 
-  uint4 q[G];
+  u32x4 q[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    q[h] = *reinterpret_cast<const uint4*>(a.q + ((int64_t)s * a.Hq + hq0 + h) * D + 8 * c);
+    q[h] = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)s * a.Hq + hq0 + h) * D + 8 * c);
   }
   float m[G], l[G], acc[G][8];
 #pragma unroll
@@ -212,50 +242,84 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_partition_kernel(con
   }
 
   const int32_t* trow = a.tables + (int64_t)s * a.MB + blk0;
-  const int lane_off = r * D + 8 * c;
-  const int64_t head_stride = (int64_t)B * D;
+  const unsigned lane_off = (r * D + 8 * c) * 2u;   // bytes
 
   // Blocks are walked in chunks of 64: one lane holds one table entry of the
   // chunk and v_readlane hands the wave its entry, so no table access sits
   // inside the pipelined loop (a partition of at most 64 blocks, the default,
-  // is a single chunk). Inside a chunk the loads of the wave's next block are
-  // issued before the current block is computed. The loads are unconditional
-  // (past the wave's last block they re-read the current one, an L2 hit) so
-  // that the compiler's wait counts stay partial. Only the partition's final
-  // block can be partial; it takes the masked update. A table entry outside
-  // the pool is clamped to block 0 (no access leaves the pool; the result for
-  // such input is unspecified).
+  // is a single chunk). Wave w takes the chunk's units w, w + NW, ... and
+  // issues the loads of the units DEPTH steps ahead before computing the
+  // current one. The load instructions are unconditional (past the wave's
+  // last unit they are no-ops with an empty range) so that the compiler's
+  // wait counts stay partial. Only the partition's final unit can be
+  // partial; its loads fetch only the valid tokens and it takes the masked
+  // update. A table entry outside the pool is clamped to block 0 (no access
+  // leaves the pool; the result for such input is unspecified).
   for (int cb = 0; cb < nblk; cb += 64) {
     const int ce = cb + 64 < nblk ? cb + 64 : nblk;
     const int tbl = cb + lane < ce ? trow[cb + lane] : -1;
-    auto locate = [&](int jj) -> int64_t {
-      const int phys = __builtin_amdgcn_readlane(tbl, jj - cb);
+    const int ue = ce * UPB < nunits ? ce * UPB : nunits;
+    auto locate = [&](int u) -> int64_t {
+      const int bi = u / UPB;
+      const int phys = __builtin_amdgcn_readlane(tbl, bi - cb);
       const int safe = (unsigned)phys < (unsigned)a.NB ? phys : 0;
-      return ((int64_t)safe * a.Hkv + g) * head_stride;
+      return (((int64_t)safe * a.Hkv + g) * B + (u - bi * UPB) * kUnit) * D;
     };
-    int j = cb + wave;
-    if (j >= ce) continue;
-    Tile<B> t0, t1;
-    load_tile<B>(t0, a.k_pool, a.v_pool, locate(j), lane_off);
-    while (true) {
-      int jn = j + NW;
-      load_tile<B>(t1, a.k_pool, a.v_pool, locate(jn < ce ? jn : j), lane_off);
-      if (j < n_full) {
-        process_tile<B, G, false>(t0, q, m, l, acc, a.scale_log2, 0, 0);
+    // Loads unit u, or issues a no-op load when u is past the wave's last unit.
+    auto fetch = [&](Tile& t, int u) {
+      const bool live = u < ue;
+      const int uu = live ? u : ue - 1;
+      const int64_t base = locate(uu);
+      const int valid = len - uu * kUnit;
+      const int nbytes = !live ? 0 : (valid >= kUnit ? kUnitBytes : valid * (kHeadDim * 2));
+      load_tile<NT>(t, a.k_pool + base, a.v_pool + base, nbytes, lane_off);
+    };
+    auto step = [&](const Tile& t, int u) {
+      if (u < n_full) {
+        process_tile<G, false>(t, q, m, l, acc, a.scale_log2, 0, 0);
       } else {
-        process_tile<B, G, true>(t0, q, m, l, acc, a.scale_log2, tok0 + j * B + r, L);
+        process_tile<G, true>(t, q, m, l, acc, a.scale_log2, tok0 + u * kUnit + r, L);
       }
-      if (jn >= ce) break;
-      j = jn;
-      jn = j + NW;
-      load_tile<B>(t0, a.k_pool, a.v_pool, locate(jn < ce ? jn : j), lane_off);
-      if (j < n_full) {
-        process_tile<B, G, false>(t1, q, m, l, acc, a.scale_log2, 0, 0);
-      } else {
-        process_tile<B, G, true>(t1, q, m, l, acc, a.scale_log2, tok0 + j * B + r, L);
+    };
+    int u = cb * UPB + wave;
+    if (u >= ue) continue;
+    if (DEPTH == 1) {
+      Tile t0, t1;
+      fetch(t0, u);
+      while (true) {
+        int un = u + NW;
+        fetch(t1, un);
+        step(t0, u);
+        if (un >= ue) break;
+        u = un;
+        un = u + NW;
+        fetch(t0, un);
+        step(t1, u);
+        if (un >= ue) break;
+        u = un;
       }
-      if (jn >= ce) break;
-      j = jn;
+    } else {
+      Tile t0, t1, t2;
+      fetch(t0, u);
+      int un = u + NW;
+      fetch(t1, un);
+      while (true) {
+        un = u + 2 * NW;
+        fetch(t2, un);
+        step(t0, u);
+        u += NW;
+        if (u >= ue) break;
+        un = u + 2 * NW;
+        fetch(t0, un);
+        step(t1, u);
+        u += NW;
+        if (u >= ue) break;
+        un = u + 2 * NW;
+        fetch(t1, un);
+        step(t2, u);
+        u += NW;
+        if (u >= ue) break;
+      }
     }
   }
 
@@ -346,7 +410,8 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(const DecodeArgs a, i
 template <int B, int G>
 hipError_t launch_partition(const DecodeArgs& a, hipStream_t stream) {
   const int64_t grid = (int64_t)a.Pmax * a.S * a.Hkv;
-  decode_partition_kernel<B, G><<<(unsigned)grid, kDecodeWaves * 64, 0, stream>>>(a);
+  decode_partition_kernel<B, G, kDecodeWaves, kDecodeDepth, kDecodeNontemporal>
+      <<<(unsigned)grid, kDecodeWaves * 64, 0, stream>>>(a);
   return hipGetLastError();
 }
 

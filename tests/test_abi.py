@@ -81,7 +81,7 @@ def test_decode_host_validation(lib):
 def test_workspace_and_partition_sizing(lib):
     ws = lib.pa_decode_workspace_bytes
     ps = lib.pa_decode_partition_size
-    assert ps(128, 32, 16, 2400, 0) == 512
+    assert ps(128, 32, 16, 2400, 0) == 1024
     assert ps(1, 1, 16, 100, 48) == 48
     assert ps(1, 1, 16, 100, 40) == -1
     P = ps(16, 32, 32, 4096, 0)

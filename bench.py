@@ -1,20 +1,26 @@
-"""Benchmark: paged decode on the batch-128 chat workload, one MI355X.
+"""Benchmark: paged decode on one MI355X.
 
-Workload: 128 sequences, context = prompt U[100, 2000] + generated U[50, 500]
-tokens, 32 layers, each with its own K/V block pool (32 KV heads, head dim 128,
-fp16, blocks of 16 tokens, 1.25x pool, shuffled physical ids). One step is one
-decode step of the whole model's attention cache path: per layer, the new
-token's slot (pa_slot_mapping), its K/V store (pa_write_kv) and paged decode
-attention (pa_decode). Inputs are synthetic (seeded) and resident in HBM before
-the timed region.
+Default workload (`--workload chat`): 128 sequences, context = prompt
+U[100, 2000] + generated U[50, 500] tokens, 32 layers, each with its own K/V
+block pool (32 KV heads, head dim 128, fp16, blocks of 16 tokens, 1.25x pool,
+shuffled physical ids). One step is one decode step of the whole model's
+attention cache path: per layer, the new token's slot (pa_slot_mapping), its
+K/V store (pa_write_kv) and paged decode attention (pa_decode).
 
-Prints one JSON line. `value` is KV bytes read per step (valid tokens x 32
-heads x 128 x K and V x 2 B, summed over layers) divided by the step time.
-`roofline` prices the decode call (partition + reduce kernels), timed with HIP
-events on the stream it runs on, against 8 TB/s. `cpu_baseline` times the CPU
-oracle on a bounded sample of the same workload.
+Other workloads (`--workload 7b|shared_prefix|long_context|tiny`) time one
+layer per step and rotate over `--replicas` copies of the inputs so that the
+small ones are read from HBM rather than from the caches (`--replicas 1`
+measures them cache-warm). The shared-prefix workload also times its
+copy-on-write `pa_copy_blocks` (64 pairs) separately.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+Inputs are synthetic (seeded) and resident in HBM before the timed region.
+Prints one JSON line. `value` is KV bytes read per step (valid tokens x KV
+heads x 128 x K and V x 2 B, summed over the step's layers) divided by the step
+time. `roofline` prices one pa_decode call (partition + reduce kernels), timed
+with HIP events on the stream it runs on, against 8 TB/s. `cpu_baseline` times
+the CPU oracle on a bounded sample of the same workload.
+
+    python bench.py [--workload chat] [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -30,6 +36,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+METRIC = "paged-decode KV-read GB/s (% of HBM peak) + decode tokens/s, batch 128"
 
 
 def log(*a):
@@ -41,7 +48,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--layers", type=int, default=32)
+    ap.add_argument("--workload", default="chat",
+                    choices=["chat", "7b", "shared_prefix", "long_context", "tiny"])
+    ap.add_argument("--layers", type=int, default=32, help="chat workload: layers per step")
+    ap.add_argument("--replicas", type=int, default=0,
+                    help="other workloads: input copies rotated over steps (0 = enough to "
+                         "exceed the 256 MB last-level cache; 1 = cache-warm)")
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--cpu-sample-layers", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -93,6 +105,108 @@ def copy_reference(pa, mb):
     log(f"copy reference: {n} blocks x {blk} B per pool, {2 * n * blk} B read, same written")
 
 
+# ---------------------------------------------------------------------------
+# workload set-up: a list of "layers", each one decode call's inputs on the GPU
+# ---------------------------------------------------------------------------
+
+def _upload(case, kp, vp, dev):
+    import torch
+    return dict(case=case, kp=kp, vp=vp, tables=dev(case.block_tables), lens=dev(case.context_lens),
+                q=dev(case.query), k_new=dev(case.key_new), v_new=dev(case.value_new),
+                slots=torch.empty(case.S, dtype=torch.int64, device="cuda"))
+
+
+def _replicate(layer, n):
+    out = [layer]
+    for _ in range(n - 1):
+        out.append({k: (v.clone() if hasattr(v, "clone") else v) for k, v in layer.items()})
+    return out
+
+
+def _replicas_for(args, bytes_per_layer):
+    if args.replicas > 0:
+        return args.replicas
+    return max(1, int(np.ceil(1.0e9 / max(bytes_per_layer, 1))))   # > 1 GB in rotation
+
+
+def build_chat(args, dev):
+    import workloads as W
+    lengths = W.chat_lengths()
+    layers = []
+    for layer in range(args.layers):
+        c = W.chat_layer(layer, lengths=lengths)
+        kp, vp = W.device_pools(c.NB, c.Hkv, c.B, c.D, seed=W.chat_pool_seed(layer))
+        layers.append(_upload(c, kp, vp, dev))
+    desc = "chat decode, batch 128, 32 layers (prompt U[100,2000] + generated U[50,500])"
+    if args.layers != 32:
+        desc += f" -- REDUCED to {args.layers} layers"
+    return [layers], desc, {}
+
+
+def build_single(args, dev, case, desc):
+    kp, vp = dev(case.k_pool), dev(case.v_pool)
+    base = _upload(case, kp, vp, dev)
+    pool_bytes = 2 * kp.numel() * 2
+    reps = _replicas_for(args, pool_bytes)
+    return [[x] for x in _replicate(base, reps)], desc, {"replicas": reps}
+
+
+def build_shared_prefix(args, dev, pa):
+    """Set-up runs the workload's own boundary calls: copy-on-write of the
+    shared partial block for all 64 samples, then the suffix tokens up to
+    position L-2. The timed step writes the last token and decodes."""
+    import torch
+    import workloads as W
+    d = W.shared_prefix()
+    case = W.DecodeCase(name="shared_prefix", seed=4, S=d["S"], Hq=d["Hq"], Hkv=d["Hkv"], D=d["D"],
+                        B=d["B"], NB=d["NB"], context_lens=d["context_lens"], block_tables=d["tables"],
+                        query=d["query"], key_new=np.stack([k[-1] for k in d["suffix_k"]]),
+                        value_new=np.stack([v[-1] for v in d["suffix_v"]]), scale=d["scale"])
+    kp, vp = dev(d["k_pool"]), dev(d["v_pool"])
+    pairs = dev(d["copy_pairs"])
+    pristine = (kp.clone(), vp.clone())
+    pa.pa_copy_blocks(kp, vp, pairs)
+    seq, pos, ks, vs = [], [], [], []
+    for s in range(d["S"]):
+        n = int(d["context_lens"][s]) - d["prefix_len"] - 1
+        seq += [s] * n
+        pos += list(range(d["prefix_len"], d["prefix_len"] + n))
+        ks.append(d["suffix_k"][s][:-1])
+        vs.append(d["suffix_v"][s][:-1])
+    tables = dev(d["tables"])
+    slots = pa.pa_slot_mapping(tables, d["B"], d["NB"], seq_ids=dev(np.array(seq, np.int32)),
+                               positions=dev(np.array(pos, np.int32)))
+    pa.pa_write_kv(dev(np.concatenate(ks)), dev(np.concatenate(vs)), kp, vp, slots)
+    torch.cuda.synchronize()
+    base = _upload(case, kp, vp, dev)
+    reps = _replicas_for(args, 2 * kp.numel() * 2)
+    extra = {"replicas": reps, "copy": (pristine, pairs, d)}
+    desc = ("shared prefix: 64 samples of a 500-token prompt + suffix U[50,500], "
+            "32 query / 8 KV heads, B=16")
+    return [[x] for x in _replicate(base, reps)], desc, extra
+
+
+def time_copy_on_write(pa, extra):
+    """pa_copy_blocks of the 64 copy-on-write pairs, on a scratch copy."""
+    import torch
+    (k0, v0), pairs, d = extra["copy"]
+    kp, vp = k0.clone(), v0.clone()
+    for _ in range(3):
+        pa.pa_copy_blocks(kp, vp, pairs)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 20
+    e0.record()
+    for _ in range(n):
+        pa.pa_copy_blocks(kp, vp, pairs)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / n
+    moved = 2 * 2 * pairs.shape[0] * d["Hkv"] * d["B"] * d["D"] * 2   # read + write, K and V
+    return {"pairs": int(pairs.shape[0]), "us": round(us, 2),
+            "bytes_read_plus_written": moved, "GBs": round(moved / us / 1e3, 1)}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -100,8 +214,6 @@ def main():
               "(sequences and KV heads shard with no exchange); run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
-    if args.layers != 32:
-        log("note: --layers != 32 is a reduced workload; the JSON line says so")
 
     import torch
     import paged_kv_cache_151_amd as pa
@@ -109,31 +221,41 @@ def main():
 
     torch.cuda.set_device(0)
     dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
-    lengths = W.chat_lengths()
-    S = len(lengths)
-    layers = []
     t0 = time.time()
-    for layer in range(args.layers):
-        c = W.chat_layer(layer, lengths=lengths)
-        kp, vp = W.device_pools(c.NB, c.Hkv, c.B, c.D, seed=W.chat_pool_seed(layer))
-        layers.append(dict(case=c, kp=kp, vp=vp, tables=dev(c.block_tables),
-                           lens=dev(c.context_lens), q=dev(c.query), k_new=dev(c.key_new),
-                           v_new=dev(c.value_new),
-                           slots=torch.empty(S, dtype=torch.int64, device="cuda")))
+    if args.workload == "chat":
+        steps_inputs, desc, extra = build_chat(args, dev)
+    elif args.workload == "7b":
+        steps_inputs, desc, extra = build_single(
+            args, dev, W.seven_b_single_layer(),
+            "7B-class single layer, batch 8, lengths U[50,900) (seed 7), 32 heads, B=16")
+    elif args.workload == "long_context":
+        c = W.long_context(with_pools=False)
+        kp, vp = W.device_pools(c.NB, c.Hkv, c.B, c.D, seed=c.seed * 1000)
+        c.k_pool, c.v_pool = kp, vp
+        steps_inputs, desc, extra = build_single(
+            args, lambda x: x if hasattr(x, "is_cuda") else dev(x), c,
+            "long context, batch 16 x 4096 tokens, 32 heads, B=32")
+    elif args.workload == "tiny":
+        steps_inputs, desc, extra = build_single(
+            args, dev, W.tiny_worked_example(),
+            "tiny worked example, 2 sequences (40, 48 tokens), 4 heads, B=16")
+    else:
+        steps_inputs, desc, extra = build_shared_prefix(args, dev, pa)
     torch.cuda.synchronize()
-    c0 = layers[0]["case"]
-    pool_gb = 2 * c0.NB * c0.Hkv * c0.B * c0.D * 2 / 1e9
-    log(f"setup {time.time() - t0:.1f}s: {args.layers} layers, NB={c0.NB}, "
-        f"K+V pools {pool_gb:.2f} GB per layer")
-    maxL = c0.max_context_len
+    c0 = steps_inputs[0][0]["case"]
+    S = c0.S
+    log(f"setup {time.time() - t0:.1f}s: {desc}; {len(steps_inputs)} input set(s) x "
+        f"{len(steps_inputs[0])} layer(s), NB={c0.NB}")
+
+    maxL = max(ly["case"].max_context_len for ly in steps_inputs[0])
     P = pa.pa_decode_partition_size(S, c0.Hkv, c0.B, maxL, args.partition_size)
     ws_bytes = pa.pa_decode_workspace_bytes(S, c0.Hq, c0.Hkv, c0.D, c0.B, maxL, P)
     workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
     out = torch.empty((S, c0.Hq, c0.D), dtype=torch.float16, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def step(events=None):
-        for i, ly in enumerate(layers):
+    def step(k, events=None):
+        for i, ly in enumerate(steps_inputs[k % len(steps_inputs)]):
             c = ly["case"]
             pa.pa_slot_mapping(ly["tables"], c.B, c.NB, context_lens=ly["lens"], out=ly["slots"])
             pa.pa_write_kv(ly["k_new"], ly["v_new"], ly["kp"], ly["vp"], ly["slots"])
@@ -144,45 +266,57 @@ def main():
             if events is not None:
                 events[i][1].record(stream)
 
-    for _ in range(args.warmup):
-        step()
+    for k in range(args.warmup):
+        step(k)
     torch.cuda.synchronize()
 
     # timed region: K whole steps
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
-    for _ in range(args.steps):
-        step()
+    for k in range(args.steps):
+        step(k)
     end.record(stream)
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / args.steps
 
     # decode-call durations: events around every pa_decode of further steps
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in layers] for _ in range(args.steps)]
+           for _ in steps_inputs[0]] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for k in range(args.steps):
-        step(ev[k])
+        step(k, ev[k])
     torch.cuda.synchronize()
     decode_ms = np.array([[a.elapsed_time(b) for a, b in row] for row in ev])
     decode_avg_ms = float(decode_ms.mean())
 
-    kv_bytes_layer = [ly["case"].kv_bytes() for ly in layers]
+    kv_bytes_layer = [ly["case"].kv_bytes() for ly in steps_inputs[0]]
     kv_bytes_step = float(sum(kv_bytes_layer))
     gbs = kv_bytes_step / (ms_per_step * 1e-3) / 1e9
     tok_s = S / (ms_per_step * 1e-3)
     achieved = float(np.mean(kv_bytes_layer)) / (decode_avg_ms * 1e-3) / 1e9
+
+    cow = time_copy_on_write(pa, extra) if "copy" in extra else None
 
     if args.copy_reference_mb > 0:
         copy_reference(pa, args.copy_reference_mb)
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(layers, args.cpu_sample_layers, kv_bytes_step, args.layers)
+        cpu = cpu_baseline(steps_inputs[0], args.cpu_sample_layers, kv_bytes_step,
+                           len(steps_inputs[0]))
 
+    config = {
+        "workload": desc,
+        "batch": S, "layers": len(steps_inputs[0]), "heads_q": c0.Hq, "heads_kv": c0.Hkv,
+        "head_dim": c0.D, "block_size": c0.B, "pool_blocks_per_layer": c0.NB,
+        "tokens_per_layer": int(c0.context_lens.sum()), "max_context": maxL, "partition_size": P,
+        "kv_bytes_per_step": int(kv_bytes_step),
+    }
+    if "replicas" in extra:
+        config["input_replicas_rotated"] = extra["replicas"]
     res = {
-        "metric": "paged-decode KV-read GB/s (% of HBM peak) + decode tokens/s, batch 128",
+        "metric": METRIC,
         "value": round(gbs, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -197,26 +331,22 @@ def main():
         "data": "synthetic",
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": round(tok_s, 1),
-        "config": {
-            "workload": "chat decode, batch 128, 32 layers (prompt U[100,2000] + generated U[50,500])",
-            "batch": S, "layers": args.layers, "heads_q": c0.Hq, "heads_kv": c0.Hkv,
-            "head_dim": c0.D, "block_size": c0.B, "pool_blocks_per_layer": c0.NB,
-            "tokens": int(lengths.sum()), "max_context": maxL, "partition_size": P,
-            "kv_bytes_per_step": int(kv_bytes_step),
-        },
+        "config": config,
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(),
-            "kernel": "pa_decode (partition + reduce), average per layer call",
+            "traffic": measured_traffic() if args.workload == "chat" and args.layers == 32 else None,
+            "kernel": "pa_decode call (partition + reduce kernels), average per layer",
             "avg_launch_us": round(decode_avg_ms * 1e3, 2),
             "bytes_per_launch": int(np.mean(kv_bytes_layer)),
         },
         "cpu_baseline": cpu,
     }
+    if cow is not None:
+        res["copy_on_write"] = cow
     print(json.dumps(res), flush=True)
 
 
@@ -249,16 +379,17 @@ def cpu_baseline(layers, n_sample, kv_bytes_step, n_layers):
         del kb, vb
     per_layer = secs / n_sample
     kv_layer = kv_bytes_step / n_layers
+    S = layers[0]["case"].S
     return {
         "value": round(kv_layer / per_layer / 1e9, 4),
         "unit": "GB/s",
         "cores": len(os.sched_getaffinity(0)),
         "blas_threads": blas_threads,
         "kind": "oracle",
-        "decode_tokens_per_s": round(layers[0]["case"].S / (per_layer * n_layers), 4),
-        "sample": f"oracle decode of {n_sample} of {n_layers} layers (all 128 sequences, "
-                  f"{tokens} cached tokens x 32 heads), {secs:.1f} s; tokens/s extrapolated "
-                  f"to the 32-layer step",
+        "decode_tokens_per_s": round(S / (per_layer * n_layers), 4),
+        "sample": f"oracle decode of {n_sample} of {n_layers} layer(s) (all {S} sequences, "
+                  f"{tokens} cached tokens x {layers[0]['case'].Hq} query heads), {secs:.1f} s; "
+                  f"tokens/s extrapolated to the {n_layers}-layer step",
     }
 
 

@@ -248,7 +248,7 @@ def main():
         f"{len(steps_inputs[0])} layer(s), NB={c0.NB}")
 
     maxL = max(ly["case"].max_context_len for ly in steps_inputs[0])
-    P = pa.pa_decode_partition_size(S, c0.Hkv, c0.B, maxL, args.partition_size)
+    P = pa.pa_decode_partition_size(S, c0.Hq, c0.Hkv, c0.B, maxL, args.partition_size)
     ws_bytes = pa.pa_decode_workspace_bytes(S, c0.Hq, c0.Hkv, c0.D, c0.B, maxL, P)
     workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
     out = torch.empty((S, c0.Hq, c0.D), dtype=torch.float16, device="cuda")

@@ -149,7 +149,8 @@ pa_status pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_mappin
  * GPU). Returns -1 for invalid arguments (B <= 0, partition_size < 0 or not a
  * multiple of B).
  */
-int pa_decode_partition_size(int S, int Hkv, int B, int max_context_len, int partition_size);
+int pa_decode_partition_size(int S, int Hq, int Hkv, int B, int max_context_len,
+                             int partition_size);
 
 /*
  * pa_decode_workspace_bytes — device workspace pa_decode needs: partial

@@ -37,7 +37,7 @@ _lib.pa_write_kv.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
 _lib.pa_copy_blocks.restype = _i
 _lib.pa_copy_blocks.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _p]
 _lib.pa_decode_partition_size.restype = _i
-_lib.pa_decode_partition_size.argtypes = [_i, _i, _i, _i, _i]
+_lib.pa_decode_partition_size.argtypes = [_i, _i, _i, _i, _i, _i]
 _lib.pa_decode_workspace_bytes.restype = ctypes.c_size_t
 _lib.pa_decode_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i]
 _lib.pa_decode.restype = _i
@@ -109,8 +109,8 @@ def pa_copy_blocks(k_pool, v_pool, block_mapping, stream=None):
         _ptr(k_pool), _ptr(v_pool), _ptr(block_mapping), n, Hkv, D, B, NB, _stream(stream)))
 
 
-def pa_decode_partition_size(S, Hkv, B, max_context_len, partition_size=0) -> int:
-    return _lib.pa_decode_partition_size(S, Hkv, B, max_context_len, partition_size)
+def pa_decode_partition_size(S, Hq, Hkv, B, max_context_len, partition_size=0) -> int:
+    return _lib.pa_decode_partition_size(S, Hq, Hkv, B, max_context_len, partition_size)
 
 
 def pa_decode_workspace_bytes(S, Hq, Hkv, D, B, max_context_len, partition_size=0) -> int:

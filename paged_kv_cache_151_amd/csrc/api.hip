@@ -123,24 +123,29 @@ pa_status pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_mappin
   return ok();
 }
 
-int pa_decode_partition_size(int S, int Hkv, int B, int max_context_len, int partition_size) {
+int pa_decode_partition_size(int S, int Hq, int Hkv, int B, int max_context_len,
+                             int partition_size) {
   if (B <= 0 || partition_size < 0 || (partition_size > 0 && partition_size % B)) return -1;
   if (partition_size > 0) return partition_size;
   // Default: 1024 tokens (64 blocks of 16, one table chunk), halved while the
-  // launch would give fewer than 2048 workgroups (8 per CU), down to 4 blocks.
-  // Measured on the batch-128 chat workload: 1024 beats 512 by 4 % (fewer
-  // partials, longer load streams per wave) and matches 2048.
+  // launch would give fewer than 2048 waves (8 per CU), down to 4 blocks.
+  // Measured on MI355X: for the batch-128 chat workload 1024 beats 512 by 4 %
+  // (fewer partials, longer load streams per wave); for the 32/8-head shared
+  // prefix workload one 1024-token partition per sequence (no reduce) beats
+  // 512 by 20 %.
+  const int G = (Hkv > 0 && Hq >= Hkv && Hq % Hkv == 0) ? Hq / Hkv : 1;
+  const int64_t waves = pa::decode_waves(G);
   int P = 64 * B < 1024 ? 64 * B : 1024;
   if (P < B) P = B;
   const int64_t units = (int64_t)(S > 0 ? S : 1) * (Hkv > 0 ? Hkv : 1);
   const int maxL = max_context_len > 0 ? max_context_len : 1;
-  while (P > 4 * B && units * ceil_div(maxL, P) < 2048) P /= 2;
+  while (P > 4 * B && units * ceil_div(maxL, P) * waves < 2048) P /= 2;
   return P;
 }
 
 size_t pa_decode_workspace_bytes(int S, int Hq, int Hkv, int D, int B, int max_context_len,
                                  int partition_size) {
-  const int P = pa_decode_partition_size(S, Hkv, B, max_context_len, partition_size);
+  const int P = pa_decode_partition_size(S, Hq, Hkv, B, max_context_len, partition_size);
   if (P <= 0 || S <= 0 || Hq <= 0 || D <= 0 || max_context_len <= 0) return 0;
   const int64_t Pmax = ceil_div(max_context_len, P);
   if (Pmax <= 1) return 0;
@@ -179,12 +184,12 @@ pa_status pa_decode(void* out, const void* query, const void* k_pool, const void
   if (!aligned(block_tables, 4) || !aligned(context_lens, 4))
     return fail(PA_ERR_ALIGN, "pa_decode: block_tables/context_lens misaligned");
 
-  const int P = pa_decode_partition_size(S, Hkv, B, max_context_len, partition_size);
+  const int P = pa_decode_partition_size(S, Hq, Hkv, B, max_context_len, partition_size);
   const int Pmax = max_context_len > 0 ? ceil_div(max_context_len, P) : 1;
   if (Pmax > pa::kMaxPartitions)
     return fail(PA_ERR_SHAPE, "pa_decode: %d partitions exceed %d", Pmax, pa::kMaxPartitions);
   const int64_t wgs = (int64_t)Pmax * S * Hkv;
-  if (wgs * pa::kDecodeWaves * 64 >= ((int64_t)1 << 32) || (int64_t)S * Hq >= ((int64_t)1 << 31))
+  if (wgs * 512 >= ((int64_t)1 << 32) || (int64_t)S * Hq >= ((int64_t)1 << 31))
     return fail(PA_ERR_SHAPE, "pa_decode: launch too large (%lld workgroups)", (long long)wgs);
   const size_t need = pa_decode_workspace_bytes(S, Hq, Hkv, D, B, max_context_len, P);
   if (need > 0) {

@@ -181,21 +181,32 @@ __device__ __forceinline__ void merge_state(float& m, float& l, float* acc, floa
   for (int d = 0; d < 8; ++d) acc[d] = acc[d] * a + acco[d] * b;
 }
 
-template <int B, int G, int NW, int DEPTH, bool NT>
+// G query heads share KV head g. The workgroup's waves are split into NH =
+// G / HPW head groups (wave w serves heads HPW * (w % NH) ... of the group)
+// and NU = NW / NH unit subsets (wave w walks units w / NH, + NU, ...), so a
+// wave holds the state of at most HPW heads whatever G is. When NH > 1 each
+// K/V tile is loaded by NH waves of the same workgroup: the repeats are
+// served by the caches, HBM traffic is unchanged.
+template <int B, int G, int HPW, int NW, int DEPTH, bool NT>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(PA_DECODE_MIN_WAVES_PER_EU)))
 void decode_partition_kernel(const DecodeArgs a) {
   constexpr int D = kHeadDim;
   constexpr int UPB = B / kUnit;        // units per block
+  constexpr int NH = G / HPW;           // head groups
+  constexpr int NU = NW / NH;           // unit subsets
   static_assert(B % kUnit == 0, "block size must be a multiple of 16");
   static_assert(DEPTH == 1 || DEPTH == 2, "prefetch depth 1 or 2");
-  __shared__ float s_acc[NW][G][D];
-  __shared__ float s_ml[NW][G][2];
+  static_assert(G % HPW == 0 && NW % NH == 0, "waves must cover the head groups");
+  __shared__ float s_acc[NW][HPW][D];
+  __shared__ float s_ml[NW][HPW][2];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane >> 4;
   const int c = lane & 15;
+  const int hgrp = wave % NH;
+  const int usub = wave / NH;
 
   // blockIdx -> (p, s, g) with g fastest: consecutive workgroups go to
   // consecutive XCDs, so every workgroup of one KV head lands on the same XCD
@@ -227,14 +238,15 @@ void decode_partition_kernel(const DecodeArgs a) {
   const int nunits = (len + kUnit - 1) / kUnit;
   const int n_full = len / kUnit;        // units with every slot valid
 
-  u32x4 q[G];
+  const int hw0 = hq0 + hgrp * HPW;      // this wave's first query head
+  u32x4 q[HPW];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    q[h] = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)s * a.Hq + hq0 + h) * D + 8 * c);
+  for (int h = 0; h < HPW; ++h) {
+    q[h] = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)s * a.Hq + hw0 + h) * D + 8 * c);
   }
-  float m[G], l[G], acc[G][8];
+  float m[HPW], l[HPW], acc[HPW][8];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
+  for (int h = 0; h < HPW; ++h) {
     m[h] = kNegBig;
     l[h] = 0.f;
 #pragma unroll
@@ -276,23 +288,23 @@ void decode_partition_kernel(const DecodeArgs a) {
     };
     auto step = [&](const Tile& t, int u) {
       if (u < n_full) {
-        process_tile<G, false>(t, q, m, l, acc, a.scale_log2, 0, 0);
+        process_tile<HPW, false>(t, q, m, l, acc, a.scale_log2, 0, 0);
       } else {
-        process_tile<G, true>(t, q, m, l, acc, a.scale_log2, tok0 + u * kUnit + r, L);
+        process_tile<HPW, true>(t, q, m, l, acc, a.scale_log2, tok0 + u * kUnit + r, L);
       }
     };
-    int u = cb * UPB + wave;
+    int u = cb * UPB + usub;
     if (u >= ue) continue;
     if (DEPTH == 1) {
       Tile t0, t1;
       fetch(t0, u);
       while (true) {
-        int un = u + NW;
+        int un = u + NU;
         fetch(t1, un);
         step(t0, u);
         if (un >= ue) break;
         u = un;
-        un = u + NW;
+        un = u + NU;
         fetch(t0, un);
         step(t1, u);
         if (un >= ue) break;
@@ -301,23 +313,23 @@ void decode_partition_kernel(const DecodeArgs a) {
     } else {
       Tile t0, t1, t2;
       fetch(t0, u);
-      int un = u + NW;
+      int un = u + NU;
       fetch(t1, un);
       while (true) {
-        un = u + 2 * NW;
+        un = u + 2 * NU;
         fetch(t2, un);
         step(t0, u);
-        u += NW;
+        u += NU;
         if (u >= ue) break;
-        un = u + 2 * NW;
+        un = u + 2 * NU;
         fetch(t0, un);
         step(t1, u);
-        u += NW;
+        u += NU;
         if (u >= ue) break;
-        un = u + 2 * NW;
+        un = u + 2 * NU;
         fetch(t1, un);
         step(t2, u);
-        u += NW;
+        u += NU;
         if (u >= ue) break;
       }
     }
@@ -325,7 +337,7 @@ void decode_partition_kernel(const DecodeArgs a) {
 
   // merge the four rows of the wave (lanes c, c+16, c+32, c+48)
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
+  for (int h = 0; h < HPW; ++h) {
 #pragma unroll
     for (int x = 16; x <= 32; x *= 2) {
       const float mo = __shfl_xor(m[h], x);
@@ -338,7 +350,7 @@ void decode_partition_kernel(const DecodeArgs a) {
   }
   if (r == 0) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
+    for (int h = 0; h < HPW; ++h) {
 #pragma unroll
       for (int d = 0; d < 8; ++d) s_acc[wave][h][8 * c + d] = acc[h][d];
       if (c == 0) {
@@ -349,19 +361,23 @@ void decode_partition_kernel(const DecodeArgs a) {
   }
   __syncthreads();
 
-  // combine the waves: thread e handles output element (h, d)
+  // combine the unit subsets: thread e handles output element (h, d); the
+  // waves serving head h are hg + NH * k, k < NU, with hg = h / HPW
   for (int e = threadIdx.x; e < G * D; e += NW * 64) {
     const int h = e / D;
     const int d = e % D;
-    float mx = s_ml[0][h][0];
+    const int hg = h / HPW;
+    const int hh = h % HPW;
+    float mx = s_ml[hg][hh][0];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) mx = __builtin_fmaxf(mx, s_ml[w][h][0]);
+    for (int k = 1; k < NU; ++k) mx = __builtin_fmaxf(mx, s_ml[hg + NH * k][hh][0]);
     float lsum = 0.f, num = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float f = __builtin_amdgcn_exp2f(s_ml[w][h][0] - mx);
-      lsum += f * s_ml[w][h][1];
-      num += f * s_acc[w][h][d];
+    for (int k = 0; k < NU; ++k) {
+      const int w = hg + NH * k;
+      const float f = __builtin_amdgcn_exp2f(s_ml[w][hh][0] - mx);
+      lsum += f * s_ml[w][hh][1];
+      num += f * s_acc[w][hh][d];
     }
     const int hq = hq0 + h;
     if (nparts == 1) {
@@ -409,9 +425,12 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(const DecodeArgs a, i
 
 template <int B, int G>
 hipError_t launch_partition(const DecodeArgs& a, hipStream_t stream) {
+  constexpr int HPW = G < kDecodeHeadsPerWave ? G : kDecodeHeadsPerWave;
+  constexpr int NH = G / HPW;
+  constexpr int NW = decode_waves(G) > NH ? decode_waves(G) : NH;
   const int64_t grid = (int64_t)a.Pmax * a.S * a.Hkv;
-  decode_partition_kernel<B, G, kDecodeWaves, kDecodeDepth, kDecodeNontemporal>
-      <<<(unsigned)grid, kDecodeWaves * 64, 0, stream>>>(a);
+  decode_partition_kernel<B, G, HPW, NW, kDecodeDepth, kDecodeNontemporal>
+      <<<(unsigned)grid, NW * 64, 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -23,12 +23,26 @@ constexpr int kHeadDim = 128;        // decode kernels are specialised for D = 1
 #ifndef PA_DECODE_NT
 #define PA_DECODE_NT 1
 #endif
+// Query heads of one KV group that one wave serves (grouped-query attention).
+// Fewer heads per wave means fewer registers but more waves re-reading each
+// tile; on MI355X four heads per wave measured fastest for G = 4.
+#ifndef PA_DECODE_HEADS_PER_WAVE
+#define PA_DECODE_HEADS_PER_WAVE 4
+#endif
 #ifndef PA_DECODE_MIN_WAVES_PER_EU
 #define PA_DECODE_MIN_WAVES_PER_EU 1
 #endif
 constexpr int kDecodeWaves = PA_DECODE_WAVES;
 constexpr int kDecodeDepth = PA_DECODE_DEPTH;
 constexpr bool kDecodeNontemporal = PA_DECODE_NT != 0;
+constexpr int kDecodeHeadsPerWave = PA_DECODE_HEADS_PER_WAVE;
+
+// Waves per decode workgroup for a query group of G heads: a group's update
+// costs G times the arithmetic per tile, so larger groups split each
+// partition's units over more waves (measured: 2 for one head, 4 for four).
+constexpr int decode_waves(int G) {
+  return G >= 8 ? 4 * kDecodeWaves : (G >= 4 ? 2 * kDecodeWaves : kDecodeWaves);
+}
 constexpr int kMaxPartitions = 1 << 16;
 
 // Arguments of the decode partition kernel (passed by value in the kernarg segment).

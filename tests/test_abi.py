@@ -81,10 +81,11 @@ def test_decode_host_validation(lib):
 def test_workspace_and_partition_sizing(lib):
     ws = lib.pa_decode_workspace_bytes
     ps = lib.pa_decode_partition_size
-    assert ps(128, 32, 16, 2400, 0) == 1024
-    assert ps(1, 1, 16, 100, 48) == 48
-    assert ps(1, 1, 16, 100, 40) == -1
-    P = ps(16, 32, 32, 4096, 0)
+    assert ps(128, 32, 32, 16, 2400, 0) == 1024
+    assert ps(64, 32, 8, 16, 993, 0) == 1024      # grouped heads: one partition per sequence
+    assert ps(1, 1, 1, 16, 100, 48) == 48
+    assert ps(1, 1, 1, 16, 100, 40) == -1
+    P = ps(16, 32, 32, 32, 4096, 0)
     assert P % 32 == 0
     assert ws(16, 32, 32, 128, 32, 4096, 512) == 16 * 32 * 8 * 130 * 4
     assert ws(2, 4, 4, 128, 16, 48, 0) == 0              # one partition: no workspace

@@ -51,6 +51,10 @@ def parse():
     ap.add_argument("--workload", default="chat",
                     choices=["chat", "7b", "shared_prefix", "long_context", "tiny"])
     ap.add_argument("--layers", type=int, default=32, help="chat workload: layers per step")
+    ap.add_argument("--block-size", type=int, default=16, help="chat workload: tokens per block")
+    ap.add_argument("--contiguous", action="store_true",
+                    help="chat workload: one block per sequence sized for the longest one "
+                         "(the pre-paging layout), for comparison")
     ap.add_argument("--replicas", type=int, default=0,
                     help="other workloads: input copies rotated over steps (0 = enough to "
                          "exceed the 256 MB last-level cache; 1 = cache-warm)")
@@ -134,12 +138,16 @@ def build_chat(args, dev):
     lengths = W.chat_lengths()
     layers = []
     for layer in range(args.layers):
-        c = W.chat_layer(layer, lengths=lengths)
+        c = W.chat_layer(layer, lengths=lengths, B=args.block_size, contiguous=args.contiguous)
         kp, vp = W.device_pools(c.NB, c.Hkv, c.B, c.D, seed=W.chat_pool_seed(layer))
         layers.append(_upload(c, kp, vp, dev))
     desc = "chat decode, batch 128, 32 layers (prompt U[100,2000] + generated U[50,500])"
     if args.layers != 32:
         desc += f" -- REDUCED to {args.layers} layers"
+    if args.contiguous:
+        desc += f" -- CONTIGUOUS layout (one {layers[0]['case'].B}-token block per sequence)"
+    elif args.block_size != 16:
+        desc += f" -- block size {args.block_size}"
     return [layers], desc, {}
 
 
@@ -338,7 +346,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic() if args.workload == "chat" and args.layers == 32 else None,
+            "traffic": (measured_traffic() if args.workload == "chat" and args.layers == 32
+                        and args.block_size == 16 and not args.contiguous else None),
             "kernel": "pa_decode call (partition + reduce kernels), average per layer",
             "avg_launch_us": round(decode_avg_ms * 1e3, 2),
             "bytes_per_launch": int(np.mean(kv_bytes_layer)),

@@ -145,9 +145,9 @@ pa_status pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_mappin
 /*
  * pa_decode_partition_size — the context partition (in tokens) pa_decode uses
  * for these sizes: partition_size itself when positive, otherwise the
- * library's choice (a multiple of B that gives enough workgroups to fill the
- * GPU). Returns -1 for invalid arguments (B <= 0, partition_size < 0 or not a
- * multiple of B).
+ * library's choice (a multiple of 16 that gives enough waves to fill the GPU,
+ * at most 1024). Returns -1 for invalid arguments (B <= 0, partition_size < 0
+ * or not a multiple of 16).
  */
 int pa_decode_partition_size(int S, int Hq, int Hkv, int B, int max_context_len,
                              int partition_size);
@@ -185,10 +185,12 @@ size_t pa_decode_workspace_bytes(int S, int Hq, int Hkv, int D, int B, int max_c
  *   max_context_len   host bound on every L_s (sizes the launch)
  *   scale             softmax scale, usually 1/sqrt(D)
  *   partition_size    tokens per context partition: 0 = library choice, else a
- *                     positive multiple of B
+ *                     positive multiple of 16 (a partition may start inside a
+ *                     block)
  *   workspace         device buffer of at least pa_decode_workspace_bytes(...)
  *                     bytes, 16-byte aligned; may be NULL when that is 0
- * Supported: D = 128; B in {16, 32}; Hq / Hkv in {1, 2, 4, 8}. S = 0 is a no-op.
+ * Supported: D = 128; B a multiple of 16 (one block per sequence of at least
+ * its length is the contiguous layout); Hq / Hkv in {1, 2, 4, 8}. S = 0 is a no-op.
  * L_s outside the stated range is a caller error: the kernels clamp to the
  * table and the launch, so no access leaves the buffers.
  */

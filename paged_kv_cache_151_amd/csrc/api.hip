@@ -125,21 +125,21 @@ pa_status pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_mappin
 
 int pa_decode_partition_size(int S, int Hq, int Hkv, int B, int max_context_len,
                              int partition_size) {
-  if (B <= 0 || partition_size < 0 || (partition_size > 0 && partition_size % B)) return -1;
+  const int U = pa::kDecodeUnit;
+  if (B <= 0 || partition_size < 0 || (partition_size > 0 && partition_size % U)) return -1;
   if (partition_size > 0) return partition_size;
   // Default: 1024 tokens (64 blocks of 16, one table chunk), halved while the
-  // launch would give fewer than 2048 waves (8 per CU), down to 4 blocks.
+  // launch would give fewer than 2048 waves (8 per CU), down to 64 tokens.
   // Measured on MI355X: for the batch-128 chat workload 1024 beats 512 by 4 %
   // (fewer partials, longer load streams per wave); for the 32/8-head shared
   // prefix workload one 1024-token partition per sequence (no reduce) beats
   // 512 by 20 %.
   const int G = (Hkv > 0 && Hq >= Hkv && Hq % Hkv == 0) ? Hq / Hkv : 1;
   const int64_t waves = pa::decode_waves(G);
-  int P = 64 * B < 1024 ? 64 * B : 1024;
-  if (P < B) P = B;
+  int P = 1024;
   const int64_t units = (int64_t)(S > 0 ? S : 1) * (Hkv > 0 ? Hkv : 1);
   const int maxL = max_context_len > 0 ? max_context_len : 1;
-  while (P > 4 * B && units * ceil_div(maxL, P) * waves < 2048) P /= 2;
+  while (P > 4 * U && units * ceil_div(maxL, P) * waves < 2048) P /= 2;
   return P;
 }
 
@@ -167,12 +167,14 @@ pa_status pa_decode(void* out, const void* query, const void* k_pool, const void
   if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)MB * B)
     return fail(PA_ERR_SHAPE, "pa_decode: max_context_len=%d outside [0, MB*B=%lld]",
                 max_context_len, (long long)MB * B);
-  if (partition_size < 0 || (partition_size > 0 && partition_size % B))
-    return fail(PA_ERR_SHAPE, "pa_decode: partition_size=%d must be 0 or a multiple of B=%d",
-                partition_size, B);
+  if (partition_size < 0 || (partition_size > 0 && partition_size % pa::kDecodeUnit))
+    return fail(PA_ERR_SHAPE, "pa_decode: partition_size=%d must be 0 or a multiple of %d",
+                partition_size, pa::kDecodeUnit);
   const int G = Hq / Hkv;
   if (D != pa::kHeadDim) return fail(PA_ERR_UNSUPPORTED, "pa_decode: D=%d (supported: 128)", D);
-  if (B != 16 && B != 32) return fail(PA_ERR_UNSUPPORTED, "pa_decode: B=%d (supported: 16, 32)", B);
+  if (B % pa::kDecodeUnit)
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode: B=%d (supported: multiples of %d)", B,
+                pa::kDecodeUnit);
   if (G != 1 && G != 2 && G != 4 && G != 8)
     return fail(PA_ERR_UNSUPPORTED, "pa_decode: Hq/Hkv=%d (supported: 1, 2, 4, 8)", G);
   if (!std::isfinite(scale)) return fail(PA_ERR_SHAPE, "pa_decode: scale is not finite");
@@ -214,6 +216,7 @@ pa_status pa_decode(void* out, const void* query, const void* k_pool, const void
   a.Hkv = Hkv;
   a.NB = NB;
   a.MB = MB;
+  a.B = B;
   a.P = P;
   a.Pmax = Pmax;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);

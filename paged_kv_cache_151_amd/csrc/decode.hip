@@ -8,13 +8,15 @@
 //     "How PagedAttention works": two-level indirection (table -> block,
 //     tokens contiguous inside the block) keeps the loads coalesced.
 //
-// Work decomposition. One workgroup of 4 waves per (sequence s, KV head g,
-// context partition p). A partition is P consecutive tokens (P a multiple of
-// B), so it covers whole blocks. Wave w takes the partition's blocks w, w+4,
-// w+8, ... . Inside a wave, lane = 16 * r + c: DPP row r (0..3) holds tokens
-// 4i + r of the block (i = 0 .. B/4-1) and lane c of the row holds dims
-// 8c .. 8c+7, so each 16-byte load of a row reads 256 contiguous bytes and a
-// wave-wide load reads 1 KiB of one contiguous 4 KiB (B = 16) K or V tile.
+// Work decomposition. One workgroup per (sequence s, KV head g, context
+// partition p). A partition is P consecutive tokens, P a multiple of 16; the
+// work unit is 16 tokens of one KV head (a 4 KiB K tile and a 4 KiB V tile),
+// so a block of B tokens is B / 16 units and a partition may start inside a
+// block. The workgroup's waves take the partition's units round-robin.
+// Inside a wave, lane = 16 * r + c: DPP row r (0..3) holds tokens 4i + r of
+// the unit (i = 0..3) and lane c of the row holds dims 8c .. 8c+7, so each
+// 16-byte load of a row reads 256 contiguous bytes and a wave-wide load reads
+// 1 KiB of the contiguous 4 KiB tile.
 //
 // q.K: 4 dot2 per lane, then a sum over the 16 lanes of the DPP row (four
 // DPP adds). Softmax: every lane keeps an online (max, sum) for the tokens of
@@ -187,15 +189,16 @@ __device__ __forceinline__ void merge_state(float& m, float& l, float* acc, floa
 // wave holds the state of at most HPW heads whatever G is. When NH > 1 each
 // K/V tile is loaded by NH waves of the same workgroup: the repeats are
 // served by the caches, HBM traffic is unchanged.
-template <int B, int G, int HPW, int NW, int DEPTH, bool NT>
+template <int BT, int G, int HPW, int NW, int DEPTH, bool NT>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(PA_DECODE_MIN_WAVES_PER_EU)))
 void decode_partition_kernel(const DecodeArgs a) {
   constexpr int D = kHeadDim;
-  constexpr int UPB = B / kUnit;        // units per block
   constexpr int NH = G / HPW;           // head groups
   constexpr int NU = NW / NH;           // unit subsets
-  static_assert(B % kUnit == 0, "block size must be a multiple of 16");
+  static_assert(BT % kUnit == 0, "block size must be a multiple of 16");
+  const int B = BT > 0 ? BT : a.B;      // BT = 0: block size known at run time only
+  const int UPB = B / kUnit;            // units per block
   static_assert(DEPTH == 1 || DEPTH == 2, "prefetch depth 1 or 2");
   static_assert(G % HPW == 0 && NW % NH == 0, "waves must cover the head groups");
   __shared__ float s_acc[NW][HPW][D];
@@ -233,10 +236,13 @@ void decode_partition_kernel(const DecodeArgs a) {
   }
   const int nparts = (L + a.P - 1) / a.P;
   const int len = (tok0 + a.P < L ? tok0 + a.P : L) - tok0;
-  const int blk0 = tok0 / B;
-  const int nblk = (len + B - 1) / B;
   const int nunits = (len + kUnit - 1) / kUnit;
   const int n_full = len / kUnit;        // units with every slot valid
+  // P is a multiple of 16, not necessarily of B: the partition may start
+  // inside a block. U0 is its first unit counted from the sequence start.
+  const int U0 = tok0 / kUnit;
+  const int blk0 = U0 / UPB;
+  const int nblk = (U0 + nunits - 1) / UPB - blk0 + 1;
 
   const int hw0 = hq0 + hgrp * HPW;      // this wave's first query head
   u32x4 q[HPW];
@@ -270,12 +276,17 @@ void decode_partition_kernel(const DecodeArgs a) {
   for (int cb = 0; cb < nblk; cb += 64) {
     const int ce = cb + 64 < nblk ? cb + 64 : nblk;
     const int tbl = cb + lane < ce ? trow[cb + lane] : -1;
-    const int ue = ce * UPB < nunits ? ce * UPB : nunits;
+    // the partition's units (counted from its start) whose block is in [cb, ce)
+    const int ub0 = (blk0 + cb) * UPB - U0;
+    const int ue0 = (blk0 + ce) * UPB - U0;
+    const int ub = ub0 > 0 ? ub0 : 0;
+    const int ue = ue0 < nunits ? ue0 : nunits;
     auto locate = [&](int u) -> int64_t {
-      const int bi = u / UPB;
-      const int phys = __builtin_amdgcn_readlane(tbl, bi - cb);
+      const int au = U0 + u;
+      const int bi = au / UPB;
+      const int phys = __builtin_amdgcn_readlane(tbl, bi - blk0 - cb);
       const int safe = (unsigned)phys < (unsigned)a.NB ? phys : 0;
-      return (((int64_t)safe * a.Hkv + g) * B + (u - bi * UPB) * kUnit) * D;
+      return (((int64_t)safe * a.Hkv + g) * B + (au - bi * UPB) * kUnit) * D;
     };
     // Loads unit u, or issues a no-op load when u is past the wave's last unit.
     auto fetch = [&](Tile& t, int u) {
@@ -293,7 +304,7 @@ void decode_partition_kernel(const DecodeArgs a) {
         process_tile<HPW, true>(t, q, m, l, acc, a.scale_log2, tok0 + u * kUnit + r, L);
       }
     };
-    int u = cb * UPB + usub;
+    int u = ub + usub;
     if (u >= ue) continue;
     if (DEPTH == 1) {
       Tile t0, t1;
@@ -423,24 +434,24 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(const DecodeArgs a, i
   o[1] = (_Float16)(den > 0.f ? n1 / den : 0.f);
 }
 
-template <int B, int G>
+template <int BT, int G>
 hipError_t launch_partition(const DecodeArgs& a, hipStream_t stream) {
   constexpr int HPW = G < kDecodeHeadsPerWave ? G : kDecodeHeadsPerWave;
   constexpr int NH = G / HPW;
   constexpr int NW = decode_waves(G) > NH ? decode_waves(G) : NH;
   const int64_t grid = (int64_t)a.Pmax * a.S * a.Hkv;
-  decode_partition_kernel<B, G, HPW, NW, kDecodeDepth, kDecodeNontemporal>
+  decode_partition_kernel<BT, G, HPW, NW, kDecodeDepth, kDecodeNontemporal>
       <<<(unsigned)grid, NW * 64, 0, stream>>>(a);
   return hipGetLastError();
 }
 
-template <int B>
+template <int BT>
 hipError_t launch_partition_g(const DecodeArgs& a, int G, hipStream_t stream) {
   switch (G) {
-    case 1: return launch_partition<B, 1>(a, stream);
-    case 2: return launch_partition<B, 2>(a, stream);
-    case 4: return launch_partition<B, 4>(a, stream);
-    case 8: return launch_partition<B, 8>(a, stream);
+    case 1: return launch_partition<BT, 1>(a, stream);
+    case 2: return launch_partition<BT, 2>(a, stream);
+    case 4: return launch_partition<BT, 4>(a, stream);
+    case 8: return launch_partition<BT, 8>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -449,10 +460,10 @@ hipError_t launch_partition_g(const DecodeArgs& a, int G, hipStream_t stream) {
 
 hipError_t launch_decode(const DecodeArgs& a, int B, int G, hipStream_t stream) {
   hipError_t e;
-  switch (B) {
+  switch (B) {   // the common block sizes are compile-time specialisations
     case 16: e = launch_partition_g<16>(a, G, stream); break;
     case 32: e = launch_partition_g<32>(a, G, stream); break;
-    default: return hipErrorInvalidValue;
+    default: e = launch_partition_g<0>(a, G, stream); break;
   }
   if (e != hipSuccess || a.Pmax <= 1) return e;
   const int64_t grid = (int64_t)a.S * a.Hq;

@@ -7,6 +7,7 @@
 namespace pa {
 
 constexpr int kHeadDim = 128;        // decode kernels are specialised for D = 128
+constexpr int kDecodeUnit = 16;      // tokens per decode work unit; B and P are multiples
 // Decode tuning parameters (compile-time): waves per workgroup, software
 // prefetch depth in 16-token units, and whether K/V loads carry the
 // non-temporal hint. Defaults are the fastest measured on MI355X for the
@@ -56,7 +57,8 @@ struct DecodeArgs {
   float* part_acc;                   // [S][Hq][Pmax][D]   (unused when Pmax == 1)
   float* part_ml;                    // [S][Hq][Pmax][2]   (running max, sum; log2 domain)
   int S, Hq, Hkv, NB, MB;
-  int P;                             // partition size in tokens (multiple of B)
+  int B;                             // block size in tokens (multiple of 16)
+  int P;                             // partition size in tokens (multiple of 16)
   int Pmax;                          // partitions the launch covers
   float scale_log2;                  // softmax scale times log2(e)
 };

@@ -69,7 +69,8 @@ def test_decode_host_validation(lib):
     assert decode(lib, B=8, NB=16, MB=6) == PA_ERR_UNSUPPORTED
     assert decode(lib, Hq=48, Hkv=4) == PA_ERR_UNSUPPORTED      # group of 12
     assert decode(lib, maxL=49) == PA_ERR_SHAPE                 # beyond MB * B
-    assert decode(lib, P=24) == PA_ERR_SHAPE                    # not a multiple of B
+    assert decode(lib, P=24) == PA_ERR_SHAPE                    # not a multiple of 16
+    assert decode(lib, B=40, NB=16, MB=2) == PA_ERR_UNSUPPORTED   # block not a multiple of 16
     assert decode(lib, q=FAKE + 4) == PA_ERR_ALIGN
     assert decode(lib, scale=float("inf")) == PA_ERR_SHAPE
     # two partitions need a workspace
@@ -85,6 +86,7 @@ def test_workspace_and_partition_sizing(lib):
     assert ps(64, 32, 8, 16, 993, 0) == 1024      # grouped heads: one partition per sequence
     assert ps(1, 1, 1, 16, 100, 48) == 48
     assert ps(1, 1, 1, 16, 100, 40) == -1
+    assert ps(1, 1, 1, 32, 100, 48) == 48        # partitions may start inside a block
     P = ps(16, 32, 32, 32, 4096, 0)
     assert P % 32 == 0
     assert ws(16, 32, 32, 128, 32, 4096, 512) == 16 * 32 * 8 * 130 * 4

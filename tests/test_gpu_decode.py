@@ -276,3 +276,22 @@ def test_chat_batch128_full_size_sampled(pa):
             ref = oracle.decode(c.query[s:s + 1], k1, v1, table, L, c.scale)
             assert_attention_close(got[s:s + 1], ref, f"{c.name} seq {s}")
         del kp, vp
+
+
+@pytest.mark.parametrize("B", [48, 64, 128, 256])
+@pytest.mark.parametrize("G", [1, 4])
+def test_other_block_sizes_and_partitions_inside_blocks(pa, B, G):
+    lens = [1, 15, B - 1, B, B + 17, 3 * B + 5, 700]
+    c = W.make_case(f"B{B}_G{G}", 2000 + B + G, lens, Hq=2 * G, Hkv=2, B=B)
+    for ps in (0, 16, 48, 2 * B, 1024):
+        check_case(pa, c, partition_size=ps)
+
+
+def test_contiguous_layout_one_block_per_sequence(pa):
+    # the pre-paging layout: every sequence in one block as long as the longest
+    lens = [1000, 37, 512, 999, 640]
+    B = 1008
+    c = W.make_case("contiguous", 2100, lens, Hq=8, Hkv=8, B=B)
+    assert c.MB == 1
+    for ps in (0, 256, 1008):
+        check_case(pa, c, partition_size=ps)

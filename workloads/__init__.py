@@ -191,19 +191,29 @@ def chat_lengths(seed: int = CHAT_SEED, S: int = 128) -> np.ndarray:
 
 
 def chat_layer(layer: int, seed: int = CHAT_SEED, S: int = 128, with_pools: bool = False,
-               lengths: Optional[np.ndarray] = None) -> DecodeCase:
+               lengths: Optional[np.ndarray] = None, B: int = 16,
+               contiguous: bool = False) -> DecodeCase:
     """One layer of the batch-128 chat workload (32 heads, B = 16, 1.25x pool).
 
     All layers share the lengths; each layer has its own shuffle, query and new
-    K/V (rng seeded with seed * 1000 + layer). Pools are large (about 1.7 GB
+    K/V (rng seeded with seed * 1000 + layer). `B` changes the block size;
+    `contiguous=True` gives every sequence one block as long as the longest
+    sequence (the pre-paging layout), in a pool of exactly S blocks. Pools are large (about 1.7 GB
     each), so by default they are not drawn here: `device_pools` draws them on
     the GPU. `with_pools=True` draws them on the host (slow; small S only).
     """
     if lengths is None:
         lengths = chat_lengths(seed, S)
+    lengths = np.asarray(lengths, np.int32)
     rng = np.random.default_rng(seed * 1000 + layer)
-    case = _finish_case(f"chat_b{S}_layer{layer}", seed, rng, np.asarray(lengths, np.int32),
-                        32, 32, 16, HEAD_DIM, None, (5, 4), None, with_pools)
+    NB = None
+    if contiguous:
+        # the layout before paging: one region per sequence, sized for the
+        # longest sequence of the batch (a multiple of 16 tokens)
+        B = -(-int(lengths.max()) // 16) * 16
+        NB = len(lengths)
+    case = _finish_case(f"chat_b{S}_layer{layer}", seed, rng, lengths,
+                        32, 32, B, HEAD_DIM, NB, (5, 4), None, with_pools)
     case.extra["layer"] = layer
     return case
 

@@ -49,7 +49,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="chat",
-                    choices=["chat", "7b", "shared_prefix", "long_context", "tiny"])
+                    choices=["chat", "7b", "shared_prefix", "long_context", "tiny", "block_manager"])
     ap.add_argument("--layers", type=int, default=32, help="chat workload: layers per step")
     ap.add_argument("--block-size", type=int, default=16, help="chat workload: tokens per block")
     ap.add_argument("--contiguous", action="store_true",
@@ -215,8 +215,64 @@ def time_copy_on_write(pa, extra):
             "bytes_read_plus_written": moved, "GBs": round(moved / us / 1e3, 1)}
 
 
+def bench_block_manager(args):
+    """Host block manager (pa_bm_*): the bookkeeping of one decode step of the
+    batch-128 chat workload -- one token appended to each sequence, then the
+    batch's block tables and lengths exported for pa_decode. The oracle's
+    Python manager does the same steps as the CPU baseline."""
+    import paged_kv_cache_151_amd as pa
+    import oracle
+    import workloads as W
+    lengths = W.chat_lengths()
+    S, B = len(lengths), 16
+    NB = W.pool_blocks(sum(W.row_len(L, B) for L in lengths))
+    MB = W.row_len(int(lengths.max()) + args.steps + args.warmup + 1, B)
+    m = pa.BlockManager(NB, B)
+    seqs = [m.add_sequence() for _ in range(S)]
+    t0 = time.perf_counter()
+    for sid, L in zip(seqs, lengths):
+        m.append_tokens([sid] * (int(L) - 1))
+    prefill_s = time.perf_counter() - t0
+    ids = np.array(seqs, np.int32)
+    for _ in range(args.warmup):
+        m.append_tokens(ids)
+        m.export(ids, MB)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        m.append_tokens(ids)
+        m.export(ids, MB)
+    us = (time.perf_counter() - t0) / args.steps * 1e6
+    # the oracle's manager on the same work (prefill excluded from its timing too)
+    ref = oracle.BlockManager(NB, B)
+    tables = [[] for _ in range(S)]
+    for t, L in zip(tables, lengths):
+        for _ in range(int(L) - 1):
+            ref.append_token(t)
+    n_ref = max(1, min(args.steps, 20))
+    t0 = time.perf_counter()
+    for _ in range(n_ref):
+        for t in tables:
+            ref.append_token(t)
+        np.array([t + [-1] * (MB - len(t)) for t in tables], np.int32)
+    ref_us = (time.perf_counter() - t0) / n_ref * 1e6
+    res = {
+        "metric": "host block manager: one decode step of bookkeeping (append + export), batch 128",
+        "value": round(us, 2), "unit": "us/step", "n_gpus": 0, "steps": args.steps,
+        "warmup": args.warmup, "higher_is_better": False, "data": "synthetic",
+        "config": {"workload": "chat lengths (prompt U[100,2000] + generated U[50,500]), 128 sequences",
+                   "pool_blocks": NB, "block_size": B, "table_width": MB,
+                   "prefill_tokens": int((lengths - 1).sum()), "prefill_s": round(prefill_s, 3)},
+        "cpu_baseline": {"value": round(ref_us, 1), "unit": "us/step", "cores": 1, "kind": "oracle",
+                         "sample": f"oracle's Python manager, {n_ref} steps"},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
+    if args.workload == "block_manager":
+        bench_block_manager(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the decode path has no cross-GPU step "
               "(sequences and KV heads shard with no exchange); run with --gpus 1",

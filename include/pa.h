@@ -66,7 +66,9 @@ typedef enum {
   PA_ERR_ALIGN = 3,       /* a pointer is not aligned as documented */
   PA_ERR_UNSUPPORTED = 4, /* valid but not implemented: D, B or group size */
   PA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than pa_decode_workspace_bytes */
-  PA_ERR_HIP = 6          /* the HIP runtime reported an error at launch */
+  PA_ERR_HIP = 6,         /* the HIP runtime reported an error at launch */
+  PA_ERR_EXHAUSTED = 7,   /* block manager: no free block left (queue or preempt a request) */
+  PA_ERR_STATE = 8        /* block manager: unknown or released sequence id, or a full table */
 } pa_status;
 
 /* Short constant name of a status code ("PA_OK", ...). Never NULL. */
@@ -199,6 +201,74 @@ pa_status pa_decode(void* out, const void* query, const void* k_pool, const void
                     int Hkv, int D, int B, int NB, int MB, int max_context_len, float scale,
                     int partition_size, void* workspace, size_t workspace_bytes,
                     hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Host block manager ([L], "How PagedAttention works", steps 1-3 and 5;
+ * "Memory sharing across requests"; "Practice: try it yourself").
+ *
+ * Host-side bookkeeping that decides where tokens go and when blocks are
+ * copied; it produces the host arrays that the device calls above consume
+ * (slot mappings, block tables, context lengths, copy pairs). All pointers in
+ * these calls are HOST memory. A manager is not thread-safe: use one per
+ * thread or lock around it. Behaviour:
+ *   - a free list of physical ids, handed out from the front, returned to the
+ *     back when a block's reference count reaches zero;
+ *   - appending a token to a sequence takes a fresh block when the sequence
+ *     has none or its last block is full; otherwise, if the last block is
+ *     shared (reference count > 1), the sequence gets a fresh block holding a
+ *     copy of the slots written so far (the pair (old, new) is reported for
+ *     pa_copy_blocks), the old block's count drops by one and the table entry
+ *     is repointed; the token then takes the next slot of its last block;
+ *   - fork: a new sequence shares every block of its parent;
+ *   - release: every block of the sequence loses one reference.
+ * ------------------------------------------------------------------------- */
+typedef struct pa_block_manager pa_block_manager;
+
+/* Creates a manager for a pool of num_blocks blocks of block_size tokens.
+ * max_blocks_per_seq bounds one table (0 = num_blocks). */
+pa_status pa_bm_create(int num_blocks, int block_size, int max_blocks_per_seq,
+                       pa_block_manager** out);
+void pa_bm_destroy(pa_block_manager* bm);
+
+/* A new empty sequence; its id (small integer, reused after release) goes to *seq_id. */
+pa_status pa_bm_add_sequence(pa_block_manager* bm, int* seq_id);
+
+/* A new sequence sharing every block (and the token count) of `parent`. */
+pa_status pa_bm_fork(pa_block_manager* bm, int parent, int* child);
+
+/*
+ * Appends one token to each of the n listed sequences, in order (a sequence
+ * may appear several times). slots[i] receives token i's pool-wide slot
+ * (block * block_size + offset). Copy-on-write pairs (src, dst) are written
+ * to copy_pairs[2k], copy_pairs[2k+1] (capacity max_copies pairs; n pairs
+ * always suffice) and their number to *n_copies; copy them with
+ * pa_copy_blocks before writing the tokens with pa_write_kv. Tokens are
+ * applied one by one: on PA_ERR_EXHAUSTED or PA_ERR_STATE, *n_applied tokens
+ * (and their copies) took effect and the rest did not.
+ */
+pa_status pa_bm_append_tokens(pa_block_manager* bm, const int* seq_ids, int n, int64_t* slots,
+                              int32_t* copy_pairs, int max_copies, int* n_copies,
+                              int* n_applied);
+
+/* Drops the sequence; blocks whose count reaches zero return to the free list.
+ * *n_freed (may be NULL) receives how many did. */
+pa_status pa_bm_release(pa_block_manager* bm, int seq_id, int* n_freed);
+
+/* Block table row and context length of one sequence: row[0 .. *n_blocks) is
+ * written (capacity max_len entries). *num_tokens may be NULL. With row ==
+ * NULL and max_len == 0 only *n_blocks and *num_tokens are reported. */
+pa_status pa_bm_get_table(const pa_block_manager* bm, int seq_id, int32_t* row, int max_len,
+                          int* n_blocks, int64_t* num_tokens);
+
+/* Tables for a batch in pa_decode's layout: tables[i][0 .. MB) for sequence
+ * seq_ids[i] (unused entries -1) and context_lens[i]. PA_ERR_SHAPE if a table
+ * is longer than MB. */
+pa_status pa_bm_export(const pa_block_manager* bm, const int* seq_ids, int n, int32_t* tables,
+                       int MB, int32_t* context_lens);
+
+/* Pool accounting: free blocks, and the reference count of one block (0 when free). */
+int pa_bm_num_free(const pa_block_manager* bm);
+int pa_bm_refcount(const pa_block_manager* bm, int block);
 
 #ifdef __cplusplus
 }

@@ -44,6 +44,27 @@ _lib.pa_decode.restype = _i
 _lib.pa_decode.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i,
                            ctypes.c_float, _i, _p, ctypes.c_size_t, _p]
 
+_lib.pa_bm_create.restype = _i
+_lib.pa_bm_create.argtypes = [_i, _i, _i, ctypes.POINTER(_p)]
+_lib.pa_bm_destroy.restype = None
+_lib.pa_bm_destroy.argtypes = [_p]
+_lib.pa_bm_add_sequence.restype = _i
+_lib.pa_bm_add_sequence.argtypes = [_p, ctypes.POINTER(_i)]
+_lib.pa_bm_fork.restype = _i
+_lib.pa_bm_fork.argtypes = [_p, _i, ctypes.POINTER(_i)]
+_lib.pa_bm_append_tokens.restype = _i
+_lib.pa_bm_append_tokens.argtypes = [_p, _p, _i, _p, _p, _i, ctypes.POINTER(_i), ctypes.POINTER(_i)]
+_lib.pa_bm_release.restype = _i
+_lib.pa_bm_release.argtypes = [_p, _i, ctypes.POINTER(_i)]
+_lib.pa_bm_get_table.restype = _i
+_lib.pa_bm_get_table.argtypes = [_p, _i, _p, _i, ctypes.POINTER(_i), ctypes.POINTER(ctypes.c_int64)]
+_lib.pa_bm_export.restype = _i
+_lib.pa_bm_export.argtypes = [_p, _p, _i, _p, _i, _p]
+_lib.pa_bm_num_free.restype = _i
+_lib.pa_bm_num_free.argtypes = [_p]
+_lib.pa_bm_refcount.restype = _i
+_lib.pa_bm_refcount.argtypes = [_p, _i]
+
 PA_OK = 0
 
 
@@ -136,6 +157,97 @@ def pa_decode(query, k_pool, v_pool, block_tables, context_lens, max_context_len
     return out
 
 
+# ---------------------------------------------------------------------------
+# Host block manager (host numpy arrays; see the pa_bm_* calls in include/pa.h)
+# ---------------------------------------------------------------------------
+
+import numpy as _np
+
+
+def _np_ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+class BlockManager:
+    """Owner of one native pa_block_manager; every method is one pa_bm_* call."""
+
+    def __init__(self, num_blocks: int, block_size: int, max_blocks_per_seq: int = 0):
+        h = _p()
+        _check("pa_bm_create", _lib.pa_bm_create(num_blocks, block_size, max_blocks_per_seq,
+                                                 ctypes.byref(h)))
+        self._h = h
+        self.block_size = block_size
+
+    def close(self):
+        if self._h:
+            _lib.pa_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def add_sequence(self) -> int:
+        out = _i()
+        _check("pa_bm_add_sequence", _lib.pa_bm_add_sequence(self._h, ctypes.byref(out)))
+        return out.value
+
+    def fork(self, parent: int) -> int:
+        out = _i()
+        _check("pa_bm_fork", _lib.pa_bm_fork(self._h, parent, ctypes.byref(out)))
+        return out.value
+
+    def append_tokens(self, seq_ids):
+        """One token per listed sequence. Returns (slots int64 [n], copy pairs int32 [k, 2]).
+        Raises PaError (with .n_applied) when the pool is exhausted mid-batch."""
+        ids = _np.ascontiguousarray(seq_ids, dtype=_np.int32)
+        n = len(ids)
+        slots = _np.empty(n, dtype=_np.int64)
+        pairs = _np.empty((max(n, 1), 2), dtype=_np.int32)
+        nc, na = _i(), _i()
+        st = _lib.pa_bm_append_tokens(self._h, _np_ptr(ids), n, _np_ptr(slots), _np_ptr(pairs), n,
+                                      ctypes.byref(nc), ctypes.byref(na))
+        if st != PA_OK:
+            err = PaError("pa_bm_append_tokens", st)
+            err.n_applied = na.value
+            err.slots = slots[:na.value].copy()
+            err.copy_pairs = pairs[:nc.value].copy()
+            raise err
+        return slots, pairs[:nc.value].copy()
+
+    def release(self, seq_id: int) -> int:
+        out = _i()
+        _check("pa_bm_release", _lib.pa_bm_release(self._h, seq_id, ctypes.byref(out)))
+        return out.value
+
+    def table(self, seq_id: int):
+        """(block ids int32 [n], number of tokens)."""
+        nb, nt = _i(), ctypes.c_int64()
+        _check("pa_bm_get_table", _lib.pa_bm_get_table(self._h, seq_id, None, 0, ctypes.byref(nb),
+                                                        ctypes.byref(nt)))
+        row = _np.empty(max(nb.value, 1), dtype=_np.int32)
+        _check("pa_bm_get_table", _lib.pa_bm_get_table(self._h, seq_id, _np_ptr(row), len(row),
+                                                        ctypes.byref(nb), ctypes.byref(nt)))
+        return row[:nb.value].copy(), nt.value
+
+    def export(self, seq_ids, MB: int):
+        """pa_decode inputs for a batch: (block_tables int32 [n, MB], context_lens int32 [n])."""
+        ids = _np.ascontiguousarray(seq_ids, dtype=_np.int32)
+        tables = _np.empty((len(ids), MB), dtype=_np.int32)
+        lens = _np.empty(len(ids), dtype=_np.int32)
+        _check("pa_bm_export", _lib.pa_bm_export(self._h, _np_ptr(ids), len(ids), _np_ptr(tables),
+                                                 MB, _np_ptr(lens)))
+        return tables, lens
+
+    def num_free(self) -> int:
+        return _lib.pa_bm_num_free(self._h)
+
+    def refcount(self, block: int) -> int:
+        return _lib.pa_bm_refcount(self._h, block)
+
+
 __all__ = ["PaError", "lib", "LIB_PATH", "pa_version", "pa_slot_mapping", "pa_write_kv",
            "pa_copy_blocks", "pa_decode_partition_size", "pa_decode_workspace_bytes",
-           "pa_decode"]
+           "pa_decode", "BlockManager"]

@@ -34,7 +34,8 @@ def hipcc() -> str:
 
 
 def sources():
-    return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
+    csrc = os.path.join(PKG, "csrc")
+    return sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.cpp")))
 
 
 def build(verbose: bool = False) -> str:

@@ -6,11 +6,14 @@
 #include <cmath>
 
 #include "pa.h"
+#include "pa_error.h"
 #include "pa_internal.h"
 
-namespace {
+namespace pa {
 
+namespace {
 thread_local char g_err[512] = "";
+}  // namespace
 
 pa_status fail(pa_status st, const char* fmt, ...) {
   va_list ap;
@@ -24,6 +27,15 @@ pa_status ok() {
   g_err[0] = '\0';
   return PA_OK;
 }
+
+const char* last_error() { return g_err; }
+
+}  // namespace pa
+
+namespace {
+
+using pa::fail;
+using pa::ok;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -47,11 +59,13 @@ const char* pa_status_str(int status) {
     case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE";
     case PA_ERR_HIP: return "PA_ERR_HIP";
+    case PA_ERR_EXHAUSTED: return "PA_ERR_EXHAUSTED";
+    case PA_ERR_STATE: return "PA_ERR_STATE";
     default: return "PA_ERR_UNKNOWN";
   }
 }
 
-const char* pa_last_error(void) { return g_err; }
+const char* pa_last_error(void) { return pa::last_error(); }
 
 int pa_version(void) { return 100; }
 

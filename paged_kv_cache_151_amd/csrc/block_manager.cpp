@@ -1,0 +1,220 @@
+// Host block manager: free list, reference counts, on-demand allocation,
+// fork, copy-on-write decisions and release. Declared in include/pa.h.
+//
+// [L] "Paged Attention: OS-Inspired Memory Management for KV Caches":
+//     "How PagedAttention works" (prefill takes just enough blocks, new tokens
+//     fill the last block, a full last block triggers one more, blocks go back
+//     to the free list when the request ends), "Memory sharing across
+//     requests" (reference counts, copy-on-write of a shared block before a
+//     write), "Practice: try it yourself" (the same manager in miniature).
+//
+// Host memory only; no GPU call is made here. The device-side copy that a
+// copy-on-write decision requires is reported as a (src, dst) pair for
+// pa_copy_blocks.
+#include <cstdint>
+#include <deque>
+#include <set>
+#include <vector>
+
+#include "pa.h"
+#include "pa_error.h"
+
+struct pa_block_manager {
+  struct Seq {
+    bool live = false;
+    std::vector<int32_t> table;   // physical block of logical block i
+    int64_t tokens = 0;
+  };
+
+  int num_blocks = 0;
+  int block_size = 0;
+  int max_blocks_per_seq = 0;
+  std::deque<int32_t> free_list;  // handed out from the front, returned to the back
+  std::vector<int32_t> refs;      // sequences using each block (0 = free)
+  std::vector<int32_t> fill;      // slots of each block already written
+  std::vector<Seq> seqs;
+  std::set<int> free_ids;         // released sequence ids, reused smallest first
+
+  int32_t take() {
+    const int32_t b = free_list.front();
+    free_list.pop_front();
+    refs[b] = 1;
+    fill[b] = 0;
+    return b;
+  }
+
+  int new_id() {
+    if (!free_ids.empty()) {
+      const int id = *free_ids.begin();
+      free_ids.erase(free_ids.begin());
+      return id;
+    }
+    seqs.emplace_back();
+    return (int)seqs.size() - 1;
+  }
+
+  bool valid(int id) const { return id >= 0 && id < (int)seqs.size() && seqs[id].live; }
+};
+
+namespace {
+
+using pa::fail;
+using pa::ok;
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_bm_create(int num_blocks, int block_size, int max_blocks_per_seq,
+                       pa_block_manager** out) {
+  if (!out) return fail(PA_ERR_NULL, "pa_bm_create: out is NULL");
+  *out = nullptr;
+  if (num_blocks <= 0 || block_size <= 0 || max_blocks_per_seq < 0)
+    return fail(PA_ERR_SHAPE, "pa_bm_create: num_blocks=%d block_size=%d max_blocks_per_seq=%d",
+                num_blocks, block_size, max_blocks_per_seq);
+  pa_block_manager* bm = new pa_block_manager();
+  bm->num_blocks = num_blocks;
+  bm->block_size = block_size;
+  bm->max_blocks_per_seq = max_blocks_per_seq > 0 ? max_blocks_per_seq : num_blocks;
+  bm->refs.assign(num_blocks, 0);
+  bm->fill.assign(num_blocks, 0);
+  for (int b = 0; b < num_blocks; ++b) bm->free_list.push_back(b);
+  *out = bm;
+  return ok();
+}
+
+void pa_bm_destroy(pa_block_manager* bm) { delete bm; }
+
+pa_status pa_bm_add_sequence(pa_block_manager* bm, int* seq_id) {
+  if (!bm || !seq_id) return fail(PA_ERR_NULL, "pa_bm_add_sequence: null argument");
+  const int id = bm->new_id();
+  bm->seqs[id] = pa_block_manager::Seq();
+  bm->seqs[id].live = true;
+  *seq_id = id;
+  return ok();
+}
+
+pa_status pa_bm_fork(pa_block_manager* bm, int parent, int* child) {
+  if (!bm || !child) return fail(PA_ERR_NULL, "pa_bm_fork: null argument");
+  if (!bm->valid(parent)) return fail(PA_ERR_STATE, "pa_bm_fork: no live sequence %d", parent);
+  const int id = bm->new_id();
+  pa_block_manager::Seq& p = bm->seqs[parent];   // new_id may grow seqs: take the reference after
+  for (int32_t b : p.table) bm->refs[b] += 1;
+  pa_block_manager::Seq c;
+  c.live = true;
+  c.table = p.table;
+  c.tokens = p.tokens;
+  bm->seqs[id] = c;
+  *child = id;
+  return ok();
+}
+
+pa_status pa_bm_append_tokens(pa_block_manager* bm, const int* seq_ids, int n, int64_t* slots,
+                              int32_t* copy_pairs, int max_copies, int* n_copies,
+                              int* n_applied) {
+  if (!bm || !n_copies || !n_applied || (n > 0 && (!seq_ids || !slots)))
+    return fail(PA_ERR_NULL, "pa_bm_append_tokens: null argument");
+  *n_copies = 0;
+  *n_applied = 0;
+  if (n < 0 || max_copies < 0) return fail(PA_ERR_SHAPE, "pa_bm_append_tokens: n=%d", n);
+  if (max_copies > 0 && !copy_pairs)
+    return fail(PA_ERR_NULL, "pa_bm_append_tokens: copy_pairs is NULL");
+  const int B = bm->block_size;
+  for (int i = 0; i < n; ++i) {
+    const int id = seq_ids[i];
+    if (!bm->valid(id)) return fail(PA_ERR_STATE, "pa_bm_append_tokens: no live sequence %d", id);
+    pa_block_manager::Seq& q = bm->seqs[id];
+    const int32_t last = q.table.empty() ? -1 : q.table.back();
+    if (last < 0 || bm->fill[last] == B) {
+      // no block yet, or the last one is full: take one more
+      if ((int)q.table.size() >= bm->max_blocks_per_seq)
+        return fail(PA_ERR_STATE, "pa_bm_append_tokens: sequence %d has %d blocks (maximum)", id,
+                    (int)q.table.size());
+      if (bm->free_list.empty())
+        return fail(PA_ERR_EXHAUSTED, "pa_bm_append_tokens: no free block (token %d)", i);
+      q.table.push_back(bm->take());
+    } else if (bm->refs[last] > 1) {
+      // the last block is shared: copy it before writing
+      if (bm->free_list.empty())
+        return fail(PA_ERR_EXHAUSTED, "pa_bm_append_tokens: no free block for a copy (token %d)", i);
+      if (*n_copies >= max_copies)
+        return fail(PA_ERR_SHAPE, "pa_bm_append_tokens: more than %d copies", max_copies);
+      const int32_t fresh = bm->take();
+      bm->fill[fresh] = bm->fill[last];
+      bm->refs[last] -= 1;
+      copy_pairs[2 * *n_copies] = last;
+      copy_pairs[2 * *n_copies + 1] = fresh;
+      *n_copies += 1;
+      q.table.back() = fresh;
+    }
+    const int32_t blk = q.table.back();
+    const int32_t off = bm->fill[blk];
+    bm->fill[blk] = off + 1;
+    q.tokens += 1;
+    slots[i] = (int64_t)blk * B + off;
+    *n_applied = i + 1;
+  }
+  return ok();
+}
+
+pa_status pa_bm_release(pa_block_manager* bm, int seq_id, int* n_freed) {
+  if (!bm) return fail(PA_ERR_NULL, "pa_bm_release: null manager");
+  if (!bm->valid(seq_id)) return fail(PA_ERR_STATE, "pa_bm_release: no live sequence %d", seq_id);
+  pa_block_manager::Seq& q = bm->seqs[seq_id];
+  int freed = 0;
+  for (int32_t b : q.table) {
+    if (--bm->refs[b] == 0) {
+      bm->fill[b] = 0;
+      bm->free_list.push_back(b);
+      ++freed;
+    }
+  }
+  q = pa_block_manager::Seq();
+  bm->free_ids.insert(seq_id);
+  if (n_freed) *n_freed = freed;
+  return ok();
+}
+
+pa_status pa_bm_get_table(const pa_block_manager* bm, int seq_id, int32_t* row, int max_len,
+                          int* n_blocks, int64_t* num_tokens) {
+  if (!bm || !n_blocks) return fail(PA_ERR_NULL, "pa_bm_get_table: null argument");
+  if (!bm->valid(seq_id)) return fail(PA_ERR_STATE, "pa_bm_get_table: no live sequence %d", seq_id);
+  const pa_block_manager::Seq& q = bm->seqs[seq_id];
+  const int nb = (int)q.table.size();
+  *n_blocks = nb;
+  if (num_tokens) *num_tokens = q.tokens;
+  if (!row && max_len == 0) return ok();   // size query
+  if (nb > 0 && (!row || max_len < nb))
+    return fail(PA_ERR_SHAPE, "pa_bm_get_table: row holds %d entries, table has %d", max_len, nb);
+  for (int j = 0; j < nb; ++j) row[j] = q.table[j];
+  return ok();
+}
+
+pa_status pa_bm_export(const pa_block_manager* bm, const int* seq_ids, int n, int32_t* tables,
+                       int MB, int32_t* context_lens) {
+  if (!bm || (n > 0 && (!seq_ids || !tables || !context_lens)))
+    return fail(PA_ERR_NULL, "pa_bm_export: null argument");
+  if (n < 0 || MB <= 0) return fail(PA_ERR_SHAPE, "pa_bm_export: n=%d MB=%d", n, MB);
+  for (int i = 0; i < n; ++i) {
+    const int id = seq_ids[i];
+    if (!bm->valid(id)) return fail(PA_ERR_STATE, "pa_bm_export: no live sequence %d", id);
+    const pa_block_manager::Seq& q = bm->seqs[id];
+    if ((int)q.table.size() > MB)
+      return fail(PA_ERR_SHAPE, "pa_bm_export: sequence %d has %d blocks > MB=%d", id,
+                  (int)q.table.size(), MB);
+    if (q.tokens > INT32_MAX) return fail(PA_ERR_SHAPE, "pa_bm_export: sequence %d too long", id);
+    int32_t* row = tables + (int64_t)i * MB;
+    for (int j = 0; j < MB; ++j) row[j] = j < (int)q.table.size() ? q.table[j] : -1;
+    context_lens[i] = (int32_t)q.tokens;
+  }
+  return ok();
+}
+
+int pa_bm_num_free(const pa_block_manager* bm) { return bm ? (int)bm->free_list.size() : -1; }
+
+int pa_bm_refcount(const pa_block_manager* bm, int block) {
+  if (!bm || block < 0 || block >= bm->num_blocks) return -1;
+  return bm->refs[block];
+}
+
+}  // extern "C"

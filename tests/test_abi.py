@@ -34,7 +34,8 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert {"pa_decode", "pa_write_kv", "pa_copy_blocks", "pa_slot_mapping"} <= set(names)
+    assert {"pa_decode", "pa_write_kv", "pa_copy_blocks", "pa_slot_mapping", "pa_bm_create",
+            "pa_bm_append_tokens", "pa_bm_fork", "pa_bm_release", "pa_bm_export"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -42,6 +43,8 @@ def test_every_declared_symbol_is_exported(lib):
 def test_status_strings(lib):
     assert lib.pa_status_str(0) == b"PA_OK"
     assert lib.pa_status_str(5) == b"PA_ERR_WORKSPACE"
+    assert lib.pa_status_str(7) == b"PA_ERR_EXHAUSTED"
+    assert lib.pa_status_str(8) == b"PA_ERR_STATE"
     assert lib.pa_status_str(99) == b"PA_ERR_UNKNOWN"
     assert lib.pa_version() >= 100
 

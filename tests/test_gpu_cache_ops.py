@@ -121,3 +121,55 @@ def test_calls_with_zero_work_are_no_ops(pa):
                    torch.zeros((0, 1, 128), dtype=torch.float16, device="cuda"), kp, kp.clone(),
                    torch.zeros(0, dtype=torch.int64, device="cuda"))
     assert not host(kp).any()
+
+
+def test_native_block_manager_drives_the_device_path(pa):
+    """Prompt -> fork into samples -> each sample generates tokens, all through
+    the native manager (host), whose slots and copy pairs drive pa_copy_blocks,
+    pa_write_kv and pa_decode on the GPU. The oracle replays the same steps
+    with its own manager, write, copy and decode."""
+    rng = np.random.default_rng(77)
+    NB, H, B, D = 96, 4, 16, 128
+    kpool = W.f16_normal(rng, (NB, H, B, D))
+    vpool = W.f16_normal(rng, (NB, H, B, D))
+    kp, vp = dev(kpool), dev(vpool)
+    rk, rv = kpool, vpool
+    nat = pa.BlockManager(NB, B)
+    ref = oracle.BlockManager(NB, B)
+
+    def step(nat_ids, ref_tables):
+        """One token for each listed sequence: copies first, then the write."""
+        nonlocal rk, rv
+        keys = W.f16_normal(rng, (len(nat_ids), H, D))
+        vals = W.f16_normal(rng, (len(nat_ids), H, D))
+        slots, copies = nat.append_tokens(nat_ids)
+        c0 = len(ref.copies)
+        ref_slots = [ref.append_token(t) for t in ref_tables]
+        assert slots.tolist() == ref_slots
+        assert [tuple(p) for p in copies.tolist()] == ref.copies[c0:]
+        if len(copies):
+            pa.pa_copy_blocks(kp, vp, dev(copies))
+            rk, rv = oracle.copy_blocks(rk, rv, copies)
+        pa.pa_write_kv(dev(keys), dev(vals), kp, vp, dev(slots))
+        rk, rv = oracle.write_kv(rk, rv, keys, vals, np.array(ref_slots))
+
+    prompt = nat.add_sequence()
+    rprompt = []
+    say("native manager: 37-token prompt, 5 samples, 21 steps")
+    for _ in range(37):
+        step([prompt], [rprompt])
+    samples = [nat.fork(prompt) for _ in range(5)]
+    rsamples = [ref.fork(rprompt) for _ in range(5)]
+    nat.release(prompt)
+    ref.release(rprompt)
+    for _ in range(21):
+        step(samples, rsamples)
+    tables, lens = nat.export(samples, 6)
+    assert (lens == 37 + 21).all()
+    q = W.f16_normal(rng, (5, H, D))
+    out = host(pa.pa_decode(dev(q), kp, vp, dev(tables), dev(lens), int(lens.max()), 0.088))
+    assert np.array_equal(u16(host(kp)), u16(rk)) and np.array_equal(u16(host(vp)), u16(rv))
+    want = oracle.decode(q, rk, rv, np.array([t + [-1] * (6 - len(t)) for t in rsamples], np.int32),
+                         lens, 0.088)
+    from gpu_util import assert_attention_close
+    assert_attention_close(out, want, "managed samples")

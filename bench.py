@@ -49,7 +49,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="chat",
-                    choices=["chat", "7b", "shared_prefix", "long_context", "tiny", "block_manager"])
+                    choices=["chat", "7b", "shared_prefix", "long_context", "tiny", "block_manager",
+                             "swap"])
     ap.add_argument("--layers", type=int, default=32, help="chat workload: layers per step")
     ap.add_argument("--block-size", type=int, default=16, help="chat workload: tokens per block")
     ap.add_argument("--contiguous", action="store_true",
@@ -268,10 +269,56 @@ def bench_block_manager(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_swap(args):
+    """pa_swap_blocks between the chat workload's device pool (layer 0) and a
+    pinned host pool: 4096 blocks of 32 heads x 16 tokens x 128 dims fp16
+    (128 KiB per pool each, 1 GiB of K + V per direction)."""
+    import torch
+    import paged_kv_cache_151_amd as pa
+    import workloads as W
+    torch.cuda.set_device(0)
+    c = W.chat_layer(0)
+    kp, vp = W.device_pools(c.NB, c.Hkv, c.B, c.D, seed=W.chat_pool_seed(0))
+    n = 4096
+    host_k = torch.empty((n, c.Hkv, c.B, c.D), dtype=torch.float16).pin_memory()
+    host_v = torch.empty_like(host_k).pin_memory()
+    rng = np.random.default_rng(0)
+    dev_ids = rng.permutation(c.NB)[:n].astype(np.int32)
+    out_pairs = torch.from_numpy(np.stack([dev_ids, np.arange(n, dtype=np.int32)], 1)).cuda()
+    in_pairs = torch.from_numpy(np.stack([np.arange(n, dtype=np.int32),
+                                          rng.permutation(c.NB)[:n].astype(np.int32)], 1)).cuda()
+    block_bytes = c.Hkv * c.B * c.D * 2
+    moved = 2 * n * block_bytes
+    res = {}
+    for name, fn in (("out", lambda: pa.pa_swap_blocks(host_k, host_v, kp, vp, out_pairs)),
+                     ("in", lambda: pa.pa_swap_blocks(kp, vp, host_k, host_v, in_pairs))):
+        for _ in range(max(1, args.warmup)):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        res[name] = {"ms": round(ms, 3), "GBs": round(moved / ms / 1e6, 1)}
+    print(json.dumps({
+        "metric": "pa_swap_blocks host-link GB/s (device pool <-> pinned host pool)",
+        "value": res["out"]["GBs"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "higher_is_better": True, "data": "synthetic",
+        "config": {"workload": "4096 blocks of the chat workload's layer-0 pool (32 heads x 16 tokens x "
+                               "128 dims fp16), K and V", "bytes_per_direction": moved},
+        "swap_out": res["out"], "swap_in": res["in"]}), flush=True)
+
+
 def main():
     args = parse()
     if args.workload == "block_manager":
         bench_block_manager(args)
+        return
+    if args.workload == "swap":
+        bench_swap(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the decode path has no cross-GPU step "

@@ -145,6 +145,33 @@ pa_status pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_mappin
                          int Hkv, int D, int B, int NB, hipStream_t stream);
 
 /*
+ * pa_swap_blocks — move blocks between two pools, typically the device pool
+ * and a pool in pinned host memory, to offload a preempted request's cache
+ * and bring it back ([L], "Memory sharing across requests", misconceptions
+ * paragraph: blocks can be swapped out under memory pressure; [B], "Why it
+ * matters for KV cache": evict to CPU memory and fetch back on resume).
+ *
+ *   dst_k_pool[dst] = src_k_pool[src];  dst_v_pool[dst] = src_v_pool[src]
+ *
+ * for each pair (src, dst) = (block_mapping[2p], block_mapping[2p+1]), all
+ * heads and all B slots, a bit copy. Pairs with src outside [0, NB_src) or
+ * dst outside [0, NB_dst) are skipped. Destinations must be distinct and must
+ * not overlap a source of the same call.
+ *
+ *   dst_*_pool        fp16 [NB_dst][Hkv][B][D], 16-byte aligned
+ *   src_*_pool        fp16 [NB_src][Hkv][B][D], 16-byte aligned
+ *   block_mapping     int32 [n][2], device memory or pinned host memory
+ * Each pool is device memory or pinned host memory (hipHostMalloc); the call
+ * checks this with hipPointerGetAttributes and returns PA_ERR_UNSUPPORTED for
+ * anything else (pageable memory is never handed to a kernel). Asynchronous on
+ * `stream` like the other calls: host pools must stay allocated, and must not
+ * be read by the host, until the stream has passed the copy.
+ */
+pa_status pa_swap_blocks(void* dst_k_pool, void* dst_v_pool, const void* src_k_pool,
+                         const void* src_v_pool, const int32_t* block_mapping, int n, int Hkv,
+                         int D, int B, int NB_dst, int NB_src, hipStream_t stream);
+
+/*
  * pa_decode_partition_size — the context partition (in tokens) pa_decode uses
  * for these sizes: partition_size itself when positive, otherwise the
  * library's choice (a multiple of 16 that gives enough waves to fill the GPU,

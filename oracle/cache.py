@@ -84,3 +84,25 @@ def copy_blocks(k_pool, v_pool, pairs):
         k_out[dst] = k_pool[src]
         v_out[dst] = v_pool[src]
     return k_out, v_out
+
+
+def swap_blocks(dst_k, dst_v, src_k, src_v, pairs):
+    """For each (src, dst): block dst of the destination pools becomes a copy
+    of block src of the source pools (both pools, all heads, all B slots).
+
+    Returns new destination pools. Pairs naming a block outside either pool
+    are skipped; destinations must be distinct. ([L], "Memory sharing across
+    requests" and [B], "Why it matters for KV cache": blocks evicted to host
+    memory under pressure and fetched back when the request resumes.)
+    """
+    k_out, v_out = dst_k.copy(), dst_v.copy()
+    pairs = np.asarray(pairs, dtype=np.int64).reshape(-1, 2)
+    ok = [(int(s), int(d)) for s, d in pairs
+          if 0 <= s < src_k.shape[0] and 0 <= d < dst_k.shape[0]]
+    dsts = [d for _, d in ok]
+    if len(dsts) != len(set(dsts)):
+        raise ValueError("swap destinations must be distinct")
+    for s_, d in ok:
+        k_out[d] = src_k[s_]
+        v_out[d] = src_v[s_]
+    return k_out, v_out

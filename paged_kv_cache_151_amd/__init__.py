@@ -36,6 +36,8 @@ _lib.pa_write_kv.restype = _i
 _lib.pa_write_kv.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
 _lib.pa_copy_blocks.restype = _i
 _lib.pa_copy_blocks.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _p]
+_lib.pa_swap_blocks.restype = _i
+_lib.pa_swap_blocks.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p]
 _lib.pa_decode_partition_size.restype = _i
 _lib.pa_decode_partition_size.argtypes = [_i, _i, _i, _i, _i, _i]
 _lib.pa_decode_workspace_bytes.restype = ctypes.c_size_t
@@ -128,6 +130,18 @@ def pa_copy_blocks(k_pool, v_pool, block_mapping, stream=None):
     n = block_mapping.shape[0]
     _check("pa_copy_blocks", _lib.pa_copy_blocks(
         _ptr(k_pool), _ptr(v_pool), _ptr(block_mapping), n, Hkv, D, B, NB, _stream(stream)))
+
+
+def pa_swap_blocks(dst_k_pool, dst_v_pool, src_k_pool, src_v_pool, block_mapping, stream=None):
+    """Copy block src of the source pools to block dst of the destination pools for each row
+    (src, dst) of block_mapping [n, 2] (int32, on the device). Pools are device tensors or
+    pinned host tensors (pin_memory=True)."""
+    NB_src, Hkv, B, D = src_k_pool.shape
+    NB_dst = dst_k_pool.shape[0]
+    n = block_mapping.shape[0]
+    _check("pa_swap_blocks", _lib.pa_swap_blocks(
+        _ptr(dst_k_pool), _ptr(dst_v_pool), _ptr(src_k_pool), _ptr(src_v_pool),
+        _ptr(block_mapping), n, Hkv, D, B, NB_dst, NB_src, _stream(stream)))
 
 
 def pa_decode_partition_size(S, Hq, Hkv, B, max_context_len, partition_size=0) -> int:
@@ -250,4 +264,4 @@ class BlockManager:
 
 __all__ = ["PaError", "lib", "LIB_PATH", "pa_version", "pa_slot_mapping", "pa_write_kv",
            "pa_copy_blocks", "pa_decode_partition_size", "pa_decode_workspace_bytes",
-           "pa_decode", "BlockManager"]
+           "pa_decode", "pa_swap_blocks", "BlockManager"]

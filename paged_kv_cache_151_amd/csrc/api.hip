@@ -130,9 +130,66 @@ pa_status pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_mappin
   const int kMaxY = 65535;
   for (int off = 0; off < n; off += kMaxY) {
     const int cnt = n - off < kMaxY ? n - off : kMaxY;
-    hipError_t e = pa::launch_copy_blocks(k_pool, v_pool, block_mapping + 2 * (int64_t)off, cnt,
-                                          Hkv, D, B, NB, stream);
+    hipError_t e = pa::launch_copy_blocks(k_pool, v_pool, k_pool, v_pool,
+                                          block_mapping + 2 * (int64_t)off, cnt, Hkv, D, B, NB,
+                                          NB, stream);
     if (e != hipSuccess) return hip_status(e, "pa_copy_blocks launch");
+  }
+  return ok();
+}
+
+// The address a kernel uses for `p`: p itself for device memory, the mapped
+// device address for pinned host memory; NULL for anything else (pageable
+// host memory is never handed to a kernel).
+static void* device_view(const void* p) {
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (attr.type == hipMemoryTypeDevice) return const_cast<void*>(p);
+  if (attr.type == hipMemoryTypeHost) {
+    void* d = nullptr;
+    if (hipHostGetDevicePointer(&d, const_cast<void*>(p), 0) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    return d;
+  }
+  return nullptr;
+}
+
+pa_status pa_swap_blocks(void* dst_k_pool, void* dst_v_pool, const void* src_k_pool,
+                         const void* src_v_pool, const int32_t* block_mapping, int n, int Hkv,
+                         int D, int B, int NB_dst, int NB_src, hipStream_t stream) {
+  if (n < 0) return fail(PA_ERR_SHAPE, "pa_swap_blocks: n=%d must be >= 0", n);
+  if (Hkv <= 0 || D <= 0 || B <= 0 || NB_dst <= 0 || NB_src <= 0)
+    return fail(PA_ERR_SHAPE, "pa_swap_blocks: Hkv=%d D=%d B=%d NB_dst=%d NB_src=%d must be > 0",
+                Hkv, D, B, NB_dst, NB_src);
+  if (D % 8) return fail(PA_ERR_UNSUPPORTED, "pa_swap_blocks: D=%d must be a multiple of 8", D);
+  if (n == 0) return ok();
+  if (!dst_k_pool || !dst_v_pool || !src_k_pool || !src_v_pool || !block_mapping)
+    return fail(PA_ERR_NULL, "pa_swap_blocks: null pointer argument");
+  if (!aligned(dst_k_pool, 16) || !aligned(dst_v_pool, 16) || !aligned(src_k_pool, 16) ||
+      !aligned(src_v_pool, 16))
+    return fail(PA_ERR_ALIGN, "pa_swap_blocks: pools must be 16-byte aligned");
+  if (!aligned(block_mapping, 4)) return fail(PA_ERR_ALIGN, "pa_swap_blocks: mapping misaligned");
+  void* dk = device_view(dst_k_pool);
+  void* dv = device_view(dst_v_pool);
+  void* sk = device_view(src_k_pool);
+  void* sv = device_view(src_v_pool);
+  if (!dk || !dv || !sk || !sv)
+    return fail(PA_ERR_UNSUPPORTED,
+                "pa_swap_blocks: every pool must be device memory or pinned host memory");
+  const int32_t* map = static_cast<const int32_t*>(device_view(block_mapping));
+  if (!map)
+    return fail(PA_ERR_UNSUPPORTED, "pa_swap_blocks: block_mapping must be device-accessible");
+  const int kMaxY = 65535;
+  for (int off = 0; off < n; off += kMaxY) {
+    const int cnt = n - off < kMaxY ? n - off : kMaxY;
+    hipError_t e = pa::launch_copy_blocks(dk, dv, sk, sv, map + 2 * (int64_t)off, cnt, Hkv, D, B,
+                                          NB_src, NB_dst, stream);
+    if (e != hipSuccess) return hip_status(e, "pa_swap_blocks launch");
   }
   return ok();
 }

@@ -53,26 +53,46 @@ __global__ __launch_bounds__(256) void write_kv_kernel(
 }
 
 // Grid: (segments, n pairs). Each workgroup copies one contiguous segment of
-// a block, in both pools; a block is Hkv * B * D fp16 = `chunks` 16-byte chunks.
+// a block from the source pools to the destination pools (the same pools for
+// copy-on-write; a device pool and a pinned host pool for swapping). A block
+// is Hkv * B * D fp16 = `chunks` 16-byte chunks. Each thread issues four
+// chunks' loads before their stores, so enough reads are in flight to cover
+// host-link latency when one side is host memory.
 __global__ __launch_bounds__(256) void copy_blocks_kernel(
-    uint4* __restrict__ k_pool, uint4* __restrict__ v_pool, const int32_t* __restrict__ pairs,
-    int64_t chunks, int seg_chunks, int NB) {
+    uint4* __restrict__ k_dst, uint4* __restrict__ v_dst, const uint4* __restrict__ k_src,
+    const uint4* __restrict__ v_src, const int32_t* __restrict__ pairs, int64_t chunks,
+    int seg_chunks, int NB_src, int NB_dst) {
   const int p = blockIdx.y;
   const int src = pairs[2 * p];
   const int dst = pairs[2 * p + 1];
-  if (src < 0 || src >= NB || dst < 0 || dst >= NB) return;
+  if (src < 0 || src >= NB_src || dst < 0 || dst >= NB_dst) return;
   const int64_t lo = (int64_t)blockIdx.x * seg_chunks;
   int64_t hi = lo + seg_chunks;
   if (hi > chunks) hi = chunks;
-  const uint4* ks = k_pool + (int64_t)src * chunks;
-  const uint4* vs = v_pool + (int64_t)src * chunks;
-  uint4* kd = k_pool + (int64_t)dst * chunks;
-  uint4* vd = v_pool + (int64_t)dst * chunks;
-  for (int64_t x = lo + threadIdx.x; x < hi; x += blockDim.x) {
-    const uint4 a = ks[x];
-    const uint4 b = vs[x];
-    kd[x] = a;
-    vd[x] = b;
+  const uint4* ks = k_src + (int64_t)src * chunks;
+  const uint4* vs = v_src + (int64_t)src * chunks;
+  uint4* kd = k_dst + (int64_t)dst * chunks;
+  uint4* vd = v_dst + (int64_t)dst * chunks;
+  constexpr int U = 4;
+  const int stride = blockDim.x;
+  for (int64_t x = lo + threadIdx.x; x < hi; x += U * stride) {
+    uint4 a[U], b[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int64_t y = x + j * stride;
+      if (y < hi) {
+        a[j] = ks[y];
+        b[j] = vs[y];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int64_t y = x + j * stride;
+      if (y < hi) {
+        kd[y] = a[j];
+        vd[y] = b[j];
+      }
+    }
   }
 }
 
@@ -102,15 +122,16 @@ hipError_t launch_write_kv(const void* key, const void* value, void* k_pool, voi
   return hipGetLastError();
 }
 
-hipError_t launch_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int n, int Hkv,
-                              int D, int B, int NB, hipStream_t stream) {
+hipError_t launch_copy_blocks(void* k_dst, void* v_dst, const void* k_src, const void* v_src,
+                              const int32_t* pairs, int n, int Hkv, int D, int B, int NB_src,
+                              int NB_dst, hipStream_t stream) {
   const int64_t chunks = (int64_t)Hkv * B * D / 8;
   const int seg = 2048;                          // 32 KiB of each pool per workgroup
   const int64_t segs = (chunks + seg - 1) / seg;
   dim3 grid((unsigned)segs, (unsigned)n);
-  copy_blocks_kernel<<<grid, 256, 0, stream>>>(static_cast<uint4*>(k_pool),
-                                               static_cast<uint4*>(v_pool), pairs, chunks, seg,
-                                               NB);
+  copy_blocks_kernel<<<grid, 256, 0, stream>>>(
+      static_cast<uint4*>(k_dst), static_cast<uint4*>(v_dst), static_cast<const uint4*>(k_src),
+      static_cast<const uint4*>(v_src), pairs, chunks, seg, NB_src, NB_dst);
   return hipGetLastError();
 }
 

@@ -71,8 +71,11 @@ hipError_t launch_write_kv(const void* key, const void* value, void* k_pool, voi
                            const int64_t* slots, int T, int Hkv, int D, int B, int NB,
                            hipStream_t stream);
 
-hipError_t launch_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int n, int Hkv,
-                              int D, int B, int NB, hipStream_t stream);
+// Copies block src of the source pools to block dst of the destination pools
+// for each (src, dst) pair; the pools may be the same (copy-on-write).
+hipError_t launch_copy_blocks(void* k_dst, void* v_dst, const void* k_src, const void* v_src,
+                              const int32_t* pairs, int n, int Hkv, int D, int B, int NB_src,
+                              int NB_dst, hipStream_t stream);
 
 // Launches the partition kernel and, when Pmax > 1, the cross-partition reduce.
 hipError_t launch_decode(const DecodeArgs& a, int B, int G, hipStream_t stream);

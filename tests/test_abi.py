@@ -106,6 +106,11 @@ def test_write_copy_slot_validation(lib):
     assert lib.pa_copy_blocks(v(FAKE), None, v(FAKE), 3, 2, 128, 16, 8, None) == PA_ERR_NULL
     assert lib.pa_copy_blocks(v(FAKE), v(FAKE), v(FAKE), -1, 2, 128, 16, 8, None) == PA_ERR_SHAPE
     assert lib.pa_copy_blocks(None, None, None, 0, 2, 128, 16, 8, None) == PA_OK
+    assert lib.pa_swap_blocks(v(FAKE), v(FAKE), None, v(FAKE), v(FAKE), 2, 2, 128, 16, 8, 8, None) == PA_ERR_NULL
+    assert lib.pa_swap_blocks(v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(FAKE), -1, 2, 128, 16, 8, 8, None) == PA_ERR_SHAPE
+    assert lib.pa_swap_blocks(v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(FAKE), 2, 2, 12, 16, 8, 8, None) == PA_ERR_UNSUPPORTED
+    assert lib.pa_swap_blocks(v(FAKE + 4), v(FAKE), v(FAKE), v(FAKE), v(FAKE), 2, 2, 128, 16, 8, 8, None) == PA_ERR_ALIGN
+    assert lib.pa_swap_blocks(None, None, None, None, None, 0, 2, 128, 16, 8, 8, None) == PA_OK
     assert lib.pa_slot_mapping(v(FAKE), v(FAKE), None, None, None, 4, 4, 3, 16, 8, None) == PA_ERR_NULL
     assert lib.pa_slot_mapping(v(FAKE), v(FAKE), None, v(FAKE), None, 5, 4, 3, 16, 8, None) == PA_ERR_SHAPE
     assert lib.pa_slot_mapping(v(FAKE), v(FAKE), None, v(FAKE), None, 4, 4, 3, 0, 8, None) == PA_ERR_SHAPE

@@ -173,3 +173,49 @@ def test_native_block_manager_drives_the_device_path(pa):
                          lens, 0.088)
     from gpu_util import assert_attention_close
     assert_attention_close(out, want, "managed samples")
+
+
+def test_swap_out_to_pinned_host_and_back_in(pa):
+    """Preempt-and-resume: a sequence's blocks go to a pinned host pool and come
+    back into other device blocks; the pools match the oracle bit for bit and
+    decode on the resumed cache equals decode on the original."""
+    import torch
+    c = W.seven_b_single_layer()
+    kp, vp = dev(c.k_pool), dev(c.v_pool)
+    H, B, D = c.Hkv, c.B, c.D
+    s = 0                                             # the 853-token sequence
+    nb = oracle.blocks_for(int(c.context_lens[s]), B)
+    ids = c.block_tables[s, :nb]
+    host_k = torch.zeros((nb + 3, H, B, D), dtype=torch.float16).pin_memory()
+    host_v = torch.zeros_like(host_k).pin_memory()
+    out_pairs = np.stack([ids, np.arange(nb) + 2], 1).astype(np.int32)   # host slots 2..nb+1
+    say(f"swap out {nb} blocks to pinned host memory")
+    pa.pa_swap_blocks(host_k, host_v, kp, vp, dev(out_pairs))
+    torch.cuda.synchronize()
+    rk, rv = oracle.swap_blocks(np.zeros((nb + 3, H, B, D), np.float16),
+                                np.zeros((nb + 3, H, B, D), np.float16), c.k_pool, c.v_pool, out_pairs)
+    assert np.array_equal(u16(host_k.numpy()), u16(rk)) and np.array_equal(u16(host_v.numpy()), u16(rv))
+
+    # resume into a fresh device pool at shuffled positions
+    NB2 = nb + 7
+    new_ids = np.random.default_rng(5).permutation(NB2)[:nb].astype(np.int32)
+    kp2 = torch.full((NB2, H, B, D), float("nan"), dtype=torch.float16, device="cuda")
+    vp2 = torch.full_like(kp2, float("nan"))
+    in_pairs = np.stack([np.arange(nb) + 2, new_ids], 1).astype(np.int32)
+    say("swap back in")
+    pa.pa_swap_blocks(kp2, vp2, host_k, host_v, dev(in_pairs))
+    lens = c.context_lens[s:s + 1]
+    q = dev(c.query[s:s + 1])
+    a = host(pa.pa_decode(q, kp, vp, dev(c.block_tables[s:s + 1]), dev(lens), int(lens[0]), c.scale))
+    b = host(pa.pa_decode(q, kp2, vp2, dev(new_ids[None, :]), dev(lens), int(lens[0]), c.scale))
+    assert np.array_equal(u16(a), u16(b))
+
+
+def test_swap_refuses_pageable_host_memory(pa):
+    import torch
+    pool = torch.zeros((4, 1, 16, 128), dtype=torch.float16, device="cuda")
+    pageable = torch.zeros((4, 1, 16, 128), dtype=torch.float16)     # not pinned
+    pairs = dev(np.array([[0, 1]], np.int32))
+    say("swap with pageable memory is refused before any launch")
+    with pytest.raises(pa.PaError, match="PA_ERR_UNSUPPORTED"):
+        pa.pa_swap_blocks(pageable, pageable, pool, pool, pairs)

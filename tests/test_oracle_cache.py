@@ -82,3 +82,43 @@ def test_gather_rejects_bad_tables():
         oracle.gather(pool, [0, 7], 3, 2)
     with pytest.raises(ValueError):
         oracle.gather(pool, [0], 3, 2)
+
+
+def test_swap_blocks_tiny_hand_example():
+    g = load_golden("swap_tiny.json")
+    shape = lambda blocks: np.array(blocks, dtype=np.float32).reshape(len(blocks), g["Hkv"], g["B"], g["D"])
+    src, dst = shape(g["src_blocks"]), shape(g["dst_blocks"])
+    k, v = oracle.swap_blocks(dst, dst + 9, src, src * 10, g["pairs"])
+    exp = shape(g["expected_dst_blocks"])
+    assert np.array_equal(k, exp)
+    assert np.array_equal(v[[0, 3]], exp[[0, 3]] * 10) and np.array_equal(v[[1, 2]], dst[[1, 2]] + 9)
+
+
+def test_swap_out_and_back_in_restores_what_decode_reads():
+    rng = np.random.default_rng(12)
+    NB, H, B, D, L = 10, 2, 4, 8, 15
+    dev_k = rng.standard_normal((NB, H, B, D)).astype(np.float16)
+    dev_v = rng.standard_normal((NB, H, B, D)).astype(np.float16)
+    table = np.array([7, 1, 4, 9])
+    host_k = np.zeros((6, H, B, D), np.float16)
+    host_v = np.zeros_like(host_k)
+    out_pairs = [[b, i] for i, b in enumerate(table)]            # evict to host slots 0..3
+    host_k, host_v = oracle.swap_blocks(host_k, host_v, dev_k, dev_v, out_pairs)
+    fresh_k = np.full_like(dev_k, np.nan)
+    fresh_v = np.full_like(dev_v, np.nan)
+    new_ids = np.array([2, 5, 0, 8])                              # resume into other blocks
+    in_pairs = [[i, b] for i, b in enumerate(new_ids)]
+    fresh_k, fresh_v = oracle.swap_blocks(fresh_k, fresh_v, host_k, host_v, in_pairs)
+    assert np.array_equal(oracle.gather(fresh_k, new_ids, L, B), oracle.gather(dev_k, table, L, B))
+    assert np.array_equal(oracle.gather(fresh_v, new_ids, L, B), oracle.gather(dev_v, table, L, B))
+
+
+def test_swap_within_one_pool_is_copy_on_write():
+    rng = np.random.default_rng(13)
+    pool = rng.standard_normal((6, 2, 4, 8))
+    pairs = [[1, 4], [2, 0]]
+    a = oracle.swap_blocks(pool, pool * 2, pool, pool * 2, pairs)
+    b = oracle.copy_blocks(pool, pool * 2, pairs)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    with pytest.raises(ValueError):
+        oracle.swap_blocks(pool, pool, pool, pool, [[0, 3], [1, 3]])

@@ -63,7 +63,7 @@ def parse():
     ap.add_argument("--cpu-sample-layers", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-reference-mb", type=int, default=0,
-                    help="after timing, run one pa_copy_blocks moving this many MiB per pool "
+                    help="after timing, run one plain device-to-device copy of this many MiB "
                          "(a copy of known size for scaling traffic counters)")
     return ap.parse_args()
 
@@ -95,19 +95,17 @@ def measured_traffic():
     return t.get("traffic_bytes_per_launch")
 
 
-def copy_reference(pa, mb):
-    """One pa_copy_blocks call over a scratch pool: reads and writes exactly
-    mb MiB in each of two pools (K and V)."""
+def copy_reference(mb):
+    """One plain device-to-device copy of exactly mb MiB (torch copy_, a memory
+    copy), after the timed region: the known-size reference that scales the
+    FETCH_SIZE and WRITE_SIZE counters."""
     import torch
-    blk = 32 * 16 * 128 * 2                       # bytes of one block of one pool
-    n = max(1, (mb << 20) // blk)
-    kp = torch.empty((2 * n, 32, 16, 128), dtype=torch.float16, device="cuda")
-    vp = torch.empty_like(kp)
-    pairs = torch.stack([torch.arange(n), torch.arange(n) + n], 1).to(torch.int32).cuda()
+    a = torch.zeros(mb << 19, dtype=torch.float16, device="cuda")
+    b = torch.empty_like(a)
     torch.cuda.synchronize()
-    pa.pa_copy_blocks(kp, vp, pairs)
+    b.copy_(a)
     torch.cuda.synchronize()
-    log(f"copy reference: {n} blocks x {blk} B per pool, {2 * n * blk} B read, same written")
+    log(f"copy reference: {mb << 20} B read, {mb << 20} B written")
 
 
 # ---------------------------------------------------------------------------
@@ -410,7 +408,7 @@ def main():
     cow = time_copy_on_write(pa, extra) if "copy" in extra else None
 
     if args.copy_reference_mb > 0:
-        copy_reference(pa, args.copy_reference_mb)
+        copy_reference(args.copy_reference_mb)
 
     cpu = None
     if not args.no_cpu_baseline:

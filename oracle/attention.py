@@ -1,4 +1,5 @@
-"""Decode attention through a block table (oracle; test infrastructure only).
+"""Decode and prefill attention through a block table (oracle; test
+infrastructure only).
 
 [L] = "Paged Attention: OS-Inspired Memory Management for KV Caches";
 [B] = "What is PagedAttention and how does it manage KV cache?".
@@ -15,7 +16,14 @@ Readings the pages leave open (they are silent on these points):
   * grouped-query heads: query head h reads KV head h // (Hq / Hkv);
   * the scale is the caller's (1/sqrt(D) in every workload); no bias, cap or
     window;
-  * L = 0 gives a zero output.
+  * L = 0 gives a zero output;
+  * prefill: the pages say only that the prompt's keys and values are stored
+    in the blocks the manager hands out ([L], "How PagedAttention works",
+    step 1) and that attention reads through the table as if contiguous. The
+    plainest reading for a causal decoder: each new token attends to every
+    earlier token of its sequence and to itself, and the new tokens are the
+    last n of the L stored ones, so a cached prefix (shared prompt blocks,
+    [L] "Memory sharing across requests") is attended in full.
 """
 from __future__ import annotations
 
@@ -92,3 +100,38 @@ def merge_partials(parts):
     num = sum(np.exp(m - M) * acc for m, _, acc in parts if np.isfinite(m))
     den = sum(np.exp(m - M) * l for m, l, _ in parts if np.isfinite(m))
     return num / den
+
+
+def prefill(query, k_pool, v_pool, block_tables, context_lens, query_start, scale) -> np.ndarray:
+    """Paged attention of a chunk of new tokens per sequence (fp64, [T, Hq, D]).
+
+    Sequence s owns query rows query_start[s] .. query_start[s+1]-1: its
+    n = query_start[s+1] - query_start[s] newest tokens, at positions L-n ..
+    L-1 where L = context_lens[s] counts every cached token including these
+    (their keys and values are already in the pool). New token j attends over
+    positions 0 .. L-n+j: every earlier token of the sequence, cached prefix
+    included, and itself ([L], "How PagedAttention works", step 1: the prompt
+    is stored in the request's blocks; step 4: attention walks the table).
+    """
+    T, Hq, D = query.shape
+    NB, Hkv, B, Dk = k_pool.shape
+    if Dk != D or Hq % Hkv:
+        raise ValueError("shape mismatch")
+    G = Hq // Hkv
+    qs = np.asarray(query_start, dtype=np.int64)
+    out = np.zeros((T, Hq, D), dtype=np.float64)
+    for s in range(len(context_lens)):
+        L = int(context_lens[s])
+        n = int(qs[s + 1] - qs[s])
+        if n < 0 or n > L or L > block_tables.shape[1] * B:
+            raise ValueError("bad query range or context length")
+        if n == 0:
+            continue
+        Kc = gather(k_pool, block_tables[s], L, B).astype(np.float64)
+        Vc = gather(v_pool, block_tables[s], L, B).astype(np.float64)
+        for j in range(n):
+            pos = L - n + j
+            for h in range(Hq):
+                g = h // G
+                out[qs[s] + j, h] = attend(query[qs[s] + j, h], Kc[g, :pos + 1], Vc[g, :pos + 1], scale)
+    return out

@@ -208,3 +208,81 @@ def test_zero_length_gives_zero_output_and_bad_lengths_raise():
     assert not oracle.decode(q, pool, pool, tables, np.array([0]), 1.0).any()
     with pytest.raises(ValueError):
         oracle.decode(q, pool, pool, tables, np.array([5]), 1.0)
+
+
+# ---------------------------------------------------------------------------
+# prefill: a chunk of new tokens per sequence, causal, through the table
+# ---------------------------------------------------------------------------
+
+def _prefill_case(rng, lens, nq, Hq, Hkv, B, D=16, extra_blocks=3):
+    S = len(lens)
+    MB = max(oracle.blocks_for(L, B) for L in lens)
+    NB = sum(oracle.blocks_for(L, B) for L in lens) + extra_blocks
+    perm = rng.permutation(NB)
+    tables = np.full((S, MB), -1, np.int32)
+    off = 0
+    for s, L in enumerate(lens):
+        n = oracle.blocks_for(L, B)
+        tables[s, :n] = perm[off:off + n]
+        off += n
+    kp = rng.standard_normal((NB, Hkv, B, D))
+    vp = rng.standard_normal((NB, Hkv, B, D))
+    qs = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    q = rng.standard_normal((int(qs[-1]), Hq, D))
+    return q, kp, vp, tables, np.array(lens, np.int32), qs
+
+
+def test_prefill_of_one_token_is_decode():
+    rng = np.random.default_rng(20)
+    q, kp, vp, t, L, qs = _prefill_case(rng, [17, 40, 5], [1, 1, 1], 4, 2, 4)
+    assert np.array_equal(oracle.prefill(q, kp, vp, t, L, qs, 0.3), oracle.decode(q, kp, vp, t, L, 0.3))
+
+
+def test_prompt_prefill_equals_causal_sdpa():
+    rng = np.random.default_rng(21)
+    for Hq, Hkv, L, B in [(4, 4, 37, 4), (8, 2, 50, 16), (2, 1, 1, 4)]:
+        q, kp, vp, t, lens, qs = _prefill_case(rng, [L], [L], Hq, Hkv, B)
+        got = oracle.prefill(q, kp, vp, t, lens, qs, 0.25)
+        K = oracle.gather(kp, t[0], L, B)
+        V = oracle.gather(vp, t[0], L, B)
+        qt = torch.tensor(q.transpose(1, 0, 2))[None]
+        ref = F.scaled_dot_product_attention(qt, torch.tensor(K)[None], torch.tensor(V)[None],
+                                             scale=0.25, is_causal=True, enable_gqa=True)
+        assert np.allclose(got, ref[0].numpy().transpose(1, 0, 2), rtol=1e-12, atol=1e-13)
+
+
+def test_chunked_prefill_rows_match_full_prefill():
+    # the second chunk, with the first already cached, gives the same rows as one pass
+    rng = np.random.default_rng(22)
+    q, kp, vp, t, lens, qs = _prefill_case(rng, [45], [45], 4, 4, 8)
+    full = oracle.prefill(q, kp, vp, t, lens, qs, 0.4)
+    tail = oracle.prefill(q[30:], kp, vp, t, lens, np.array([0, 15]), 0.4)
+    assert np.array_equal(tail, full[30:])
+
+
+def test_prefill_last_row_sees_everything_first_row_sees_the_prefix():
+    rng = np.random.default_rng(23)
+    q, kp, vp, t, lens, qs = _prefill_case(rng, [30], [6], 2, 2, 4)
+    out = oracle.prefill(q, kp, vp, t, lens, qs, 0.5)
+    K = oracle.gather(kp, t[0], 30, 4)
+    V = oracle.gather(vp, t[0], 30, 4)
+    assert np.allclose(out[5, 1], oracle.attend(q[5, 1], K[1], V[1], 0.5), rtol=0, atol=1e-14)
+    assert np.allclose(out[0, 0], oracle.attend(q[0, 0], K[0, :25], V[0, :25], 0.5), rtol=0, atol=1e-14)
+
+
+def test_prefill_brute_force_tables_and_poison():
+    rng = np.random.default_rng(24)
+    B, L, Hq, Hkv, D = 2, 5, 2, 1, 4
+    q = rng.standard_normal((3, Hq, D))
+    K = rng.standard_normal((Hkv, L, D))
+    V = rng.standard_normal((Hkv, L, D))
+    qt = torch.tensor(q.transpose(1, 0, 2))[None]
+    mask = torch.ones(3, L, dtype=torch.bool).tril(diagonal=L - 3)
+    ref = F.scaled_dot_product_attention(qt, torch.tensor(K)[None], torch.tensor(V)[None],
+                                         attn_mask=mask, scale=0.7, enable_gqa=True)[0].numpy()
+    nb = oracle.blocks_for(L, B)
+    for table in itertools.permutations(range(nb + 2), nb):
+        kp = place(K, table, B, nb + 2, fill=np.nan)
+        vp = place(V, table, B, nb + 2, fill=np.nan)
+        out = oracle.prefill(q, kp, vp, np.array([table]), np.array([L]), np.array([0, 3]), 0.7)
+        assert np.allclose(out, ref.transpose(1, 0, 2), rtol=1e-12, atol=1e-14)

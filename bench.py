@@ -50,7 +50,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="chat",
                     choices=["chat", "7b", "shared_prefix", "long_context", "tiny", "block_manager",
-                             "swap"])
+                             "swap", "prefill"])
     ap.add_argument("--layers", type=int, default=32, help="chat workload: layers per step")
     ap.add_argument("--block-size", type=int, default=16, help="chat workload: tokens per block")
     ap.add_argument("--contiguous", action="store_true",
@@ -60,6 +60,7 @@ def parse():
                     help="other workloads: input copies rotated over steps (0 = enough to "
                          "exceed the 256 MB last-level cache; 1 = cache-warm)")
     ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--prompts", type=int, default=16, help="prefill workload: prompts per step")
     ap.add_argument("--cpu-sample-layers", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-reference-mb", type=int, default=0,
@@ -310,8 +311,120 @@ def bench_swap(args):
         "swap_out": res["out"], "swap_in": res["in"]}), flush=True)
 
 
+MFMA_F16_PEAK_TFLOPS = 2500.0
+
+
+def prefill_flops(new_lens, context_lens, Hq, D):
+    """Algorithmic flops of causal paged prefill: a new token at position p
+    scores p + 1 keys and sums p + 1 values, 2 D flops each, per query head."""
+    total = 0
+    for n, L in zip(new_lens.tolist(), context_lens.tolist()):
+        first = L - n + 1                      # keys seen by the first new token
+        total += (first + L) * n // 2          # sum of p + 1 over the n new tokens
+    return 4 * D * Hq * total
+
+
+def bench_prefill(args):
+    """Paged prefill of a batch of chat prompts (U[100, 2000] tokens, 32 heads
+    of 128 dims, B = 16): per step, every prompt token's slot (pa_slot_mapping),
+    its K/V store (pa_write_kv) and causal prefill attention through the block
+    tables (pa_prefill)."""
+    import torch
+    import paged_kv_cache_151_amd as pa
+    import workloads as W
+    torch.cuda.set_device(0)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    t0 = time.time()
+    c = W.chat_prefill(S=args.prompts)
+    kp, vp = dev(c.k_pool), dev(c.v_pool)
+    tables, lens, qs = dev(c.block_tables), dev(c.context_lens), dev(c.query_start)
+    q = dev(c.query)
+    rng = np.random.default_rng(c.seed + 7)
+    k_new = dev(W.f16_normal(rng, (c.T, c.Hkv, c.D)))
+    v_new = dev(W.f16_normal(rng, (c.T, c.Hkv, c.D)))
+    seq = dev(np.concatenate([np.full(n, s, np.int32) for s, n in enumerate(c.new_lens)]))
+    pos = dev(np.concatenate([np.arange(L - n, L, dtype=np.int32)
+                              for n, L in zip(c.new_lens, c.context_lens)]))
+    slots = torch.empty(c.T, dtype=torch.int64, device="cuda")
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+    flops = prefill_flops(c.new_lens, c.context_lens, c.Hq, c.D)
+    log(f"setup {time.time() - t0:.1f}s: {c.name}, T={c.T}, NB={c.NB}, {flops / 1e9:.1f} GFLOP")
+
+    def step(ev=None):
+        pa.pa_slot_mapping(tables, c.B, c.NB, seq_ids=seq, positions=pos, out=slots)
+        pa.pa_write_kv(k_new, v_new, kp, vp, slots)
+        if ev is not None:
+            ev[0].record(stream)
+        pa.pa_prefill(q, kp, vp, tables, lens, qs, c.max_query_len, c.scale, out=out)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for e in ev:
+        step(e)
+    torch.cuda.synchronize()
+    launch_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    tflops_step = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (launch_ms * 1e-3) / 1e12
+    if args.copy_reference_mb > 0:
+        copy_reference(args.copy_reference_mb)
+    cpu = None if args.no_cpu_baseline else cpu_baseline_prefill(c, flops)
+    print(json.dumps({
+        "metric": "paged-prefill attention TFLOP/s (% of fp16 MFMA peak) + prompt tokens/s",
+        "value": round(tflops_step, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16", "accumulate": "f32",
+        "data": "synthetic", "prompt_tokens_per_s": round(c.T / (ms_per_step * 1e-3), 1),
+        "config": {"workload": f"chat prefill: {c.S} prompts U[100,2000] tokens, nothing cached, "
+                               f"32 heads x 128 dims fp16, B=16", "prompts": c.S,
+                   "prompt_tokens": c.T, "max_prompt": c.max_query_len, "pool_blocks": c.NB,
+                   "flops_per_step": int(flops)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_F16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
+                     "traffic": None, "kernel": "pa_prefill (one launch per step)",
+                     "avg_launch_us": round(launch_ms * 1e3, 2), "flops_per_launch": int(flops)},
+        "cpu_baseline": cpu}), flush=True)
+
+
+def cpu_baseline_prefill(c, flops_total):
+    """Oracle attention (fp64, numpy) for 48 evenly spaced new tokens of every
+    prompt, every head, over the keys each one sees; rate = their flops / time."""
+    import oracle
+    t_total, f_total = 0.0, 0
+    for s in range(c.S):
+        L, n, q0 = int(c.context_lens[s]), int(c.new_lens[s]), int(c.query_start[s])
+        t = time.perf_counter()
+        K = oracle.gather(c.k_pool, c.block_tables[s], L, c.B)
+        V = oracle.gather(c.v_pool, c.block_tables[s], L, c.B)
+        for j in np.linspace(0, n - 1, 48).astype(int):
+            p = L - n + int(j)
+            for h in range(c.Hq):
+                oracle.attend(c.query[q0 + j, h], K[h, :p + 1], V[h, :p + 1], c.scale)
+            f_total += 4 * c.D * c.Hq * (p + 1)
+        t_total += time.perf_counter() - t
+    return {"value": round(f_total / t_total / 1e12, 6), "unit": "TFLOP/s",
+            "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"oracle attention of 48 evenly spaced new tokens per prompt x {c.Hq} heads "
+                      f"({c.S * 48 * c.Hq} rows, {f_total / 1e9:.2f} GFLOP), {t_total:.1f} s"}
+
+
 def main():
     args = parse()
+    if args.workload == "prefill":
+        bench_prefill(args)
+        return
     if args.workload == "block_manager":
         bench_block_manager(args)
         return

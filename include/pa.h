@@ -229,6 +229,49 @@ pa_status pa_decode(void* out, const void* query, const void* k_pool, const void
                     int partition_size, void* workspace, size_t workspace_bytes,
                     hipStream_t stream);
 
+/*
+ * pa_prefill — attention of a chunk of new tokens per sequence through the
+ * block table, causal ([L], "How PagedAttention works", step 1: the prompt's
+ * keys and values live in the blocks the manager handed out; step 4: attend
+ * through the table as over contiguous memory; "Memory sharing across
+ * requests": a prompt may begin with blocks other requests already filled).
+ *
+ * Sequence s owns packed query rows query_start[s] .. query_start[s+1] - 1;
+ * with n_s rows and L_s = context_lens[s] tokens in the cache (the n_s new
+ * ones included, already stored by pa_write_kv), row j is the token at
+ * position p = L_s - n_s + j and
+ *
+ *   out[row][h] = sum_t softmax_t(scale * q[row][h] . K_t) * V_t,  t = 0 .. p
+ *
+ * with K_t, V_t read for KV head h / (Hq/Hkv) from block block_tables[s][t / B]
+ * at offset t % B. A cached prefix (L_s > n_s) is attended in full. fp16
+ * inputs, fp32 scores and sums, softmax weights rounded to fp16 for the
+ * weighted sum of values (fp32 accumulation), fp16 output. Slots past L_s are
+ * never read into the result, whatever they hold; keys and values of the
+ * tokens 0 .. L_s - 1 must be finite.
+ *
+ *   out               device fp16 [T][Hq][D], 16-byte aligned, written for rows
+ *                     that belong to a sequence
+ *   query             device fp16 [T][Hq][D], 16-byte aligned
+ *   k_pool, v_pool    device fp16 [NB][Hkv][B][D], 16-byte aligned
+ *   block_tables      device int32 [S][MB]
+ *   context_lens      device int32 [S], n_s <= L_s <= MB * B
+ *   query_start       device int32 [S + 1], non-decreasing, query_start[S] <= T
+ *   max_query_len     host bound on every n_s (sizes the launch)
+ *   scale             softmax scale, usually 1/sqrt(D)
+ * Supported: D = 128; B a multiple of 16; Hq / Hkv in {1, 2, 4, 8}. S = 0 or
+ * max_query_len = 0 is a no-op. Caller errors the kernel can see are contained,
+ * never an access outside the buffers: a sequence whose query range leaves
+ * [0, T] is skipped, L_s is clamped to [0, MB * B], a sequence with
+ * n_s > max_query_len has only its last rows computed (the rest are left
+ * unwritten), and a row whose position would be negative (n_s > L_s) gets
+ * zeros.
+ */
+pa_status pa_prefill(void* out, const void* query, const void* k_pool, const void* v_pool,
+                     const int32_t* block_tables, const int32_t* context_lens,
+                     const int32_t* query_start, int S, int T, int Hq, int Hkv, int D, int B,
+                     int NB, int MB, int max_query_len, float scale, hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * Host block manager ([L], "How PagedAttention works", steps 1-3 and 5;
  * "Memory sharing across requests"; "Practice: try it yourself").

@@ -46,6 +46,9 @@ _lib.pa_decode.restype = _i
 _lib.pa_decode.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i,
                            ctypes.c_float, _i, _p, ctypes.c_size_t, _p]
 
+_lib.pa_prefill.restype = _i
+_lib.pa_prefill.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _i,
+                            ctypes.c_float, _p]
 _lib.pa_bm_create.restype = _i
 _lib.pa_bm_create.argtypes = [_i, _i, _i, ctypes.POINTER(_p)]
 _lib.pa_bm_destroy.restype = None
@@ -171,6 +174,21 @@ def pa_decode(query, k_pool, v_pool, block_tables, context_lens, max_context_len
     return out
 
 
+def pa_prefill(query, k_pool, v_pool, block_tables, context_lens, query_start,
+               max_query_len: int, scale: float, out=None, stream=None):
+    """Paged causal prefill attention of packed new tokens; returns out fp16 [T, Hq, D]."""
+    T, Hq, D = query.shape
+    NB, Hkv, B, _ = k_pool.shape
+    S, MB = block_tables.shape
+    if out is None:
+        out = torch.empty_like(query)
+    _check("pa_prefill", _lib.pa_prefill(
+        _ptr(out), _ptr(query), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+        _ptr(context_lens), _ptr(query_start), S, T, Hq, Hkv, D, B, NB, MB,
+        int(max_query_len), float(scale), _stream(stream)))
+    return out
+
+
 # ---------------------------------------------------------------------------
 # Host block manager (host numpy arrays; see the pa_bm_* calls in include/pa.h)
 # ---------------------------------------------------------------------------
@@ -264,4 +282,4 @@ class BlockManager:
 
 __all__ = ["PaError", "lib", "LIB_PATH", "pa_version", "pa_slot_mapping", "pa_write_kv",
            "pa_copy_blocks", "pa_decode_partition_size", "pa_decode_workspace_bytes",
-           "pa_decode", "pa_swap_blocks", "BlockManager"]
+           "pa_decode", "pa_prefill", "pa_swap_blocks", "BlockManager"]

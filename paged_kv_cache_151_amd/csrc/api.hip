@@ -294,4 +294,59 @@ pa_status pa_decode(void* out, const void* query, const void* k_pool, const void
   return hip_status(pa::launch_decode(a, B, G, stream), "pa_decode launch");
 }
 
+pa_status pa_prefill(void* out, const void* query, const void* k_pool, const void* v_pool,
+                     const int32_t* block_tables, const int32_t* context_lens,
+                     const int32_t* query_start, int S, int T, int Hq, int Hkv, int D, int B,
+                     int NB, int MB, int max_query_len, float scale, hipStream_t stream) {
+  if (S < 0 || T < 0) return fail(PA_ERR_SHAPE, "pa_prefill: S=%d T=%d must be >= 0", S, T);
+  if (Hq <= 0 || Hkv <= 0 || D <= 0 || B <= 0 || NB <= 0 || MB <= 0)
+    return fail(PA_ERR_SHAPE, "pa_prefill: Hq=%d Hkv=%d D=%d B=%d NB=%d MB=%d must be > 0", Hq,
+                Hkv, D, B, NB, MB);
+  if (Hq % Hkv) return fail(PA_ERR_SHAPE, "pa_prefill: Hq=%d not a multiple of Hkv=%d", Hq, Hkv);
+  if ((int64_t)MB * B >= ((int64_t)1 << 31))
+    return fail(PA_ERR_SHAPE, "pa_prefill: MB*B=%lld exceeds int32", (long long)MB * B);
+  if (max_query_len < 0 || max_query_len > T)
+    return fail(PA_ERR_SHAPE, "pa_prefill: max_query_len=%d outside [0, T=%d]", max_query_len, T);
+  const int G = Hq / Hkv;
+  if (D != pa::kHeadDim) return fail(PA_ERR_UNSUPPORTED, "pa_prefill: D=%d (supported: 128)", D);
+  if (B % pa::kDecodeUnit)
+    return fail(PA_ERR_UNSUPPORTED, "pa_prefill: B=%d (supported: multiples of %d)", B,
+                pa::kDecodeUnit);
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(PA_ERR_UNSUPPORTED, "pa_prefill: Hq/Hkv=%d (supported: 1, 2, 4, 8)", G);
+  if (!std::isfinite(scale)) return fail(PA_ERR_SHAPE, "pa_prefill: scale is not finite");
+  if (S == 0 || max_query_len == 0) return ok();
+  if (!out || !query || !k_pool || !v_pool || !block_tables || !context_lens || !query_start)
+    return fail(PA_ERR_NULL, "pa_prefill: null pointer argument");
+  if (!aligned(out, 16) || !aligned(query, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16))
+    return fail(PA_ERR_ALIGN, "pa_prefill: out/query/pools must be 16-byte aligned");
+  if (!aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(query_start, 4))
+    return fail(PA_ERR_ALIGN, "pa_prefill: index arrays misaligned");
+  if ((int64_t)T * Hq * D >= ((int64_t)1 << 62))
+    return fail(PA_ERR_SHAPE, "pa_prefill: T too large");
+  const int QB = pa::prefill_rows_per_workgroup(G);
+  const int64_t grid =
+      (int64_t)((max_query_len + QB - 1) / QB) * S * (G > 4 ? G / 4 : 1) * Hkv;
+  if (grid >= ((int64_t)1 << 31))
+    return fail(PA_ERR_SHAPE, "pa_prefill: launch too large (%lld workgroups)", (long long)grid);
+
+  pa::PrefillArgs a;
+  a.out = static_cast<_Float16*>(out);
+  a.q = static_cast<const _Float16*>(query);
+  a.k_pool = static_cast<const _Float16*>(k_pool);
+  a.v_pool = static_cast<const _Float16*>(v_pool);
+  a.tables = block_tables;
+  a.lens = context_lens;
+  a.qstart = query_start;
+  a.S = S;
+  a.T = T;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.NB = NB;
+  a.MB = MB;
+  a.B = B;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  return hip_status(pa::launch_prefill(a, B, G, max_query_len, stream), "pa_prefill launch");
+}
+
 }  // extern "C"

@@ -127,3 +127,29 @@ def test_package_refuses_to_import_without_the_library(tmp_path):
     r = subprocess.run([sys.executable, "-c", "import paged_kv_cache_151_amd"], cwd=tmp_path,
                        capture_output=True, text=True)
     assert r.returncode != 0 and "libpa.so is missing" in r.stderr
+
+
+def prefill(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, t=FAKE, l=FAKE, qs=FAKE, S=2, T=40, Hq=4, Hkv=4,
+             D=128, B=16, NB=16, MB=3, maxq=32, scale=0.1)
+    a.update(kw)
+    v = ctypes.c_void_p
+    return lib.pa_prefill(v(a["out"]), v(a["q"]), v(a["k"]), v(a["v"]), v(a["t"]), v(a["l"]),
+                          v(a["qs"]), a["S"], a["T"], a["Hq"], a["Hkv"], a["D"], a["B"], a["NB"],
+                          a["MB"], a["maxq"], F(a["scale"]), None)
+
+
+def test_prefill_host_validation(lib):
+    assert prefill(lib, qs=None) == PA_ERR_NULL
+    assert prefill(lib, Hq=6, Hkv=4) == PA_ERR_SHAPE
+    assert prefill(lib, D=64) == PA_ERR_UNSUPPORTED
+    assert prefill(lib, B=8, MB=6) == PA_ERR_UNSUPPORTED
+    assert prefill(lib, Hq=12, Hkv=4) == PA_ERR_UNSUPPORTED    # group of 3
+    assert prefill(lib, maxq=41) == PA_ERR_SHAPE               # more rows than T
+    assert prefill(lib, maxq=-1) == PA_ERR_SHAPE
+    assert prefill(lib, T=-1) == PA_ERR_SHAPE
+    assert prefill(lib, out=FAKE + 2) == PA_ERR_ALIGN
+    assert prefill(lib, qs=FAKE + 2) == PA_ERR_ALIGN
+    assert prefill(lib, scale=float("nan")) == PA_ERR_SHAPE
+    assert prefill(lib, S=0) == PA_OK
+    assert prefill(lib, maxq=0, out=None) == PA_OK

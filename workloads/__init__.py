@@ -307,3 +307,96 @@ def long_context(seed: int = 5, with_pools: bool = True) -> DecodeCase:
     lengths = np.full(16, 4096, dtype=np.int32)
     return _finish_case("long_context_b16_4096", seed, rng, lengths, 32, 32, 32, HEAD_DIM,
                         2048, (5, 4), None, with_pools)
+
+
+# ---------------------------------------------------------------------------
+# Prefill inputs: a chunk of new tokens per sequence. Sequence s holds
+# cached_lens[s] + new_lens[s] tokens in the pools (every slot drawn), its new
+# tokens are the last new_lens[s]; their queries are packed row after row.
+# ---------------------------------------------------------------------------
+
+@dataclass
+class PrefillCase:
+    name: str
+    seed: int
+    S: int
+    Hq: int
+    Hkv: int
+    D: int
+    B: int
+    NB: int
+    context_lens: np.ndarray          # int32 [S]   cached + new
+    new_lens: np.ndarray              # int32 [S]
+    query_start: np.ndarray           # int32 [S + 1]
+    block_tables: np.ndarray          # int32 [S, MB]
+    query: np.ndarray                 # fp16 [T, Hq, D]
+    k_pool: Optional[np.ndarray] = None
+    v_pool: Optional[np.ndarray] = None
+    scale: float = 1.0 / np.sqrt(HEAD_DIM)
+
+    @property
+    def T(self) -> int:
+        return int(self.query_start[-1])
+
+    @property
+    def MB(self) -> int:
+        return int(self.block_tables.shape[1])
+
+    @property
+    def max_query_len(self) -> int:
+        return int(self.new_lens.max()) if self.S else 0
+
+
+def make_prefill_case(name, seed, new_lens, cached_lens, Hq, Hkv, B, D=HEAD_DIM, NB=None,
+                      with_pools=True) -> PrefillCase:
+    """Draw order: permutation, pools (K then V), packed query."""
+    rng = np.random.default_rng(seed)
+    new_lens = np.asarray(new_lens, dtype=np.int32)
+    lengths = (np.asarray(cached_lens, dtype=np.int32) + new_lens).astype(np.int32)
+    S = len(lengths)
+    needed = sum(row_len(L, B) for L in lengths)
+    if NB is None:
+        NB = max(pool_blocks(needed), 1)
+    perm = rng.permutation(NB).astype(np.int32)
+    tables, _ = lay_out_tables(lengths, B, perm)
+    k_pool = v_pool = None
+    if with_pools:
+        k_pool = f16_normal(rng, (NB, Hkv, B, D))
+        v_pool = f16_normal(rng, (NB, Hkv, B, D))
+    qs = np.zeros(S + 1, dtype=np.int32)
+    qs[1:] = np.cumsum(new_lens)
+    query = f16_normal(rng, (int(qs[-1]), Hq, D))
+    return PrefillCase(name=name, seed=seed, S=S, Hq=Hq, Hkv=Hkv, D=D, B=B, NB=int(NB),
+                       context_lens=lengths, new_lens=new_lens, query_start=qs,
+                       block_tables=tables, query=query, k_pool=k_pool, v_pool=v_pool,
+                       scale=1.0 / np.sqrt(D))
+
+
+CHAT_PREFILL_SEED = 6
+
+
+def chat_prefill(seed: int = CHAT_PREFILL_SEED, S: int = 16, with_pools: bool = True) -> PrefillCase:
+    """Prompt processing for the chat endpoint: S prompts with lengths uniform in
+    [100, 2000] (the blog's chat example), nothing cached, 32 query heads = 32
+    KV heads of 128 dims, B = 16, pool 1.25x the blocks needed."""
+    rng = np.random.default_rng(seed)
+    prompts = rng.integers(100, 2001, size=S).astype(np.int32)
+    return make_prefill_case(f"chat_prefill_s{S}", seed * 1000 + 1, prompts, np.zeros(S, np.int32),
+                             32, 32, 16, with_pools=with_pools)
+
+
+def prefix_prefill(seed: int = 4, n_seq: int = 64) -> dict:
+    """The shared-prefix workload (shared_prefix: a cached 500-token prompt,
+    grouped heads 32/8) processed as prefill: each sequence's private suffix is
+    the chunk of new tokens. Adds the packed suffix queries (fp16 [T, Hq, D],
+    drawn from default_rng(seed * 1000 + 1)) and query_start [S + 1] to the
+    shared_prefix dict."""
+    w = shared_prefix(seed=seed, n_seq=n_seq)
+    n = (w["context_lens"] - w["prefix_len"]).astype(np.int32)
+    qs = np.zeros(len(n) + 1, dtype=np.int32)
+    qs[1:] = np.cumsum(n)
+    rng = np.random.default_rng(seed * 1000 + 1)
+    w["prefill_query"] = f16_normal(rng, (int(qs[-1]), w["Hq"], w["D"]))
+    w["query_start"] = qs
+    w["new_lens"] = n
+    return w

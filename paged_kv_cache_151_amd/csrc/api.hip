@@ -8,6 +8,7 @@
 #include "pa.h"
 #include "pa_error.h"
 #include "pa_internal.h"
+#include "prefill_internal.h"
 
 namespace pa {
 

@@ -38,7 +38,7 @@
 // Masking: keys and values past the sequence's L tokens are fetched as zeros
 // by the buffer range check (so NaN or Inf in unused slots never enters a
 // product); causal exclusions select the score to "no token" and p to 0.
-#include "pa_internal.h"
+#include "prefill_internal.h"
 
 namespace pa {
 namespace {

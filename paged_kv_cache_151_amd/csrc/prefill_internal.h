@@ -1,0 +1,36 @@
+// Internal declarations of the prefill kernel (not installed).
+#pragma once
+
+#include "pa_internal.h"
+
+namespace pa {
+
+// Query row tiles of 16 per prefill wave: each key/value fetch serves
+// 16 * kPrefillRowTiles rows.
+#ifndef PA_PREFILL_ROW_TILES
+#define PA_PREFILL_ROW_TILES 2
+#endif
+constexpr int kPrefillRowTiles = PA_PREFILL_ROW_TILES;
+
+// Arguments of the prefill kernel.
+struct PrefillArgs {
+  _Float16* out;                     // [T][Hq][D]
+  const _Float16* q;                 // [T][Hq][D]
+  const _Float16* k_pool;            // [NB][Hkv][B][D]
+  const _Float16* v_pool;            // [NB][Hkv][B][D]
+  const int32_t* tables;             // [S][MB]
+  const int32_t* lens;               // [S]   tokens in the cache, new ones included
+  const int32_t* qstart;             // [S+1] first packed query row of each sequence
+  int S, T, Hq, Hkv, NB, MB, B;
+  float scale_log2;                  // softmax scale times log2(e)
+};
+
+// Query rows one prefill workgroup covers for a group of G query heads.
+int prefill_rows_per_workgroup(int G);
+
+// Launches the prefill kernel over ceil(max_query_len / rows) row blocks per
+// sequence and head group.
+hipError_t launch_prefill(const PrefillArgs& a, int B, int G, int max_query_len,
+                          hipStream_t stream);
+
+}  // namespace pa

@@ -315,7 +315,8 @@ pa_status pa_prefill(void* out, const void* query, const void* k_pool, const voi
                 pa::kDecodeUnit);
   if (G != 1 && G != 2 && G != 4 && G != 8)
     return fail(PA_ERR_UNSUPPORTED, "pa_prefill: Hq/Hkv=%d (supported: 1, 2, 4, 8)", G);
-  if (!std::isfinite(scale)) return fail(PA_ERR_SHAPE, "pa_prefill: scale is not finite");
+  if (!std::isfinite(scale) || scale < 0.f)
+    return fail(PA_ERR_SHAPE, "pa_prefill: scale must be finite and >= 0");
   if (S == 0 || max_query_len == 0) return ok();
   if (!out || !query || !k_pool || !v_pool || !block_tables || !context_lens || !query_start)
     return fail(PA_ERR_NULL, "pa_prefill: null pointer argument");
@@ -328,7 +329,7 @@ pa_status pa_prefill(void* out, const void* query, const void* k_pool, const voi
   const int QB = pa::prefill_rows_per_workgroup(G);
   const int64_t grid =
       (int64_t)((max_query_len + QB - 1) / QB) * S * (G > 4 ? G / 4 : 1) * Hkv;
-  if (grid >= ((int64_t)1 << 31))
+  if (grid >= ((int64_t)1 << 31) - 8)   // padded to a multiple of 8 at launch
     return fail(PA_ERR_SHAPE, "pa_prefill: launch too large (%lld workgroups)", (long long)grid);
 
   pa::PrefillArgs a;

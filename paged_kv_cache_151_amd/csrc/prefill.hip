@@ -48,6 +48,11 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kNegBig = -1.0e30f;
+// Lazy rescaling slack in log2 units: softmax weights stay at most 2^kSlack.
+#ifndef PA_PREFILL_SLACK
+#define PA_PREFILL_SLACK 8.0f
+#endif
+constexpr float kSlack = PA_PREFILL_SLACK;
 constexpr int kChunk = 32;                 // tokens per loop step (two 16-token units)
 constexpr int kUnitTok = 16;
 constexpr int kRowBytes = kHeadDim * 2;    // one token row of one KV head
@@ -82,16 +87,22 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   const int m = lane & 15;
   const int kq = lane >> 4;
 
-  // blockIdx -> (rank, s, hg, g), g fastest: every workgroup of one KV head
-  // goes to the same XCD when Hkv is a multiple of 8. Rank 0 is each
-  // sequence's last row block (the most keys), so the longest work starts first.
-  int64_t id = blockIdx.x;
-  const int g = (int)(id % a.Hkv);
-  id /= a.Hkv;
+  // Work order. Workgroups are dealt to the 8 XCDs round-robin by blockIdx,
+  // so XCD x runs work items x * per_xcd, x * per_xcd + 1, ... in order. The
+  // list is ordered (g, s, hg, rank) with the row-block rank fastest: the
+  // row blocks of one (sequence, KV head) run side by side on one XCD and
+  // read its keys and values from that XCD's L2, and each XCD gets a
+  // contiguous range of KV heads across all sequences (balanced when Hkv is
+  // a multiple of 8). Rank 0 is a sequence's last row block (the most keys).
+  const int64_t bid = blockIdx.x;
+  int64_t id = (bid % 8) * a.per_xcd + bid / 8;
+  if (id >= a.n_work) return;
+  const int rank = (int)(id % a.n_rank);
+  id /= a.n_rank;
   const int hg = (int)(id % NHG);
   id /= NHG;
   const int s = (int)(id % a.S);
-  const int rank = (int)(id / a.S);
+  const int g = (int)(id / a.S);
 
   const int qs0 = a.qstart[s];
   const int qs1 = a.qstart[s + 1];
@@ -143,27 +154,28 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
     for (int nn = 0; nn < 8; ++nn) o[t][nn] = f4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Table entries ride in lane registers, 64 blocks at a time (v_readlane
-  // hands the wave its entry); the window moves forward when a unit's block
-  // leaves it. Entries outside the pool are clamped to block 0.
-  const int32_t* trow = a.tables + (int64_t)s * a.MB;
+  // Physical blocks come from the table through scalar loads (the index is
+  // wave-uniform): they are counted apart from the vector loads, so waiting
+  // for a table entry never waits for the K/V tiles in flight. The entries
+  // of chunk c + 1 are requested while chunk c - 1 is still being fetched
+  // and computed. Entries outside the pool are clamped to block 0.
+  typedef const __attribute__((address_space(4))) int32_t* const_i32;
+  const const_i32 trow = (const_i32)(a.tables + (int64_t)s * a.MB);
   const int nblk = (kend + B - 1) / B;
-  int wb = 0;
-  int tbl = lane < nblk ? trow[lane] : 0;
-  auto unit_base = [&](int U, int& nbytes) -> int64_t {
+  // physical block of unit U, or -1 when U holds no visible key
+  auto table_entry = [&](int U) -> int {
+    const int bi = U / UPB;
+    return U * kUnitTok < kend && bi < nblk ? trow[bi] : -1;
+  };
+  auto unit_base = [&](int U, int phys, int& nbytes) -> int64_t {
     const int tok = U * kUnitTok;
-    if (tok >= kend) {                     // past the visible keys: no-op load
+    if (phys < 0) {                        // past the visible keys: no-op load
       nbytes = 0;
       return 0;
     }
     const int valid = L - tok < kUnitTok ? L - tok : kUnitTok;
     nbytes = valid * kRowBytes;
     const int bi = U / UPB;
-    if (bi >= wb + 64) {
-      wb = bi & ~63;
-      tbl = wb + lane < nblk ? trow[wb + lane] : 0;
-    }
-    const int phys = __builtin_amdgcn_readlane(tbl, bi - wb);
     const int safe = (unsigned)phys < (unsigned)a.NB ? phys : 0;
     return (((int64_t)safe * a.Hkv + g) * B + (U - bi * UPB) * kUnitTok) * D;
   };
@@ -172,11 +184,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   // past L reads as zero whether or not the scalar offset is checked too.
   const unsigned k_voff = m * kRowBytes + kq * 16;       // token m, dims 8kq (+32c via soffset)
   const unsigned v_voff = kq * 4 * kRowBytes + m * 16;   // token 4kq, dims 8m
-  auto fetch = [&](Chunk& ch, int c) {
+  auto fetch = [&](Chunk& ch, int c, const int (&ph)[2]) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       int nbytes;
-      const int64_t base = unit_base(2 * c + u, nbytes);
+      const int64_t base = unit_base(2 * c + u, ph[u], nbytes);
       const __amdgpu_buffer_rsrc_t rk = rsrc(a.k_pool + base, nbytes);
       const __amdgpu_buffer_rsrc_t rv = rsrc(a.v_pool + base, nbytes);
 #pragma unroll
@@ -214,49 +226,68 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
                                                        qf[t][cc], acc, 0, 0, 0);
         sc[u] = acc;
       }
+      // Raw scores; the maximum is taken before scaling (the scale is
+      // positive, so the order is the same) and p = 2^(scale_log2 * s - m)
+      // is one fused multiply-add and one exp2 per score.
       float x[8];
       bool vis[8];
       float mx = kNegBig;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        float v = sc[j / 4][j % 4] * a.scale_log2;
+        const float v = sc[j / 4][j % 4];
         vis[j] = !masked || c * kChunk + 16 * (j / 4) + 4 * kq + (j % 4) <= pos[t];
-        v = vis[j] ? v : kNegBig;
         x[j] = v;
-        mx = __builtin_fmaxf(mx, v);
+        mx = __builtin_fmaxf(mx, vis[j] ? v : kNegBig);
       }
       mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16));
       mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = __builtin_fmaxf(mrow[t], mx);
-      const float alpha = __builtin_amdgcn_exp2f(mrow[t] - mnew);
-      mrow[t] = mnew;
-      float ls = lsum[t] * alpha;
+      // Running maximum m (log2 domain, scaled). Lazy rescaling: m is raised,
+      // and the accumulators rescaled, only when some row of the wave would
+      // otherwise see p above 2^kSlack; until then p <= 2^kSlack, exactly
+      // representable in fp16's range. The result is the same softmax: the
+      // final division uses the same m for numerator and denominator.
+      const float mcand = mx > 0.5f * kNegBig ? mx * a.scale_log2 : kNegBig;
+      const bool raise = mcand > mrow[t] + kSlack;
+      if (__builtin_amdgcn_ballot_w64(raise)) {
+        const float mnew = __builtin_fmaxf(mrow[t], mcand);
+        const float alpha = __builtin_amdgcn_exp2f(mrow[t] - mnew);
+        mrow[t] = mnew;
+        lsum[t] *= alpha;
+#pragma unroll
+        for (int nn = 0; nn < 8; ++nn) o[t][nn] *= alpha;
+      }
+      float ls = lsum[t];
       h8 pb;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        float p = __builtin_amdgcn_exp2f(x[j] - mnew);
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(x[j], a.scale_log2, -mrow[t]));
         p = vis[j] ? p : 0.f;
         ls += p;
         pb[j] = (_Float16)p;
       }
       lsum[t] = ls;
 #pragma unroll
-      for (int nn = 0; nn < 8; ++nn) {
-        o[t][nn] *= alpha;
+      for (int nn = 0; nn < 8; ++nn)
         o[t][nn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[nn], pb, o[t][nn], 0, 0, 0);
-      }
     }
   };
 
   if (nchunk > 0) {
     Chunk b0, b1;
-    fetch(b0, 0);
+    int ph[2] = {table_entry(0), table_entry(1)};
+    fetch(b0, 0, ph);
+    ph[0] = table_entry(2);
+    ph[1] = table_entry(3);
     int c = 0;
     while (true) {
-      fetch(b1, c + 1);
+      fetch(b1, c + 1, ph);
+      ph[0] = table_entry(2 * c + 4);
+      ph[1] = table_entry(2 * c + 5);
       compute(b0, c, c >= nfull);
       if (++c >= nchunk) break;
-      fetch(b0, c + 1);
+      fetch(b0, c + 1, ph);
+      ph[0] = table_entry(2 * c + 4);
+      ph[1] = table_entry(2 * c + 5);
       compute(b1, c, c >= nfull);
       if (++c >= nchunk) break;
     }
@@ -310,12 +341,16 @@ hipError_t launch_prefill(const PrefillArgs& a, int B, int G, int max_query_len,
                           hipStream_t stream) {
   const int QB = prefill_rows_per_workgroup(G);
   const int nhg = G > 4 ? G / 4 : 1;
-  const int64_t grid = (int64_t)((max_query_len + QB - 1) / QB) * a.S * nhg * a.Hkv;
-  if (grid == 0) return hipSuccess;
+  PrefillArgs b = a;
+  b.n_rank = (max_query_len + QB - 1) / QB;
+  b.n_work = (int64_t)b.n_rank * a.S * nhg * a.Hkv;
+  b.per_xcd = (b.n_work + 7) / 8;
+  const int64_t grid = 8 * b.per_xcd;
+  if (b.n_work == 0) return hipSuccess;
   switch (B) {
-    case 16: return launch_bt<16>(a, G, grid, stream);
-    case 32: return launch_bt<32>(a, G, grid, stream);
-    default: return launch_bt<0>(a, G, grid, stream);
+    case 16: return launch_bt<16>(b, G, grid, stream);
+    case 32: return launch_bt<32>(b, G, grid, stream);
+    default: return launch_bt<0>(b, G, grid, stream);
   }
 }
 

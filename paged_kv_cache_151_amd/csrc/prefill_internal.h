@@ -23,6 +23,9 @@ struct PrefillArgs {
   const int32_t* qstart;             // [S+1] first packed query row of each sequence
   int S, T, Hq, Hkv, NB, MB, B;
   float scale_log2;                  // softmax scale times log2(e)
+  int n_rank;                        // row blocks per (sequence, head group) in the launch
+  int64_t n_work;                    // work items: n_rank * S * head groups * Hkv
+  int64_t per_xcd;                   // work items per XCD: ceil(n_work / 8)
 };
 
 // Query rows one prefill workgroup covers for a group of G query heads.

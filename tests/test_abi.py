@@ -151,5 +151,6 @@ def test_prefill_host_validation(lib):
     assert prefill(lib, out=FAKE + 2) == PA_ERR_ALIGN
     assert prefill(lib, qs=FAKE + 2) == PA_ERR_ALIGN
     assert prefill(lib, scale=float("nan")) == PA_ERR_SHAPE
+    assert prefill(lib, scale=-0.5) == PA_ERR_SHAPE
     assert prefill(lib, S=0) == PA_OK
     assert prefill(lib, maxq=0, out=None) == PA_OK

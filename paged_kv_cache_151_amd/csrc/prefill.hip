@@ -14,26 +14,32 @@
 // Work decomposition. A wave owns 16 * QT query rows of one query head. A
 // workgroup is 4 waves over one KV head g: 4 query heads of g with the same
 // rows when the group has at least 4 heads, otherwise 4 / G row tiles of each
-// of the G heads; all 4 waves walk the same tokens, so a K/V tile fetched by
-// one is served to the others from the CU's cache. Tokens are taken 32 at a
-// time (a chunk: two 16-token units of one KV head, each a contiguous 4 KiB
-// tile in the pool).
+// of the G heads. Keys and values are taken 32 tokens at a time (a chunk: two
+// 16-token units, each a contiguous 4 KiB tile of the pool per KV head). The
+// workgroup loads each chunk once, with loads in which consecutive lanes read
+// consecutive 16-byte pieces, two chunks ahead of the one being computed, and
+// stages it in LDS; the 4 waves read their matrix operands from there.
 //
 // Matrix products (v_mfma_f32_16x16x32_f16; lane l = 16 kq + m):
-//   scores   S^T = K Q^T per unit: the A operand is the key tile itself (lane
-//            holds token m, dims 32c + 8kq .. +7, one 16-byte load from the
-//            pool), the B operand the query rows held in registers; lane l
-//            receives S for query row m and tokens 4kq + r.
+//   scores   S^T = K Q^T per unit: the A operand is key token m, dims
+//            32c + 8kq .. +7 (one 16-byte LDS read), the B operand the query
+//            rows held in registers; lane l receives S for query row m and
+//            tokens 4kq + r of the unit.
 //   output   O^T = V^T P^T per chunk: the B operand is P exactly as the score
-//            product left it (query m, the lane's 8 tokens), the A operand
-//            carries V for the same 8 tokens at one output dimension. The 16
-//            dimensions of product n are 8m' + n (m' the A row), so lane l
-//            loads dims 8m .. 8m+7 of its 8 tokens with 16-byte loads and
-//            regroups them in registers: no LDS transpose. Lane l ends with
-//            O[row m][dims 32kq + 8r + n].
+//            product left it (query m; tokens 4kq + r of both units), the A
+//            operand V for the same 8 tokens at dim 16n + m, gathered from the
+//            row-major V tile by two transposing LDS reads (ds_read_b64_tr_b16:
+//            in each 16-lane group, lane i receives 16-bit word i % 4 from the
+//            address of lane 4e + i / 4 as its element e). Lane l ends with
+//            O[row m][dims 16n + 4kq + r].
 // Every per-row softmax quantity (running max, sum, rescale factor) lives in
 // the lanes of that row, so the only cross-lane steps are the two row-max
 // exchanges per chunk and the final sum.
+//
+// LDS layout: a chunk is 32 token rows of 256 bytes for K and for V, each row
+// split into 16 pieces of 16 bytes. Piece c of row r is stored at position
+// c ^ (r % 16) for K and c ^ 2 (r % 8) for V, which spreads the operand reads
+// of a wave over all banks.
 //
 // Masking: keys and values past the sequence's L tokens are fetched as zeros
 // by the buffer range check (so NaN or Inf in unused slots never enters a
@@ -44,8 +50,10 @@ namespace pa {
 namespace {
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef short s4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kNegBig = -1.0e30f;
 // Lazy rescaling slack in log2 units: softmax weights stay at most 2^kSlack.
@@ -56,18 +64,28 @@ constexpr float kSlack = PA_PREFILL_SLACK;
 constexpr int kChunk = 32;                 // tokens per loop step (two 16-token units)
 constexpr int kUnitTok = 16;
 constexpr int kRowBytes = kHeadDim * 2;    // one token row of one KV head
+constexpr int kStageBytes = kChunk * kRowBytes;   // 8 KiB: one chunk of K (or V)
 constexpr int kRsrcWord3 = 0x00020000;     // raw buffer, gfx9 family
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const _Float16* base, int nbytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16*>(base), 0, nbytes, kRsrcWord3);
 }
 
-// Registers of one chunk: k[u][c] = key token m of unit u, dims 32c + 8kq ..;
-// v[j] = value row of token tok(8kq + j) at dims 8m .. 8m+7, where the lane's
-// token j is 16 (j / 4) + 4kq + (j % 4) of the chunk.
-struct Chunk {
-  u32x4 k[2][4];
-  u32x4 v[8];
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) s4 lds_s4;
+
+// byte offset of 16-byte piece c of token row r in a K (or V) stage
+__device__ __forceinline__ int k_pos(int r, int c) { return r * kRowBytes + ((c ^ (r & 15)) << 4); }
+__device__ __forceinline__ int v_pos(int r, int c) {
+  return r * kRowBytes + ((c ^ ((r & 7) << 1)) << 4);
+}
+
+// What one thread carries from global memory to LDS for a chunk: 16 bytes of
+// K and of V from each of the two units, at the same place in each tile.
+struct Stage {
+  u32x4 k[2];
+  u32x4 v[2];
 };
 
 template <int BT, int G, int QT, bool NT>
@@ -79,11 +97,14 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   constexpr int QB = RW * QR;              // query rows per workgroup
   constexpr int NHG = G / HW;              // workgroups per KV head and row block
   static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
+  __shared__ __attribute__((aligned(16))) unsigned char s_k[2][kStageBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char s_v[2][kStageBytes];
   const int B = BT > 0 ? BT : a.B;
   const int UPB = B / kUnitTok;
 
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m = lane & 15;
   const int kq = lane >> 4;
 
@@ -109,15 +130,32 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   if (qs0 < 0 || qs1 > a.T || qs1 <= qs0) return;
   const int n = qs1 - qs0;
   const int nqb = (n + QB - 1) / QB;
-  if (rank >= nqb) return;
+  if (rank >= nqb) return;                 // whole workgroup, before any barrier
   const int qb = nqb - 1 - rank;
   int L = a.lens[s];
   L = L < 0 ? 0 : L;
   L = L > a.MB * B ? a.MB * B : L;
+  const int base_pos = L - n;              // row j sits at position base_pos + j
+
+  // keys the workgroup walks: [0, kend_wg), as far as its last row sees
+  const int jl_wg = (qb * QB + QB < n ? qb * QB + QB : n) - 1;
+  int kend_wg = base_pos + jl_wg + 1;
+  kend_wg = kend_wg > L ? L : kend_wg;
+  kend_wg = kend_wg < 0 ? 0 : kend_wg;
+  const int nchunk_wg = (kend_wg + kChunk - 1) / kChunk;
+  const int nblk = (kend_wg + B - 1) / B;
+
+  // this wave's rows and the chunks it computes
   const int hq = g * G + hg * HW + wave % HW;
   const int j0 = qb * QB + (wave / HW) * QR;
-  if (j0 >= n) return;                     // no barriers below: waves are independent
-  const int base_pos = L - n;              // row j sits at position base_pos + j
+  const bool wave_rows = j0 < n;
+  const int jl = (j0 + QR < n ? j0 + QR : n) - 1;
+  int kend = base_pos + jl + 1;
+  kend = kend > L ? L : kend;
+  kend = kend < 0 ? 0 : kend;
+  const int nchunk = wave_rows ? (kend + kChunk - 1) / kChunk : 0;
+  int nfull = base_pos + j0 + 1 >= 0 ? (base_pos + j0 + 1) / kChunk : 0;
+  nfull = nfull > nchunk ? nchunk : nfull;
 
   // query rows as B operands
   h8 qf[QT][4];
@@ -135,15 +173,6 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
     }
   }
 
-  const int jl = (j0 + QR < n ? j0 + QR : n) - 1;   // last valid row of the wave
-  int kend = base_pos + jl + 1;                      // keys [0, kend) can be visible
-  kend = kend > L ? L : kend;
-  kend = kend < 0 ? 0 : kend;
-  const int nchunk = (kend + kChunk - 1) / kChunk;
-  // chunks whose every key is visible to every row of the wave
-  int nfull = base_pos + j0 + 1 >= 0 ? (base_pos + j0 + 1) / kChunk : 0;
-  nfull = nfull > nchunk ? nchunk : nfull;
-
   float mrow[QT], lsum[QT];
   f4 o[QT][8];
 #pragma unroll
@@ -155,64 +184,74 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   }
 
   // Physical blocks come from the table through scalar loads (the index is
-  // wave-uniform): they are counted apart from the vector loads, so waiting
-  // for a table entry never waits for the K/V tiles in flight. The entries
-  // of chunk c + 1 are requested while chunk c - 1 is still being fetched
-  // and computed. Entries outside the pool are clamped to block 0.
+  // uniform): they are counted apart from the vector loads, so waiting for a
+  // table entry never waits for K/V data in flight. Entries outside the pool
+  // are clamped to block 0.
   typedef const __attribute__((address_space(4))) int32_t* const_i32;
   const const_i32 trow = (const_i32)(a.tables + (int64_t)s * a.MB);
-  const int nblk = (kend + B - 1) / B;
-  // physical block of unit U, or -1 when U holds no visible key
+  // physical block of unit U, or -1 when U holds no key the workgroup needs
   auto table_entry = [&](int U) -> int {
     const int bi = U / UPB;
-    return U * kUnitTok < kend && bi < nblk ? trow[bi] : -1;
+    return U * kUnitTok < kend_wg && bi < nblk ? trow[bi] : -1;
   };
-  auto unit_base = [&](int U, int phys, int& nbytes) -> int64_t {
-    const int tok = U * kUnitTok;
-    if (phys < 0) {                        // past the visible keys: no-op load
-      nbytes = 0;
-      return 0;
-    }
-    const int valid = L - tok < kUnitTok ? L - tok : kUnitTok;
-    nbytes = valid * kRowBytes;
-    const int bi = U / UPB;
-    const int safe = (unsigned)phys < (unsigned)a.NB ? phys : 0;
-    return (((int64_t)safe * a.Hkv + g) * B + (U - bi * UPB) * kUnitTok) * D;
-  };
-  // Byte offsets inside a unit's 4 KiB tile. The token of every load sits in
-  // the vector offset, which the range check always covers, so a token at or
-  // past L reads as zero whether or not the scalar offset is checked too.
-  const unsigned k_voff = m * kRowBytes + kq * 16;       // token m, dims 8kq (+32c via soffset)
-  const unsigned v_voff = kq * 4 * kRowBytes + m * 16;   // token 4kq, dims 8m
-  auto fetch = [&](Chunk& ch, int c, const int (&ph)[2]) {
+
+  // Thread tid carries piece tid % 16 of token row tid / 16 of both units; a
+  // wave's load covers 4 whole rows (1 KiB) of a tile.
+  const int ld_row = tid >> 4;
+  const int ld_c = tid & 15;
+  const unsigned ld_off = ld_row * kRowBytes + ld_c * 16;
+  auto fetch = [&](Stage& st, int c, const int (&ph)[2]) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      int nbytes;
-      const int64_t base = unit_base(2 * c + u, ph[u], nbytes);
-      const __amdgpu_buffer_rsrc_t rk = rsrc(a.k_pool + base, nbytes);
-      const __amdgpu_buffer_rsrc_t rv = rsrc(a.v_pool + base, nbytes);
+      const int U = 2 * c + u;
+      int nbytes = 0;
+      int64_t base = 0;
+      if (ph[u] >= 0) {
+        const int valid = L - U * kUnitTok < kUnitTok ? L - U * kUnitTok : kUnitTok;
+        nbytes = valid * kRowBytes;
+        const int bi = U / UPB;
+        const int safe = (unsigned)ph[u] < (unsigned)a.NB ? ph[u] : 0;
+        base = (((int64_t)safe * a.Hkv + g) * B + (U - bi * UPB) * kUnitTok) * D;
+      }
+      st.k[u] = __builtin_amdgcn_raw_buffer_load_b128(rsrc(a.k_pool + base, nbytes), ld_off, 0,
+                                                      NT ? 2 : 0);
+      st.v[u] = __builtin_amdgcn_raw_buffer_load_b128(rsrc(a.v_pool + base, nbytes), ld_off, 0,
+                                                      NT ? 2 : 0);
+    }
+  };
+  auto put = [&](const Stage& st, int buf) {
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc)
-        ch.k[u][cc] = __builtin_amdgcn_raw_buffer_load_b128(rk, k_voff, cc * 64, NT ? 2 : 0);
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        ch.v[4 * u + r] =
-            __builtin_amdgcn_raw_buffer_load_b128(rv, v_voff + r * kRowBytes, 0, NT ? 2 : 0);
+    for (int u = 0; u < 2; ++u) {
+      const int row = 16 * u + ld_row;
+      *(lds_u32x4*)((lds_u8*)&s_k[buf][0] + k_pos(row, ld_c)) = st.k[u];
+      *(lds_u32x4*)((lds_u8*)&s_v[buf][0] + v_pos(row, ld_c)) = st.v[u];
     }
   };
 
-  auto compute = [&](const Chunk& ch, int c, bool masked) {
-    // V^T operands: product nn takes dim 8m + nn of the lane's 8 tokens
+  // Operand reads, per lane:
+  //   K, unit u, dim block cc: row 16u + m, piece 4cc + kq;
+  //   V, product nn: rows 4kq + m/4 (unit 0) and 16 + 4kq + m/4 (unit 1),
+  //   dims 16nn + 4 (m % 4) .. +3, i.e. half (m % 2) of piece 2nn + (m % 4) / 2.
+  const int v_row = 4 * kq + (m >> 2);
+  auto compute = [&](int buf, int c, bool masked) {
+    const lds_u8* kb = (const lds_u8*)&s_k[buf][0];
+    const lds_u8* vb = (const lds_u8*)&s_v[buf][0];
+    h8 ka[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc)
+        ka[u][cc] = __builtin_bit_cast(h8, *(const lds_u32x4*)(kb + k_pos(16 * u + m, 4 * cc + kq)));
+    }
     h8 va[8];
-    {
-      h8 vr[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) vr[j] = __builtin_bit_cast(h8, ch.v[j]);
-#pragma unroll
-      for (int nn = 0; nn < 8; ++nn) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) va[nn][j] = vr[j][nn];
-      }
+    for (int nn = 0; nn < 8; ++nn) {
+      const int off = v_pos(v_row, 2 * nn + ((m & 3) >> 1)) + (m & 1) * 8;
+      const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(vb + off));
+      const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(vb + off + 16 * kRowBytes));
+      const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+      const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+      va[nn] = __builtin_bit_cast(h8, u32x4{l2.x, l2.y, h2.x, h2.y});
     }
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
@@ -222,13 +261,12 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
         f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, ch.k[u][cc]),
-                                                       qf[t][cc], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[u][cc], qf[t][cc], acc, 0, 0, 0);
         sc[u] = acc;
       }
       // Raw scores; the maximum is taken before scaling (the scale is
-      // positive, so the order is the same) and p = 2^(scale_log2 * s - m)
-      // is one fused multiply-add and one exp2 per score.
+      // non-negative, so the order is kept) and p = 2^(scale_log2 * s - m) is
+      // one fused multiply-add and one exp2 per score.
       float x[8];
       bool vis[8];
       float mx = kNegBig;
@@ -243,9 +281,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
       mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
       // Running maximum m (log2 domain, scaled). Lazy rescaling: m is raised,
       // and the accumulators rescaled, only when some row of the wave would
-      // otherwise see p above 2^kSlack; until then p <= 2^kSlack, exactly
-      // representable in fp16's range. The result is the same softmax: the
-      // final division uses the same m for numerator and denominator.
+      // otherwise see p above 2^kSlack; until then p <= 2^kSlack, well inside
+      // fp16's range. The result is the same softmax: the final division uses
+      // the same m for numerator and denominator.
       const float mcand = mx > 0.5f * kNegBig ? mx * a.scale_log2 : kNegBig;
       const bool raise = mcand > mrow[t] + kSlack;
       if (__builtin_amdgcn_ballot_w64(raise)) {
@@ -272,28 +310,48 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
     }
   };
 
-  if (nchunk > 0) {
-    Chunk b0, b1;
+  // Pipeline: chunk k travels in register set k % 2 and is computed from LDS
+  // stage k % 2. In step c the waves compute chunk c, store chunk c + 1
+  // (loaded two steps earlier) into the other stage, meet at the barrier,
+  // and start the loads of chunk c + 3 into the register set just emptied.
+  // Table entries are read one step before their loads are issued. Every
+  // wave runs the same steps (barriers); a wave whose rows end earlier skips
+  // the arithmetic of chunks it does not need. Past the last chunk the loads
+  // have an empty range: no memory is touched.
+  if (nchunk_wg > 0) {
+    Stage r0, r1;
     int ph[2] = {table_entry(0), table_entry(1)};
-    fetch(b0, 0, ph);
+    fetch(r0, 0, ph);
     ph[0] = table_entry(2);
     ph[1] = table_entry(3);
+    fetch(r1, 1, ph);
+    ph[0] = table_entry(4);
+    ph[1] = table_entry(5);
+    put(r0, 0);
+    __syncthreads();
+    fetch(r0, 2, ph);
+    ph[0] = table_entry(6);
+    ph[1] = table_entry(7);
     int c = 0;
     while (true) {
-      fetch(b1, c + 1, ph);
-      ph[0] = table_entry(2 * c + 4);
-      ph[1] = table_entry(2 * c + 5);
-      compute(b0, c, c >= nfull);
-      if (++c >= nchunk) break;
-      fetch(b0, c + 1, ph);
-      ph[0] = table_entry(2 * c + 4);
-      ph[1] = table_entry(2 * c + 5);
-      compute(b1, c, c >= nfull);
-      if (++c >= nchunk) break;
+      if (c < nchunk) compute(0, c, c >= nfull);
+      put(r1, 1);
+      __syncthreads();
+      fetch(r1, c + 3, ph);
+      ph[0] = table_entry(2 * c + 8);
+      ph[1] = table_entry(2 * c + 9);
+      if (++c >= nchunk_wg) break;
+      if (c < nchunk) compute(1, c, c >= nfull);
+      put(r0, 0);
+      __syncthreads();
+      fetch(r0, c + 3, ph);
+      ph[0] = table_entry(2 * c + 8);
+      ph[1] = table_entry(2 * c + 9);
+      if (++c >= nchunk_wg) break;
     }
   }
 
-  // normalise and store: lane holds row m, dims 32kq + 8r + nn
+  // normalise and store: lane holds row m, dims 16nn + 4kq + r
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
     float lt = lsum[t];
@@ -302,13 +360,14 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
     const int j = j0 + 16 * t + m;
     if (j >= n) continue;
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    _Float16* orow = a.out + ((int64_t)(qs0 + j) * a.Hq + hq) * D + 32 * kq;
+    _Float16* orow = a.out + ((int64_t)(qs0 + j) * a.Hq + hq) * D + 4 * kq;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      h8 ov;
+    for (int nn = 0; nn < 8; ++nn) {
+      typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+      h4 ov;
 #pragma unroll
-      for (int nn = 0; nn < 8; ++nn) ov[nn] = (_Float16)(o[t][nn][r] * inv);
-      *reinterpret_cast<u32x4*>(orow + 8 * r) = __builtin_bit_cast(u32x4, ov);
+      for (int r = 0; r < 4; ++r) ov[r] = (_Float16)(o[t][nn][r] * inv);
+      *reinterpret_cast<u32x2*>(orow + 16 * nn) = __builtin_bit_cast(u32x2, ov);
     }
   }
 }

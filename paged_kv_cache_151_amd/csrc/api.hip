@@ -326,9 +326,7 @@ pa_status pa_prefill(void* out, const void* query, const void* k_pool, const voi
     return fail(PA_ERR_ALIGN, "pa_prefill: index arrays misaligned");
   if ((int64_t)T * Hq * D >= ((int64_t)1 << 62))
     return fail(PA_ERR_SHAPE, "pa_prefill: T too large");
-  const int QB = pa::prefill_rows_per_workgroup(G);
-  const int64_t grid =
-      (int64_t)((max_query_len + QB - 1) / QB) * S * (G > 4 ? G / 4 : 1) * Hkv;
+  const int64_t grid = pa::prefill_work_items(G, S, Hkv, max_query_len);
   if (grid >= ((int64_t)1 << 31) - 8)   // padded to a multiple of 8 at launch
     return fail(PA_ERR_SHAPE, "pa_prefill: launch too large (%lld workgroups)", (long long)grid);
 

@@ -61,10 +61,8 @@ constexpr float kNegBig = -1.0e30f;
 #define PA_PREFILL_SLACK 8.0f
 #endif
 constexpr float kSlack = PA_PREFILL_SLACK;
-constexpr int kChunk = 32;                 // tokens per loop step (two 16-token units)
 constexpr int kUnitTok = 16;
 constexpr int kRowBytes = kHeadDim * 2;    // one token row of one KV head
-constexpr int kStageBytes = kChunk * kRowBytes;   // 8 KiB: one chunk of K (or V)
 constexpr int kRsrcWord3 = 0x00020000;     // raw buffer, gfx9 family
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const _Float16* base, int nbytes) {
@@ -81,22 +79,38 @@ __device__ __forceinline__ int v_pos(int r, int c) {
   return r * kRowBytes + ((c ^ ((r & 7) << 1)) << 4);
 }
 
-// What one thread carries from global memory to LDS for a chunk: 16 bytes of
-// K and of V from each of the two units, at the same place in each tile.
-struct Stage {
-  u32x4 k[2];
-  u32x4 v[2];
+template <bool V>
+struct Flag {
+  static constexpr bool value = V;
 };
 
-template <int BT, int G, int QT, bool NT>
-__global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
+// A chunk of KC tokens is 32 KC pieces of 16 bytes: pieces x < 16 KC are K,
+// the rest V; within each, x / 256 is the 16-token unit, (x / 16) % 16 the
+// token row of the unit and x % 16 the piece of the row. Thread t of a
+// workgroup of NTH threads carries pieces t, t + NTH, ...: consecutive lanes
+// read consecutive 16-byte pieces.
+template <int NP>
+struct Stage {
+  u32x4 p[NP];
+};
+
+template <int BT, int G, int QT, int NW, int KC, bool NT>
+__global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
   constexpr int D = kHeadDim;
-  constexpr int HW = G < 4 ? G : 4;        // query heads in a workgroup
-  constexpr int RW = 4 / HW;               // row tiles per head in a workgroup
+  constexpr int HW = G < NW ? G : NW;      // query heads in a workgroup
+  constexpr int RW = NW / HW;              // row tiles per head in a workgroup
   constexpr int QR = 16 * QT;              // query rows per wave
   constexpr int QB = RW * QR;              // query rows per workgroup
   constexpr int NHG = G / HW;              // workgroups per KV head and row block
+  constexpr int NTH = NW * 64;             // threads
+  constexpr int NU = KC / kUnitTok;        // 16-token units per chunk
+  constexpr int NKS = KC / 32;             // 32-token steps of the value product
+  constexpr int NPC = 32 * KC;             // 16-byte pieces per chunk (K and V)
+  constexpr int NP = NPC / NTH;            // pieces per thread and chunk
+  constexpr int kStageBytes = KC * kRowBytes;
   static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
+  static_assert(NW == 4 || NW == 8, "waves per workgroup");
+  static_assert(KC == 32 || KC == 64, "keys per step");
   __shared__ __attribute__((aligned(16))) unsigned char s_k[2][kStageBytes];
   __shared__ __attribute__((aligned(16))) unsigned char s_v[2][kStageBytes];
   const int B = BT > 0 ? BT : a.B;
@@ -142,7 +156,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   int kend_wg = base_pos + jl_wg + 1;
   kend_wg = kend_wg > L ? L : kend_wg;
   kend_wg = kend_wg < 0 ? 0 : kend_wg;
-  const int nchunk_wg = (kend_wg + kChunk - 1) / kChunk;
+  const int nchunk_wg = (kend_wg + KC - 1) / KC;
   const int nblk = (kend_wg + B - 1) / B;
 
   // this wave's rows and the chunks it computes
@@ -153,8 +167,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   int kend = base_pos + jl + 1;
   kend = kend > L ? L : kend;
   kend = kend < 0 ? 0 : kend;
-  const int nchunk = wave_rows ? (kend + kChunk - 1) / kChunk : 0;
-  int nfull = base_pos + j0 + 1 >= 0 ? (base_pos + j0 + 1) / kChunk : 0;
+  const int nchunk = wave_rows ? (kend + KC - 1) / KC : 0;
+  int nfull = base_pos + j0 + 1 >= 0 ? (base_pos + j0 + 1) / KC : 0;
   nfull = nfull > nchunk ? nchunk : nfull;
 
   // query rows as B operands
@@ -195,36 +209,45 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
     return U * kUnitTok < kend_wg && bi < nblk ? trow[bi] : -1;
   };
 
-  // Thread tid carries piece tid % 16 of token row tid / 16 of both units; a
-  // wave's load covers 4 whole rows (1 KiB) of a tile.
-  const int ld_row = tid >> 4;
-  const int ld_c = tid & 15;
-  const unsigned ld_off = ld_row * kRowBytes + ld_c * 16;
-  auto fetch = [&](Stage& st, int c, const int (&ph)[2]) {
+  auto fetch = [&](Stage<NP>& st, int c, const int (&ph)[NU]) {
+    int nbytes[NU];
+    int64_t base[NU];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int U = 2 * c + u;
-      int nbytes = 0;
-      int64_t base = 0;
+    for (int u = 0; u < NU; ++u) {
+      const int U = NU * c + u;
+      nbytes[u] = 0;
+      base[u] = 0;
       if (ph[u] >= 0) {
         const int valid = L - U * kUnitTok < kUnitTok ? L - U * kUnitTok : kUnitTok;
-        nbytes = valid * kRowBytes;
+        nbytes[u] = valid * kRowBytes;
         const int bi = U / UPB;
         const int safe = (unsigned)ph[u] < (unsigned)a.NB ? ph[u] : 0;
-        base = (((int64_t)safe * a.Hkv + g) * B + (U - bi * UPB) * kUnitTok) * D;
+        base[u] = (((int64_t)safe * a.Hkv + g) * B + (U - bi * UPB) * kUnitTok) * D;
       }
-      st.k[u] = __builtin_amdgcn_raw_buffer_load_b128(rsrc(a.k_pool + base, nbytes), ld_off, 0,
-                                                      NT ? 2 : 0);
-      st.v[u] = __builtin_amdgcn_raw_buffer_load_b128(rsrc(a.v_pool + base, nbytes), ld_off, 0,
+    }
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      // The wave's first piece (64 wave + i NTH) is a multiple of 64, so the
+      // unit and the pool (K or V) are the same for all its lanes; they are
+      // computed from the wave index so the compiler sees a uniform resource.
+      const int xw = wave * 64 + i * NTH;
+      const int u = (xw % (16 * KC)) >> 8;
+      const unsigned off = (unsigned)((xw + lane) & 255) * 16;
+      const _Float16* pool = xw < 16 * KC ? a.k_pool : a.v_pool;
+      st.p[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc(pool + base[u], nbytes[u]), off, 0,
                                                       NT ? 2 : 0);
     }
   };
-  auto put = [&](const Stage& st, int buf) {
+  auto put = [&](const Stage<NP>& st, int buf) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int row = 16 * u + ld_row;
-      *(lds_u32x4*)((lds_u8*)&s_k[buf][0] + k_pos(row, ld_c)) = st.k[u];
-      *(lds_u32x4*)((lds_u8*)&s_v[buf][0] + v_pos(row, ld_c)) = st.v[u];
+    for (int i = 0; i < NP; ++i) {
+      const int x = tid + i * NTH;
+      const int row = (x % (16 * KC)) >> 4;
+      const int c16 = x & 15;
+      if (x < 16 * KC)
+        *(lds_u32x4*)((lds_u8*)&s_k[buf][0] + k_pos(row, c16)) = st.p[i];
+      else
+        *(lds_u32x4*)((lds_u8*)&s_v[buf][0] + v_pos(row, c16)) = st.p[i];
     }
   };
 
@@ -233,31 +256,35 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
   //   V, product nn: rows 4kq + m/4 (unit 0) and 16 + 4kq + m/4 (unit 1),
   //   dims 16nn + 4 (m % 4) .. +3, i.e. half (m % 2) of piece 2nn + (m % 4) / 2.
   const int v_row = 4 * kq + (m >> 2);
-  auto compute = [&](int buf, int c, bool masked) {
+  auto compute = [&](int buf, int c, auto masked_flag) {
+    constexpr bool masked = decltype(masked_flag)::value;
     const lds_u8* kb = (const lds_u8*)&s_k[buf][0];
     const lds_u8* vb = (const lds_u8*)&s_v[buf][0];
-    h8 ka[2][4];
+    h8 ka[NU][4];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < NU; ++u) {
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc)
         ka[u][cc] = __builtin_bit_cast(h8, *(const lds_u32x4*)(kb + k_pos(16 * u + m, 4 * cc + kq)));
     }
-    h8 va[8];
+    h8 va[NKS][8];
 #pragma unroll
-    for (int nn = 0; nn < 8; ++nn) {
-      const int off = v_pos(v_row, 2 * nn + ((m & 3) >> 1)) + (m & 1) * 8;
-      const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(vb + off));
-      const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(vb + off + 16 * kRowBytes));
-      const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
-      const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
-      va[nn] = __builtin_bit_cast(h8, u32x4{l2.x, l2.y, h2.x, h2.y});
+    for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+      for (int nn = 0; nn < 8; ++nn) {
+        const int off = v_pos(32 * ks + v_row, 2 * nn + ((m & 3) >> 1)) + (m & 1) * 8;
+        const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(vb + off));
+        const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(vb + off + 16 * kRowBytes));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+        const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+        va[ks][nn] = __builtin_bit_cast(h8, u32x4{l2.x, l2.y, h2.x, h2.y});
+      }
     }
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
-      f4 sc[2];
+      f4 sc[NU];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < NU; ++u) {
         f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc)
@@ -267,13 +294,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
       // Raw scores; the maximum is taken before scaling (the scale is
       // non-negative, so the order is kept) and p = 2^(scale_log2 * s - m) is
       // one fused multiply-add and one exp2 per score.
-      float x[8];
-      bool vis[8];
+      float x[4 * NU];
+      bool vis[4 * NU];
       float mx = kNegBig;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < 4 * NU; ++j) {
         const float v = sc[j / 4][j % 4];
-        vis[j] = !masked || c * kChunk + 16 * (j / 4) + 4 * kq + (j % 4) <= pos[t];
+        vis[j] = !masked || c * KC + 16 * (j / 4) + 4 * kq + (j % 4) <= pos[t];
         x[j] = v;
         mx = __builtin_fmaxf(mx, vis[j] ? v : kNegBig);
       }
@@ -295,58 +322,68 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
         for (int nn = 0; nn < 8; ++nn) o[t][nn] *= alpha;
       }
       float ls = lsum[t];
-      h8 pb;
+      h8 pb[NKS];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < 4 * NU; ++j) {
         float p = __builtin_amdgcn_exp2f(__builtin_fmaf(x[j], a.scale_log2, -mrow[t]));
         p = vis[j] ? p : 0.f;
         ls += p;
-        pb[j] = (_Float16)p;
+        pb[j / 8][j % 8] = (_Float16)p;
       }
       lsum[t] = ls;
 #pragma unroll
-      for (int nn = 0; nn < 8; ++nn)
-        o[t][nn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[nn], pb, o[t][nn], 0, 0, 0);
+      for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+        for (int nn = 0; nn < 8; ++nn)
+          o[t][nn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[ks][nn], pb[ks], o[t][nn], 0, 0, 0);
+      }
     }
   };
 
   // Pipeline: chunk k travels in register set k % 2 and is computed from LDS
-  // stage k % 2. In step c the waves compute chunk c, store chunk c + 1
-  // (loaded two steps earlier) into the other stage, meet at the barrier,
-  // and start the loads of chunk c + 3 into the register set just emptied.
-  // Table entries are read one step before their loads are issued. Every
-  // wave runs the same steps (barriers); a wave whose rows end earlier skips
-  // the arithmetic of chunks it does not need. Past the last chunk the loads
-  // have an empty range: no memory is touched.
+  // stage k % 2. Iteration c: barrier (chunk c is in LDS, stage (c + 1) % 2 is
+  // free), start the loads of chunk c + 2 into the register set chunk c has
+  // left, compute chunk c, store chunk c + 1 into the other stage. Two chunks
+  // are in flight while a chunk is computed. At the top of an iteration only
+  // the loads of chunk c + 1 are outstanding: with a single group in flight
+  // across the loop edge the compiler's wait counts stay exact (with two it
+  // waited for both before every store). Table entries are read one
+  // iteration before their loads. Every wave runs the same iterations
+  // (barriers); a wave whose rows end earlier skips the arithmetic of chunks
+  // it does not need. Past the last chunk the loads have an empty range: no
+  // memory is touched.
   if (nchunk_wg > 0) {
-    Stage r0, r1;
-    int ph[2] = {table_entry(0), table_entry(1)};
+    Stage<NP> r0, r1;
+    int ph[NU];
+    auto entries = [&](int chunk) {
+#pragma unroll
+      for (int u = 0; u < NU; ++u) ph[u] = table_entry(NU * chunk + u);
+    };
+    entries(0);
     fetch(r0, 0, ph);
-    ph[0] = table_entry(2);
-    ph[1] = table_entry(3);
+    entries(1);
     fetch(r1, 1, ph);
-    ph[0] = table_entry(4);
-    ph[1] = table_entry(5);
+    entries(2);
     put(r0, 0);
-    __syncthreads();
-    fetch(r0, 2, ph);
-    ph[0] = table_entry(6);
-    ph[1] = table_entry(7);
     int c = 0;
     while (true) {
-      if (c < nchunk) compute(0, c, c >= nfull);
+      __syncthreads();
+      fetch(r0, c + 2, ph);
+      entries(c + 3);
+      if (c < nchunk) {
+        if (c >= nfull) compute(0, c, Flag<true>{});
+        else compute(0, c, Flag<false>{});
+      }
       put(r1, 1);
-      __syncthreads();
-      fetch(r1, c + 3, ph);
-      ph[0] = table_entry(2 * c + 8);
-      ph[1] = table_entry(2 * c + 9);
       if (++c >= nchunk_wg) break;
-      if (c < nchunk) compute(1, c, c >= nfull);
-      put(r0, 0);
       __syncthreads();
-      fetch(r0, c + 3, ph);
-      ph[0] = table_entry(2 * c + 8);
-      ph[1] = table_entry(2 * c + 9);
+      fetch(r1, c + 2, ph);
+      entries(c + 3);
+      if (c < nchunk) {
+        if (c >= nfull) compute(1, c, Flag<true>{});
+        else compute(1, c, Flag<false>{});
+      }
+      put(r0, 0);
       if (++c >= nchunk_wg) break;
     }
   }
@@ -374,7 +411,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillArgs a) {
 
 template <int BT, int G>
 hipError_t launch_g(const PrefillArgs& a, int64_t grid, hipStream_t stream) {
-  prefill_kernel<BT, G, kPrefillRowTiles, kDecodeNontemporal><<<(unsigned)grid, 256, 0, stream>>>(a);
+  prefill_kernel<BT, G, kPrefillRowTiles, kPrefillWaves, kPrefillChunk, kDecodeNontemporal>
+      <<<(unsigned)grid, kPrefillWaves * 64, 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -392,17 +430,22 @@ hipError_t launch_bt(const PrefillArgs& a, int G, int64_t grid, hipStream_t stre
 }  // namespace
 
 int prefill_rows_per_workgroup(int G) {
-  const int hw = G < 4 ? G : 4;
-  return (4 / hw) * 16 * kPrefillRowTiles;
+  const int hw = G < kPrefillWaves ? G : kPrefillWaves;
+  return (kPrefillWaves / hw) * 16 * kPrefillRowTiles;
+}
+
+int64_t prefill_work_items(int G, int S, int Hkv, int max_query_len) {
+  const int QB = prefill_rows_per_workgroup(G);
+  const int nhg = G > kPrefillWaves ? G / kPrefillWaves : 1;
+  return (int64_t)((max_query_len + QB - 1) / QB) * S * nhg * Hkv;
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int B, int G, int max_query_len,
                           hipStream_t stream) {
   const int QB = prefill_rows_per_workgroup(G);
-  const int nhg = G > 4 ? G / 4 : 1;
   PrefillArgs b = a;
   b.n_rank = (max_query_len + QB - 1) / QB;
-  b.n_work = (int64_t)b.n_rank * a.S * nhg * a.Hkv;
+  b.n_work = prefill_work_items(G, a.S, a.Hkv, max_query_len);
   b.per_xcd = (b.n_work + 7) / 8;
   const int64_t grid = 8 * b.per_xcd;
   if (b.n_work == 0) return hipSuccess;

@@ -13,6 +13,16 @@ namespace pa {
 #define PA_PREFILL_ROW_TILES 1
 #endif
 constexpr int kPrefillRowTiles = PA_PREFILL_ROW_TILES;
+// Waves per prefill workgroup (4 or 8): they share each staged key/value chunk.
+#ifndef PA_PREFILL_WAVES
+#define PA_PREFILL_WAVES 4
+#endif
+constexpr int kPrefillWaves = PA_PREFILL_WAVES;
+// Keys per pipeline step (32 or 64).
+#ifndef PA_PREFILL_CHUNK
+#define PA_PREFILL_CHUNK 32
+#endif
+constexpr int kPrefillChunk = PA_PREFILL_CHUNK;
 
 // Arguments of the prefill kernel.
 struct PrefillArgs {
@@ -32,6 +42,9 @@ struct PrefillArgs {
 
 // Query rows one prefill workgroup covers for a group of G query heads.
 int prefill_rows_per_workgroup(int G);
+
+// Work items (workgroups before padding to a multiple of 8) of one launch.
+int64_t prefill_work_items(int G, int S, int Hkv, int max_query_len);
 
 // Launches the prefill kernel over ceil(max_query_len / rows) row blocks per
 // sequence and head group.

@@ -519,6 +519,7 @@ def main():
     achieved = float(np.mean(kv_bytes_layer)) / (decode_avg_ms * 1e-3) / 1e9
 
     cow = time_copy_on_write(pa, extra) if "copy" in extra else None
+    stream = stream_ceiling(pa, steps_inputs) if args.workload in ("chat", "long_context") else None
 
     if args.copy_reference_mb > 0:
         copy_reference(args.copy_reference_mb)
@@ -570,7 +571,47 @@ def main():
     }
     if cow is not None:
         res["copy_on_write"] = cow
+    if stream is not None:
+        res["stream_read"] = {"GBs": stream["GBs"], "workgroups": stream["workgroups"],
+                              "decode_vs_stream": round(achieved / stream["GBs"], 4),
+                              "what": "pa_stream_read: one linear pass over this run's K/V pools "
+                                      "(non-temporal 16-byte loads), best of 3 launch shapes"}
     print(json.dumps(res), flush=True)
+
+
+def stream_ceiling(pa, steps_inputs):
+    """Practical read ceiling on this GPU in this run: pa_stream_read over the
+    workload's own pools, rotated so that no pass is served by the caches."""
+    import torch
+    bufs = []
+    for ly in steps_inputs[0]:
+        for t in (ly["kp"], ly["vp"]):
+            if t.numel() * t.element_size() >= (512 << 20):
+                bufs.append(t)
+        if len(bufs) >= 4:
+            break
+    if len(bufs) < 2:
+        return None
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    best = None
+    for wg in (2048, 4096, 8192):
+        for b in bufs:
+            pa.pa_stream_read(b, sink, wg)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 2 * len(bufs)
+        nbytes = 0
+        e0.record()
+        for r in range(reps):
+            b = bufs[r % len(bufs)]
+            pa.pa_stream_read(b, sink, wg)
+            nbytes += b.numel() * b.element_size()
+        e1.record()
+        torch.cuda.synchronize()
+        gbs = nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        if best is None or gbs > best["GBs"]:
+            best = {"GBs": round(gbs, 1), "workgroups": wg}
+    return best
 
 
 def cpu_baseline(layers, n_sample, kv_bytes_step, n_layers):

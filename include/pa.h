@@ -272,6 +272,19 @@ pa_status pa_prefill(void* out, const void* query, const void* k_pool, const voi
                      const int32_t* query_start, int S, int T, int Hq, int Hkv, int D, int B,
                      int NB, int MB, int max_query_len, float scale, hipStream_t stream);
 
+/*
+ * pa_stream_read — measurement utility, not part of the attention path: one
+ * linear read of `bytes` bytes of device memory with 16-byte non-temporal
+ * loads by `workgroups` workgroups of 256 threads. Nothing is written in
+ * practice; `sink` (device, 4 bytes) receives a value only in the unlikely
+ * case that the folded data equal a fixed constant, which keeps the reads
+ * from being optimised away. The benchmark times it as the practical read
+ * ceiling of the GPU it runs on. bytes must be a multiple of 16 (0 is a
+ * no-op); buffer 16-byte aligned; workgroups in [1, 2^20].
+ */
+pa_status pa_stream_read(const void* buffer, size_t bytes, void* sink, int workgroups,
+                         hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * Host block manager ([L], "How PagedAttention works", steps 1-3 and 5;
  * "Memory sharing across requests"; "Practice: try it yourself").

@@ -49,6 +49,8 @@ _lib.pa_decode.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _
 _lib.pa_prefill.restype = _i
 _lib.pa_prefill.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _i,
                             ctypes.c_float, _p]
+_lib.pa_stream_read.restype = _i
+_lib.pa_stream_read.argtypes = [_p, ctypes.c_size_t, _p, _i, _p]
 _lib.pa_bm_create.restype = _i
 _lib.pa_bm_create.argtypes = [_i, _i, _i, ctypes.POINTER(_p)]
 _lib.pa_bm_destroy.restype = None
@@ -189,6 +191,13 @@ def pa_prefill(query, k_pool, v_pool, block_tables, context_lens, query_start,
     return out
 
 
+def pa_stream_read(buffer, sink, workgroups: int = 4096, nbytes: int = None, stream=None):
+    """Read-bandwidth probe: one linear pass over a device tensor (measurement utility)."""
+    n = buffer.numel() * buffer.element_size() if nbytes is None else int(nbytes)
+    _check("pa_stream_read", _lib.pa_stream_read(_ptr(buffer), n - n % 16, _ptr(sink),
+                                                 int(workgroups), _stream(stream)))
+
+
 # ---------------------------------------------------------------------------
 # Host block manager (host numpy arrays; see the pa_bm_* calls in include/pa.h)
 # ---------------------------------------------------------------------------
@@ -282,4 +291,4 @@ class BlockManager:
 
 __all__ = ["PaError", "lib", "LIB_PATH", "pa_version", "pa_slot_mapping", "pa_write_kv",
            "pa_copy_blocks", "pa_decode_partition_size", "pa_decode_workspace_bytes",
-           "pa_decode", "pa_prefill", "pa_swap_blocks", "BlockManager"]
+           "pa_decode", "pa_prefill", "pa_swap_blocks", "pa_stream_read", "BlockManager"]

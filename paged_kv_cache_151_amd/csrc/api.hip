@@ -11,6 +11,11 @@
 #include "prefill_internal.h"
 
 namespace pa {
+hipError_t launch_stream_read(const void* buf, size_t bytes, void* sink, int workgroups,
+                              hipStream_t stream);
+}  // namespace pa
+
+namespace pa {
 
 namespace {
 thread_local char g_err[512] = "";
@@ -347,6 +352,19 @@ pa_status pa_prefill(void* out, const void* query, const void* k_pool, const voi
   a.B = B;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   return hip_status(pa::launch_prefill(a, B, G, max_query_len, stream), "pa_prefill launch");
+}
+
+pa_status pa_stream_read(const void* buffer, size_t bytes, void* sink, int workgroups,
+                         hipStream_t stream) {
+  if (workgroups <= 0 || workgroups > (1 << 20))
+    return fail(PA_ERR_SHAPE, "pa_stream_read: workgroups=%d outside [1, 2^20]", workgroups);
+  if (bytes % 16) return fail(PA_ERR_SHAPE, "pa_stream_read: bytes=%zu not a multiple of 16", bytes);
+  if (bytes == 0) return ok();
+  if (!buffer || !sink) return fail(PA_ERR_NULL, "pa_stream_read: null pointer argument");
+  if (!aligned(buffer, 16) || !aligned(sink, 4))
+    return fail(PA_ERR_ALIGN, "pa_stream_read: buffer must be 16-byte aligned, sink 4-byte aligned");
+  return hip_status(pa::launch_stream_read(buffer, bytes, sink, workgroups, stream),
+                    "pa_stream_read launch");
 }
 
 }  // extern "C"

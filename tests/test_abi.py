@@ -154,3 +154,13 @@ def test_prefill_host_validation(lib):
     assert prefill(lib, scale=-0.5) == PA_ERR_SHAPE
     assert prefill(lib, S=0) == PA_OK
     assert prefill(lib, maxq=0, out=None) == PA_OK
+
+
+def test_stream_read_host_validation(lib):
+    v = ctypes.c_void_p
+    lib.pa_stream_read.argtypes = [v, ctypes.c_size_t, v, ctypes.c_int, v]
+    assert lib.pa_stream_read(v(FAKE), 4096, None, 64, None) == PA_ERR_NULL
+    assert lib.pa_stream_read(v(FAKE), 4090, v(FAKE), 64, None) == PA_ERR_SHAPE
+    assert lib.pa_stream_read(v(FAKE), 4096, v(FAKE), 0, None) == PA_ERR_SHAPE
+    assert lib.pa_stream_read(v(FAKE + 8), 4096, v(FAKE), 64, None) == PA_ERR_ALIGN
+    assert lib.pa_stream_read(None, 0, None, 64, None) == PA_OK

@@ -565,7 +565,9 @@ def main():
                         and args.block_size == 16 and not args.contiguous else None),
             "kernel": "pa_decode call (partition + reduce kernels), average per layer",
             "avg_launch_us": round(decode_avg_ms * 1e3, 2),
+            "median_launch_us": round(float(np.median(decode_ms)) * 1e3, 2),
             "bytes_per_launch": int(np.mean(kv_bytes_layer)),
+            "other_bytes_per_launch": other_bytes(c0, P),
         },
         "cpu_baseline": cpu,
     }
@@ -577,6 +579,24 @@ def main():
                               "what": "pa_stream_read: one linear pass over this run's K/V pools "
                                       "(non-temporal 16-byte loads), best of 3 launch shapes"}
     print(json.dumps(res), flush=True)
+
+
+def other_bytes(c, P):
+    """Bytes one pa_decode call moves besides the counted K/V of valid tokens:
+    the rest of each sequence's last block (touched by nothing but counted by
+    a whole-block reader), query and output, table entries and lengths read,
+    and the partials written and read back across partitions."""
+    L = c.context_lens.astype(np.int64)
+    blocks = -(-L // c.B)
+    row = c.Hkv * c.D * 2 * 2                     # K and V bytes of one token, all KV heads
+    nparts = -(-L // P)
+    multi = nparts > 1
+    return {
+        "kv_unread_tail_of_last_blocks": int((blocks * c.B - L).sum() * row),
+        "query_and_output": int(2 * c.S * c.Hq * c.D * 2),
+        "tables_and_lengths": int(blocks.sum() * 4 + c.S * 4),
+        "workspace_partials_written_and_read": int(2 * (nparts[multi].sum()) * c.Hq * (c.D + 2) * 4),
+    }
 
 
 def stream_ceiling(pa, steps_inputs):

@@ -12,21 +12,22 @@
 // at position L - n + j and attends over positions 0 .. L - n + j.
 //
 // Work decomposition. A wave owns 16 * QT query rows of one query head. A
-// workgroup is 4 waves over one KV head g: 4 query heads of g with the same
-// rows when the group has at least 4 heads, otherwise 4 / G row tiles of each
-// of the G heads. Keys and values are taken 32 tokens at a time (a chunk: two
-// 16-token units, each a contiguous 4 KiB tile of the pool per KV head). The
+// workgroup is NW waves over one KV head g: NW query heads of g with the same
+// rows when the group has at least NW heads, otherwise NW / G row tiles of
+// each of the G heads. Keys and values are taken KC tokens at a time (a chunk
+// of KC / 16 units, each a contiguous 4 KiB tile of the pool per KV head). The
 // workgroup loads each chunk once, with loads in which consecutive lanes read
 // consecutive 16-byte pieces, two chunks ahead of the one being computed, and
-// stages it in LDS; the 4 waves read their matrix operands from there.
+// stages it in LDS; the waves read their matrix operands from there. Defaults
+// (QT = 1, NW = 4, KC = 32) are set in prefill_internal.h.
 //
 // Matrix products (v_mfma_f32_16x16x32_f16; lane l = 16 kq + m):
 //   scores   S^T = K Q^T per unit: the A operand is key token m, dims
 //            32c + 8kq .. +7 (one 16-byte LDS read), the B operand the query
 //            rows held in registers; lane l receives S for query row m and
 //            tokens 4kq + r of the unit.
-//   output   O^T = V^T P^T per chunk: the B operand is P exactly as the score
-//            product left it (query m; tokens 4kq + r of both units), the A
+//   output   O^T = V^T P^T per 32 keys: the B operand is P exactly as the score
+//            product left it (query m; tokens 4kq + r of two units), the A
 //            operand V for the same 8 tokens at dim 16n + m, gathered from the
 //            row-major V tile by two transposing LDS reads (ds_read_b64_tr_b16:
 //            in each 16-lane group, lane i receives 16-bit word i % 4 from the
@@ -36,7 +37,7 @@
 // the lanes of that row, so the only cross-lane steps are the two row-max
 // exchanges per chunk and the final sum.
 //
-// LDS layout: a chunk is 32 token rows of 256 bytes for K and for V, each row
+// LDS layout: a chunk is KC token rows of 256 bytes for K and for V, each row
 // split into 16 pieces of 16 bytes. Piece c of row r is stored at position
 // c ^ (r % 16) for K and c ^ 2 (r % 8) for V, which spreads the operand reads
 // of a wave over all banks.

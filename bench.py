@@ -96,6 +96,27 @@ def measured_traffic():
     return t.get("traffic_bytes_per_launch")
 
 
+PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pa_prefill_chat_s16_traffic.json")
+
+
+def prefill_measured_traffic():
+    """HBM bytes per prefill launch from the committed counter summary, or None
+    when the prefill kernel or its build flags changed after the counters were taken."""
+    import hashlib
+    try:
+        with open(PREFILL_TRAFFIC_FILE) as f:
+            t = json.load(f)
+        h = hashlib.sha256()
+        for rel in t["sources"]:
+            with open(os.path.join(ROOT, rel), "rb") as fh:
+                h.update(fh.read())
+    except (OSError, ValueError, KeyError):
+        return None
+    if t.get("prefill_source_sha256") != h.hexdigest():
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
 def copy_reference(mb):
     """One plain device-to-device copy of exactly mb MiB (torch copy_, a memory
     copy), after the timed region: the known-size reference that scales the
@@ -393,7 +414,8 @@ def bench_prefill(args):
                    "flops_per_step": int(flops)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_F16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
-                     "traffic": None, "kernel": "pa_prefill (one launch per step)",
+                     "traffic": prefill_measured_traffic() if args.prompts == 16 else None,
+                     "kernel": "pa_prefill (one launch per step)",
                      "avg_launch_us": round(launch_ms * 1e3, 2), "flops_per_launch": int(flops)},
         "cpu_baseline": cpu}), flush=True)
 

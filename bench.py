@@ -444,6 +444,11 @@ def cpu_baseline_prefill(c, flops_total):
 
 def main():
     args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the decode path has no cross-GPU step "
+              "(sequences and KV heads shard with no exchange); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
     if args.workload == "prefill":
         bench_prefill(args)
         return
@@ -453,11 +458,6 @@ def main():
     if args.workload == "swap":
         bench_swap(args)
         return
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the decode path has no cross-GPU step "
-              "(sequences and KV heads shard with no exchange); run with --gpus 1",
-              file=sys.stderr)
-        sys.exit(2)
 
     import torch
     import paged_kv_cache_151_amd as pa

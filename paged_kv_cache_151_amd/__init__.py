@@ -88,8 +88,27 @@ def _check(fn: str, status: int):
         raise PaError(fn, status)
 
 
-def _ptr(t):
-    return None if t is None else t.data_ptr()
+def _arg(t, name, dtype=None, device=True):
+    """Pointer of a contiguous tensor of the expected dtype (on the GPU unless
+    device=False), or None. The library reads raw memory, so a strided view or
+    a wrong element type is refused here rather than misread there."""
+    if t is None:
+        return None
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device and not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    return t.data_ptr()
+
+
+def _same_shape(a, b, names):
+    if a is not None and b is not None and tuple(a.shape) != tuple(b.shape):
+        raise ValueError(f"{names}: shapes {tuple(a.shape)} and {tuple(b.shape)} differ")
+
+
+_F16, _I32, _I64 = torch.float16, torch.int32, torch.int64
 
 
 def _stream(stream):
@@ -115,8 +134,10 @@ def pa_slot_mapping(block_tables, block_size: int, num_blocks: int, context_lens
     if out is None:
         out = torch.empty(T, dtype=torch.int64, device=block_tables.device)
     _check("pa_slot_mapping", _lib.pa_slot_mapping(
-        _ptr(out), _ptr(block_tables), _ptr(seq_ids), _ptr(positions), _ptr(context_lens),
-        T, S, MB, block_size, num_blocks, _stream(stream)))
+        _arg(out, "out", _I64), _arg(block_tables, "block_tables", _I32),
+        _arg(seq_ids, "seq_ids", _I32), _arg(positions, "positions", _I32),
+        _arg(context_lens, "context_lens", _I32), T, S, MB, block_size, num_blocks,
+        _stream(stream)))
     return out
 
 
@@ -124,8 +145,11 @@ def pa_write_kv(key, value, k_pool, v_pool, slot_mapping, stream=None):
     """Scatter key/value [T, Hkv, D] into the pools [NB, Hkv, B, D] at their slots."""
     T, Hkv, D = key.shape
     NB, _, B, _ = k_pool.shape
+    _same_shape(key, value, "key/value")
+    _same_shape(k_pool, v_pool, "k_pool/v_pool")
     _check("pa_write_kv", _lib.pa_write_kv(
-        _ptr(key), _ptr(value), _ptr(k_pool), _ptr(v_pool), _ptr(slot_mapping),
+        _arg(key, "key", _F16), _arg(value, "value", _F16), _arg(k_pool, "k_pool", _F16),
+        _arg(v_pool, "v_pool", _F16), _arg(slot_mapping, "slot_mapping", _I64),
         T, Hkv, D, B, NB, _stream(stream)))
 
 
@@ -133,8 +157,10 @@ def pa_copy_blocks(k_pool, v_pool, block_mapping, stream=None):
     """Copy whole blocks src -> dst for each row of block_mapping [n, 2] (int32)."""
     NB, Hkv, B, D = k_pool.shape
     n = block_mapping.shape[0]
+    _same_shape(k_pool, v_pool, "k_pool/v_pool")
     _check("pa_copy_blocks", _lib.pa_copy_blocks(
-        _ptr(k_pool), _ptr(v_pool), _ptr(block_mapping), n, Hkv, D, B, NB, _stream(stream)))
+        _arg(k_pool, "k_pool", _F16), _arg(v_pool, "v_pool", _F16),
+        _arg(block_mapping, "block_mapping", _I32), n, Hkv, D, B, NB, _stream(stream)))
 
 
 def pa_swap_blocks(dst_k_pool, dst_v_pool, src_k_pool, src_v_pool, block_mapping, stream=None):
@@ -144,9 +170,17 @@ def pa_swap_blocks(dst_k_pool, dst_v_pool, src_k_pool, src_v_pool, block_mapping
     NB_src, Hkv, B, D = src_k_pool.shape
     NB_dst = dst_k_pool.shape[0]
     n = block_mapping.shape[0]
+    _same_shape(dst_k_pool, dst_v_pool, "dst pools")
+    _same_shape(src_k_pool, src_v_pool, "src pools")
+    if tuple(dst_k_pool.shape[1:]) != tuple(src_k_pool.shape[1:]):
+        raise ValueError("pa_swap_blocks: source and destination blocks differ in shape")
     _check("pa_swap_blocks", _lib.pa_swap_blocks(
-        _ptr(dst_k_pool), _ptr(dst_v_pool), _ptr(src_k_pool), _ptr(src_v_pool),
-        _ptr(block_mapping), n, Hkv, D, B, NB_dst, NB_src, _stream(stream)))
+        _arg(dst_k_pool, "dst_k_pool", _F16, device=False),
+        _arg(dst_v_pool, "dst_v_pool", _F16, device=False),
+        _arg(src_k_pool, "src_k_pool", _F16, device=False),
+        _arg(src_v_pool, "src_v_pool", _F16, device=False),
+        _arg(block_mapping, "block_mapping", _I32, device=False), n, Hkv, D, B, NB_dst, NB_src,
+        _stream(stream)))
 
 
 def pa_decode_partition_size(S, Hq, Hkv, B, max_context_len, partition_size=0) -> int:
@@ -169,10 +203,14 @@ def pa_decode(query, k_pool, v_pool, block_tables, context_lens, max_context_len
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _same_shape(out, query, "out/query")
+    _same_shape(k_pool, v_pool, "k_pool/v_pool")
     _check("pa_decode", _lib.pa_decode(
-        _ptr(out), _ptr(query), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
-        _ptr(context_lens), S, Hq, Hkv, D, B, NB, MB, int(max_context_len), float(scale),
-        int(partition_size), _ptr(workspace), ws_bytes, _stream(stream)))
+        _arg(out, "out", _F16), _arg(query, "query", _F16), _arg(k_pool, "k_pool", _F16),
+        _arg(v_pool, "v_pool", _F16), _arg(block_tables, "block_tables", _I32),
+        _arg(context_lens, "context_lens", _I32), S, Hq, Hkv, D, B, NB, MB,
+        int(max_context_len), float(scale), int(partition_size), _arg(workspace, "workspace"),
+        ws_bytes, _stream(stream)))
     return out
 
 
@@ -184,18 +222,24 @@ def pa_prefill(query, k_pool, v_pool, block_tables, context_lens, query_start,
     S, MB = block_tables.shape
     if out is None:
         out = torch.empty_like(query)
+    _same_shape(out, query, "out/query")
+    _same_shape(k_pool, v_pool, "k_pool/v_pool")
+    if context_lens.shape[0] != S or query_start.shape[0] != S + 1:
+        raise ValueError("pa_prefill: context_lens needs S entries and query_start S + 1")
     _check("pa_prefill", _lib.pa_prefill(
-        _ptr(out), _ptr(query), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
-        _ptr(context_lens), _ptr(query_start), S, T, Hq, Hkv, D, B, NB, MB,
-        int(max_query_len), float(scale), _stream(stream)))
+        _arg(out, "out", _F16), _arg(query, "query", _F16), _arg(k_pool, "k_pool", _F16),
+        _arg(v_pool, "v_pool", _F16), _arg(block_tables, "block_tables", _I32),
+        _arg(context_lens, "context_lens", _I32), _arg(query_start, "query_start", _I32),
+        S, T, Hq, Hkv, D, B, NB, MB, int(max_query_len), float(scale), _stream(stream)))
     return out
 
 
 def pa_stream_read(buffer, sink, workgroups: int = 4096, nbytes: int = None, stream=None):
     """Read-bandwidth probe: one linear pass over a device tensor (measurement utility)."""
     n = buffer.numel() * buffer.element_size() if nbytes is None else int(nbytes)
-    _check("pa_stream_read", _lib.pa_stream_read(_ptr(buffer), n - n % 16, _ptr(sink),
-                                                 int(workgroups), _stream(stream)))
+    _check("pa_stream_read", _lib.pa_stream_read(_arg(buffer, "buffer"), n - n % 16,
+                                                 _arg(sink, "sink"), int(workgroups),
+                                                 _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

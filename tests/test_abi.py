@@ -164,3 +164,22 @@ def test_stream_read_host_validation(lib):
     assert lib.pa_stream_read(v(FAKE), 4096, v(FAKE), 0, None) == PA_ERR_SHAPE
     assert lib.pa_stream_read(v(FAKE + 8), 4096, v(FAKE), 64, None) == PA_ERR_ALIGN
     assert lib.pa_stream_read(None, 0, None, 64, None) == PA_OK
+
+
+def test_binding_refuses_tensors_it_would_misread():
+    # checked in the binding before any library call, so this runs without a GPU
+    import torch
+    import paged_kv_cache_151_amd as pa
+    key = torch.zeros(4, 2, 128, dtype=torch.float16)
+    pool = torch.zeros(8, 2, 16, 128, dtype=torch.float16)
+    slots = torch.zeros(4, dtype=torch.int64)
+    with pytest.raises(ValueError, match="device tensor"):
+        pa.pa_write_kv(key, key, pool, pool, slots)
+    with pytest.raises(TypeError, match="float16"):
+        pa.pa_write_kv(key.float(), key, pool, pool, slots)
+    with pytest.raises(ValueError, match="contiguous"):
+        pa.pa_write_kv(key.transpose(0, 1), key.transpose(0, 1), pool, pool, slots)
+    with pytest.raises(ValueError, match="differ"):
+        pa.pa_write_kv(key, key[:3], pool, pool, slots)
+    with pytest.raises(TypeError, match="int32"):   # an int64 block mapping would be misread
+        pa._arg(torch.zeros(2, 2, dtype=torch.int64), "block_mapping", torch.int32)

@@ -295,3 +295,12 @@ def test_contiguous_layout_one_block_per_sequence(pa):
     assert c.MB == 1
     for ps in (0, 256, 1008):
         check_case(pa, c, partition_size=ps)
+
+
+def test_very_long_context_65536_tokens(pa):
+    """One 65,536-token sequence (4,096 blocks of 16: 64 table windows per
+    1,024-token partition sweep, 64 partitions merged) next to a 1-token one."""
+    c = W.make_case("ctx65536", 2300, [65536, 1], Hq=4, Hkv=4, B=16)
+    say(c.name, f"NB={c.NB} MB={c.MB}")
+    for ps in (0, 4096):
+        check_case(pa, c, partition_size=ps)

@@ -52,9 +52,10 @@ def test_ragged_chunks_all_groups_and_block_sizes(pa, G, B):
     check(pa, c)
 
 
-@pytest.mark.parametrize("n", [127, 128, 129, 255, 257])
+@pytest.mark.parametrize("n", [63, 64, 65, 127, 128, 129, 255, 257])
 def test_prompt_lengths_around_workgroup_row_blocks(pa, n):
-    # one head: a workgroup covers 128 rows (4 waves of 32)
+    # one head: a workgroup covers 64 rows (4 waves of 16) in the default build,
+    # 128 with two row tiles per wave; these lengths straddle both edges
     c = W.make_prefill_case(f"prompt_{n}", 3100 + n, [n, 3], [0, 40], Hq=1, Hkv=1, B=16)
     check(pa, c)
 
@@ -185,3 +186,23 @@ def test_chat_prefill_full_size_sampled(pa):
             for h in range(c.Hq):
                 want[i, h] = oracle.attend(c.query[q0 + j, h], K[h, :p + 1], V[h, :p + 1], c.scale)
         assert_attention_close(got[[q0 + j for j in rows]], want, f"chat prefill seq {s}")
+
+
+def test_long_prompt_after_long_cached_prefix_sampled(pa):
+    """6,000 new tokens after 3,000 cached ones (282 blocks of 32, many LDS
+    chunks and table reads per row block), grouped heads 4/2; sampled rows
+    across the whole chunk against the oracle's attention."""
+    c = W.make_prefill_case("long_prompt", 3700, [6000], [3000], Hq=4, Hkv=2, B=32)
+    say(c.name, f"T={c.T} L={int(c.context_lens[0])} NB={c.NB}")
+    got = run(pa, c)
+    L, n = int(c.context_lens[0]), int(c.new_lens[0])
+    K = oracle.gather(c.k_pool, c.block_tables[0], L, c.B)
+    V = oracle.gather(c.v_pool, c.block_tables[0], L, c.B)
+    rows = [0, 1, 63, 64, 2047, 2048, 4095, 5000, n - 2, n - 1]
+    want = np.empty((len(rows), c.Hq, c.D))
+    for i, j in enumerate(rows):
+        p = L - n + j
+        for h in range(c.Hq):
+            g = h // (c.Hq // c.Hkv)
+            want[i, h] = oracle.attend(c.query[j, h], K[g, :p + 1], V[g, :p + 1], c.scale)
+    assert_attention_close(got[rows], want, c.name)

@@ -274,8 +274,9 @@ pa_status pa_prefill(void* out, const void* query, const void* k_pool, const voi
 
 /*
  * pa_stream_read — measurement utility, not part of the attention path: one
- * linear read of `bytes` bytes of device memory with 16-byte non-temporal
- * loads by `workgroups` workgroups of 256 threads. Nothing is written in
+ * linear read of `bytes` bytes of device memory by `workgroups` workgroups of
+ * 256 threads, each lane keeping 8 independent 16-byte loads in flight with
+ * the non-temporal and sc1 cache-policy bits (the fastest read form measured). Nothing is written in
  * practice; `sink` (device, 4 bytes) receives a value only in the unlikely
  * case that the folded data equal a fixed constant, which keeps the reads
  * from being optimised away. The benchmark times it as the practical read

@@ -13,6 +13,7 @@
 // pa_copy_blocks.
 #include <cstdint>
 #include <deque>
+#include <new>
 #include <set>
 #include <vector>
 
@@ -61,6 +62,19 @@ namespace {
 using pa::fail;
 using pa::ok;
 
+// Runs the body of an entry point that may allocate host memory: no C++
+// exception crosses the C boundary; running out of memory becomes a status.
+template <class F>
+pa_status guarded(const char* fn, F&& body) {
+  try {
+    return body();
+  } catch (const std::bad_alloc&) {
+    return fail(PA_ERR_EXHAUSTED, "%s: out of host memory", fn);
+  } catch (...) {
+    return fail(PA_ERR_STATE, "%s: internal error", fn);
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -72,41 +86,53 @@ pa_status pa_bm_create(int num_blocks, int block_size, int max_blocks_per_seq,
   if (num_blocks <= 0 || block_size <= 0 || max_blocks_per_seq < 0)
     return fail(PA_ERR_SHAPE, "pa_bm_create: num_blocks=%d block_size=%d max_blocks_per_seq=%d",
                 num_blocks, block_size, max_blocks_per_seq);
-  pa_block_manager* bm = new pa_block_manager();
-  bm->num_blocks = num_blocks;
-  bm->block_size = block_size;
-  bm->max_blocks_per_seq = max_blocks_per_seq > 0 ? max_blocks_per_seq : num_blocks;
-  bm->refs.assign(num_blocks, 0);
-  bm->fill.assign(num_blocks, 0);
-  for (int b = 0; b < num_blocks; ++b) bm->free_list.push_back(b);
-  *out = bm;
-  return ok();
+  return guarded("pa_bm_create", [&]() {
+    pa_block_manager* bm = new pa_block_manager();
+    try {
+      bm->num_blocks = num_blocks;
+      bm->block_size = block_size;
+      bm->max_blocks_per_seq = max_blocks_per_seq > 0 ? max_blocks_per_seq : num_blocks;
+      bm->refs.assign(num_blocks, 0);
+      bm->fill.assign(num_blocks, 0);
+      for (int b = 0; b < num_blocks; ++b) bm->free_list.push_back(b);
+    } catch (...) {
+      delete bm;
+      throw;
+    }
+    *out = bm;
+    return ok();
+  });
 }
 
 void pa_bm_destroy(pa_block_manager* bm) { delete bm; }
 
 pa_status pa_bm_add_sequence(pa_block_manager* bm, int* seq_id) {
   if (!bm || !seq_id) return fail(PA_ERR_NULL, "pa_bm_add_sequence: null argument");
-  const int id = bm->new_id();
-  bm->seqs[id] = pa_block_manager::Seq();
-  bm->seqs[id].live = true;
-  *seq_id = id;
-  return ok();
+  return guarded("pa_bm_add_sequence", [&]() {
+    const int id = bm->new_id();
+    bm->seqs[id] = pa_block_manager::Seq();
+    bm->seqs[id].live = true;
+    *seq_id = id;
+    return ok();
+  });
 }
 
 pa_status pa_bm_fork(pa_block_manager* bm, int parent, int* child) {
   if (!bm || !child) return fail(PA_ERR_NULL, "pa_bm_fork: null argument");
   if (!bm->valid(parent)) return fail(PA_ERR_STATE, "pa_bm_fork: no live sequence %d", parent);
-  const int id = bm->new_id();
-  pa_block_manager::Seq& p = bm->seqs[parent];   // new_id may grow seqs: take the reference after
-  for (int32_t b : p.table) bm->refs[b] += 1;
-  pa_block_manager::Seq c;
-  c.live = true;
-  c.table = p.table;
-  c.tokens = p.tokens;
-  bm->seqs[id] = c;
-  *child = id;
-  return ok();
+  return guarded("pa_bm_fork", [&]() {
+    // the child is built completely before any reference count changes, so a
+    // failed allocation leaves the manager as it was
+    pa_block_manager::Seq c;
+    c.live = true;
+    c.table = bm->seqs[parent].table;
+    c.tokens = bm->seqs[parent].tokens;
+    const int id = bm->new_id();
+    for (int32_t b : c.table) bm->refs[b] += 1;
+    bm->seqs[id] = std::move(c);
+    *child = id;
+    return ok();
+  });
 }
 
 pa_status pa_bm_append_tokens(pa_block_manager* bm, const int* seq_ids, int n, int64_t* slots,
@@ -120,59 +146,64 @@ pa_status pa_bm_append_tokens(pa_block_manager* bm, const int* seq_ids, int n, i
   if (max_copies > 0 && !copy_pairs)
     return fail(PA_ERR_NULL, "pa_bm_append_tokens: copy_pairs is NULL");
   const int B = bm->block_size;
-  for (int i = 0; i < n; ++i) {
-    const int id = seq_ids[i];
-    if (!bm->valid(id)) return fail(PA_ERR_STATE, "pa_bm_append_tokens: no live sequence %d", id);
-    pa_block_manager::Seq& q = bm->seqs[id];
-    const int32_t last = q.table.empty() ? -1 : q.table.back();
-    if (last < 0 || bm->fill[last] == B) {
-      // no block yet, or the last one is full: take one more
-      if ((int)q.table.size() >= bm->max_blocks_per_seq)
-        return fail(PA_ERR_STATE, "pa_bm_append_tokens: sequence %d has %d blocks (maximum)", id,
-                    (int)q.table.size());
-      if (bm->free_list.empty())
-        return fail(PA_ERR_EXHAUSTED, "pa_bm_append_tokens: no free block (token %d)", i);
-      q.table.push_back(bm->take());
-    } else if (bm->refs[last] > 1) {
-      // the last block is shared: copy it before writing
-      if (bm->free_list.empty())
-        return fail(PA_ERR_EXHAUSTED, "pa_bm_append_tokens: no free block for a copy (token %d)", i);
-      if (*n_copies >= max_copies)
-        return fail(PA_ERR_SHAPE, "pa_bm_append_tokens: more than %d copies", max_copies);
-      const int32_t fresh = bm->take();
-      bm->fill[fresh] = bm->fill[last];
-      bm->refs[last] -= 1;
-      copy_pairs[2 * *n_copies] = last;
-      copy_pairs[2 * *n_copies + 1] = fresh;
-      *n_copies += 1;
-      q.table.back() = fresh;
+  return guarded("pa_bm_append_tokens", [&]() {
+    for (int i = 0; i < n; ++i) {
+      const int id = seq_ids[i];
+      if (!bm->valid(id)) return fail(PA_ERR_STATE, "pa_bm_append_tokens: no live sequence %d", id);
+      pa_block_manager::Seq& q = bm->seqs[id];
+      const int32_t last = q.table.empty() ? -1 : q.table.back();
+      if (last < 0 || bm->fill[last] == B) {
+        // no block yet, or the last one is full: take one more
+        if ((int)q.table.size() >= bm->max_blocks_per_seq)
+          return fail(PA_ERR_STATE, "pa_bm_append_tokens: sequence %d has %d blocks (maximum)", id,
+                      (int)q.table.size());
+        if (bm->free_list.empty())
+          return fail(PA_ERR_EXHAUSTED, "pa_bm_append_tokens: no free block (token %d)", i);
+        q.table.reserve(q.table.size() + 1);   // may throw: before the block leaves the list
+        q.table.push_back(bm->take());
+      } else if (bm->refs[last] > 1) {
+        // the last block is shared: copy it before writing
+        if (bm->free_list.empty())
+          return fail(PA_ERR_EXHAUSTED, "pa_bm_append_tokens: no free block for a copy (token %d)", i);
+        if (*n_copies >= max_copies)
+          return fail(PA_ERR_SHAPE, "pa_bm_append_tokens: more than %d copies", max_copies);
+        const int32_t fresh = bm->take();
+        bm->fill[fresh] = bm->fill[last];
+        bm->refs[last] -= 1;
+        copy_pairs[2 * *n_copies] = last;
+        copy_pairs[2 * *n_copies + 1] = fresh;
+        *n_copies += 1;
+        q.table.back() = fresh;
+      }
+      const int32_t blk = q.table.back();
+      const int32_t off = bm->fill[blk];
+      bm->fill[blk] = off + 1;
+      q.tokens += 1;
+      slots[i] = (int64_t)blk * B + off;
+      *n_applied = i + 1;
     }
-    const int32_t blk = q.table.back();
-    const int32_t off = bm->fill[blk];
-    bm->fill[blk] = off + 1;
-    q.tokens += 1;
-    slots[i] = (int64_t)blk * B + off;
-    *n_applied = i + 1;
-  }
-  return ok();
+    return ok();
+  });
 }
 
 pa_status pa_bm_release(pa_block_manager* bm, int seq_id, int* n_freed) {
   if (!bm) return fail(PA_ERR_NULL, "pa_bm_release: null manager");
   if (!bm->valid(seq_id)) return fail(PA_ERR_STATE, "pa_bm_release: no live sequence %d", seq_id);
-  pa_block_manager::Seq& q = bm->seqs[seq_id];
-  int freed = 0;
-  for (int32_t b : q.table) {
-    if (--bm->refs[b] == 0) {
-      bm->fill[b] = 0;
-      bm->free_list.push_back(b);
-      ++freed;
+  return guarded("pa_bm_release", [&]() {
+    bm->free_ids.insert(seq_id);   // first: a failed insert leaves the sequence as it was
+    pa_block_manager::Seq& q = bm->seqs[seq_id];
+    int freed = 0;
+    for (int32_t b : q.table) {
+      if (--bm->refs[b] == 0) {
+        bm->fill[b] = 0;
+        bm->free_list.push_back(b);
+        ++freed;
+      }
     }
-  }
-  q = pa_block_manager::Seq();
-  bm->free_ids.insert(seq_id);
-  if (n_freed) *n_freed = freed;
-  return ok();
+    q = pa_block_manager::Seq();
+    if (n_freed) *n_freed = freed;
+    return ok();
+  });
 }
 
 pa_status pa_bm_get_table(const pa_block_manager* bm, int seq_id, int32_t* row, int max_len,

@@ -52,6 +52,25 @@ pa_status hip_status(hipError_t e, const char* what) {
 
 int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
+// A dispatch packet holds the grid as a 32-bit count of work-items per
+// dimension: `workgroups` of `threads` each must stay within it.
+constexpr int64_t kMaxWorkItems = 0xFFFFFFFFLL;
+bool dispatch_fits(int64_t workgroups, int threads) {
+  return workgroups >= 0 && workgroups <= kMaxWorkItems / threads;
+}
+
+// 16-byte chunks in one block of one pool (Hkv * B * D fp16), or -1 when that
+// exceeds what one copy launch covers: the copy kernel gives each workgroup of
+// 256 threads a segment of 2048 chunks, so at most 2^24 - 1 segments (just
+// under 512 GiB per block).
+int64_t block_chunks(int Hkv, int B, int D) {
+  const int64_t max_chunks = (kMaxWorkItems / 256) * 2048;
+  const int64_t hb = (int64_t)Hkv * B;
+  const int64_t per = D / 8;
+  if (hb > max_chunks / per) return -1;
+  return hb * per;
+}
+
 }  // namespace
 
 extern "C" {
@@ -106,8 +125,10 @@ pa_status pa_write_kv(const void* key, const void* value, void* k_pool, void* v_
   if (Hkv <= 0 || D <= 0 || B <= 0 || NB <= 0)
     return fail(PA_ERR_SHAPE, "pa_write_kv: Hkv=%d D=%d B=%d NB=%d must be > 0", Hkv, D, B, NB);
   if (D % 8) return fail(PA_ERR_UNSUPPORTED, "pa_write_kv: D=%d must be a multiple of 8", D);
-  if ((int64_t)T * Hkv * (D / 8) >= ((int64_t)1 << 40))
-    return fail(PA_ERR_SHAPE, "pa_write_kv: too many tokens");
+  // one work-item per 16-byte chunk of every token's row: T * Hkv * D / 8
+  if (T > 0 && (int64_t)Hkv * (D / 8) > (kMaxWorkItems - 255) / T)
+    return fail(PA_ERR_SHAPE, "pa_write_kv: T=%d tokens of Hkv=%d x D=%d exceed one launch", T,
+                Hkv, D);
   if (T == 0) return ok();
   if (!key || !value || !k_pool || !v_pool || !slot_mapping)
     return fail(PA_ERR_NULL, "pa_write_kv: null pointer argument");
@@ -126,6 +147,8 @@ pa_status pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_mappin
     return fail(PA_ERR_SHAPE, "pa_copy_blocks: Hkv=%d D=%d B=%d NB=%d must be > 0", Hkv, D, B,
                 NB);
   if (D % 8) return fail(PA_ERR_UNSUPPORTED, "pa_copy_blocks: D=%d must be a multiple of 8", D);
+  if (block_chunks(Hkv, B, D) < 0)
+    return fail(PA_ERR_SHAPE, "pa_copy_blocks: block of Hkv=%d x B=%d x D=%d too large", Hkv, B, D);
   if (n == 0) return ok();
   if (!k_pool || !v_pool || !block_mapping)
     return fail(PA_ERR_NULL, "pa_copy_blocks: null pointer argument");
@@ -173,6 +196,8 @@ pa_status pa_swap_blocks(void* dst_k_pool, void* dst_v_pool, const void* src_k_p
     return fail(PA_ERR_SHAPE, "pa_swap_blocks: Hkv=%d D=%d B=%d NB_dst=%d NB_src=%d must be > 0",
                 Hkv, D, B, NB_dst, NB_src);
   if (D % 8) return fail(PA_ERR_UNSUPPORTED, "pa_swap_blocks: D=%d must be a multiple of 8", D);
+  if (block_chunks(Hkv, B, D) < 0)
+    return fail(PA_ERR_SHAPE, "pa_swap_blocks: block of Hkv=%d x B=%d x D=%d too large", Hkv, B, D);
   if (n == 0) return ok();
   if (!dst_k_pool || !dst_v_pool || !src_k_pool || !src_v_pool || !block_mapping)
     return fail(PA_ERR_NULL, "pa_swap_blocks: null pointer argument");
@@ -255,6 +280,19 @@ pa_status pa_decode(void* out, const void* query, const void* k_pool, const void
   if (G != 1 && G != 2 && G != 4 && G != 8)
     return fail(PA_ERR_UNSUPPORTED, "pa_decode: Hq/Hkv=%d (supported: 1, 2, 4, 8)", G);
   if (!std::isfinite(scale)) return fail(PA_ERR_SHAPE, "pa_decode: scale is not finite");
+  const int P = pa_decode_partition_size(S, Hq, Hkv, B, max_context_len, partition_size);
+  const int Pmax = max_context_len > 0 ? ceil_div(max_context_len, P) : 1;
+  if (Pmax > pa::kMaxPartitions)
+    return fail(PA_ERR_SHAPE, "pa_decode: %d partitions exceed %d", Pmax, pa::kMaxPartitions);
+  // partition kernel: one workgroup per (partition, sequence, KV head) of
+  // max(waves for the group size, heads / heads per wave) waves; reduce
+  // kernel: one wave per (sequence, query head)
+  const int hpw = G < pa::kDecodeHeadsPerWave ? G : pa::kDecodeHeadsPerWave;
+  const int waves = pa::decode_waves(G) > G / hpw ? pa::decode_waves(G) : G / hpw;
+  const int64_t wgs = (int64_t)Pmax * S * Hkv;
+  if (!dispatch_fits(wgs, waves * 64) || !dispatch_fits((int64_t)S * Hq, 64))
+    return fail(PA_ERR_SHAPE, "pa_decode: launch too large (S=%d Hq=%d, %lld workgroups)", S, Hq,
+                (long long)wgs);
   if (S == 0) return ok();
   if (!out || !query || !k_pool || !v_pool || !block_tables || !context_lens)
     return fail(PA_ERR_NULL, "pa_decode: null pointer argument");
@@ -263,13 +301,6 @@ pa_status pa_decode(void* out, const void* query, const void* k_pool, const void
   if (!aligned(block_tables, 4) || !aligned(context_lens, 4))
     return fail(PA_ERR_ALIGN, "pa_decode: block_tables/context_lens misaligned");
 
-  const int P = pa_decode_partition_size(S, Hq, Hkv, B, max_context_len, partition_size);
-  const int Pmax = max_context_len > 0 ? ceil_div(max_context_len, P) : 1;
-  if (Pmax > pa::kMaxPartitions)
-    return fail(PA_ERR_SHAPE, "pa_decode: %d partitions exceed %d", Pmax, pa::kMaxPartitions);
-  const int64_t wgs = (int64_t)Pmax * S * Hkv;
-  if (wgs * 512 >= ((int64_t)1 << 32) || (int64_t)S * Hq >= ((int64_t)1 << 31))
-    return fail(PA_ERR_SHAPE, "pa_decode: launch too large (%lld workgroups)", (long long)wgs);
   const size_t need = pa_decode_workspace_bytes(S, Hq, Hkv, D, B, max_context_len, P);
   if (need > 0) {
     if (!workspace || workspace_bytes < need)
@@ -322,6 +353,10 @@ pa_status pa_prefill(void* out, const void* query, const void* k_pool, const voi
     return fail(PA_ERR_UNSUPPORTED, "pa_prefill: Hq/Hkv=%d (supported: 1, 2, 4, 8)", G);
   if (!std::isfinite(scale) || scale < 0.f)
     return fail(PA_ERR_SHAPE, "pa_prefill: scale must be finite and >= 0");
+  // workgroups of kPrefillWaves waves, padded to a multiple of 8 at launch
+  const int64_t grid = pa::prefill_work_items(G, S, Hkv, max_query_len);
+  if (!dispatch_fits(grid + 7, pa::kPrefillWaves * 64))
+    return fail(PA_ERR_SHAPE, "pa_prefill: launch too large (%lld workgroups)", (long long)grid);
   if (S == 0 || max_query_len == 0) return ok();
   if (!out || !query || !k_pool || !v_pool || !block_tables || !context_lens || !query_start)
     return fail(PA_ERR_NULL, "pa_prefill: null pointer argument");
@@ -329,11 +364,6 @@ pa_status pa_prefill(void* out, const void* query, const void* k_pool, const voi
     return fail(PA_ERR_ALIGN, "pa_prefill: out/query/pools must be 16-byte aligned");
   if (!aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(query_start, 4))
     return fail(PA_ERR_ALIGN, "pa_prefill: index arrays misaligned");
-  if ((int64_t)T * Hq * D >= ((int64_t)1 << 62))
-    return fail(PA_ERR_SHAPE, "pa_prefill: T too large");
-  const int64_t grid = pa::prefill_work_items(G, S, Hkv, max_query_len);
-  if (grid >= ((int64_t)1 << 31) - 8)   // padded to a multiple of 8 at launch
-    return fail(PA_ERR_SHAPE, "pa_prefill: launch too large (%lld workgroups)", (long long)grid);
 
   pa::PrefillArgs a;
   a.out = static_cast<_Float16*>(out);

@@ -156,6 +156,26 @@ def test_prefill_host_validation(lib):
     assert prefill(lib, maxq=0, out=None) == PA_OK
 
 
+
+def test_launch_size_limits(lib):
+    """Shapes whose launch would not fit a dispatch packet (a 32-bit count of
+    work-items) are refused as shape errors before any pointer is looked at;
+    the largest shapes that fit get as far as the null-pointer check."""
+    v = ctypes.c_void_p
+    # decode: one workgroup of 2 waves per (sequence, KV head) at group size 1
+    assert decode(lib, out=None, S=2**23 - 1, Hq=4, Hkv=4, MB=3, maxL=48) == PA_ERR_NULL
+    assert decode(lib, out=None, S=2**23, Hq=4, Hkv=4, MB=3, maxL=48) == PA_ERR_SHAPE
+    # prefill, group size 1: 64 rows and 256 threads per workgroup, grid padded to 8
+    assert prefill(lib, out=None, S=2**20, T=64, Hq=15, Hkv=15, maxq=64) == PA_ERR_NULL
+    assert prefill(lib, out=None, S=2**20, T=64, Hq=16, Hkv=16, maxq=64) == PA_ERR_SHAPE
+    # write_kv: one work-item per 16-byte chunk, T * Hkv * D / 8 of them
+    assert lib.pa_write_kv(None, None, None, None, None, 2**26 - 4, 4, 128, 16, 8, None) == PA_ERR_NULL
+    assert lib.pa_write_kv(None, None, None, None, None, 2**26 - 3, 4, 128, 16, 8, None) == PA_ERR_SHAPE
+    # copy and swap: one block of Hkv * B * D fp16 must fit one launch
+    assert lib.pa_copy_blocks(None, None, None, 1, 2**14, 2**14, 128, 8, None) == PA_ERR_NULL
+    assert lib.pa_copy_blocks(None, None, None, 0, 2**16, 2**16, 128, 8, None) == PA_ERR_SHAPE
+    assert lib.pa_swap_blocks(None, None, None, None, None, 0, 2**16, 2**16, 128, 8, 8, None) == PA_ERR_SHAPE
+
 def test_stream_read_host_validation(lib):
     v = ctypes.c_void_p
     lib.pa_stream_read.argtypes = [v, ctypes.c_size_t, v, ctypes.c_int, v]

@@ -16,10 +16,18 @@
 // rows when the group has at least NW heads, otherwise NW / G row tiles of
 // each of the G heads. Keys and values are taken KC tokens at a time (a chunk
 // of KC / 16 units, each a contiguous 4 KiB tile of the pool per KV head). The
-// workgroup loads each chunk once, with loads in which consecutive lanes read
-// consecutive 16-byte pieces, two chunks ahead of the one being computed, and
-// stages it in LDS; the waves read their matrix operands from there. Defaults
-// (QT = 1, NW = 4, KC = 32) are set in prefill_internal.h.
+// workgroup loads each chunk once, two chunks ahead of the one being computed,
+// with buffer loads that write straight into LDS (no staging registers, no
+// separate store step), into one of three LDS stages; the waves read their
+// matrix operands from there. Defaults (QT = 1, NW = 4, KC = 32) are set in
+// prefill_internal.h.
+//
+// Instruction budget. A wave issues at most one instruction per turn on its
+// SIMD, so every scalar or vector instruction around the 16 matrix products of
+// a 32-key step costs issue slots the products need. The loads are laid out so
+// that the pool (K or V) and the unit of every load instruction are known at
+// compile time and each lane's offset into a unit never changes; only the
+// unit's base address and valid length are computed per chunk.
 //
 // Matrix products (v_mfma_f32_16x16x32_f16; lane l = 16 kq + m):
 //   scores   S^T = K Q^T per unit: the A operand is key token m, dims
@@ -66,9 +74,6 @@ constexpr int kUnitTok = 16;
 constexpr int kRowBytes = kHeadDim * 2;    // one token row of one KV head
 constexpr int kRsrcWord3 = 0x00020000;     // raw buffer, gfx9 family
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const _Float16* base, int nbytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16*>(base), 0, nbytes, kRsrcWord3);
-}
 
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
@@ -85,15 +90,23 @@ struct Flag {
   static constexpr bool value = V;
 };
 
-// A chunk of KC tokens is 32 KC pieces of 16 bytes: pieces x < 16 KC are K,
-// the rest V; within each, x / 256 is the 16-token unit, (x / 16) % 16 the
-// token row of the unit and x % 16 the piece of the row. Thread t of a
-// workgroup of NTH threads carries pieces t, t + NTH, ...: consecutive lanes
-// read consecutive 16-byte pieces.
-template <int NP>
-struct Stage {
-  u32x4 p[NP];
-};
+// 16-byte buffer load of each lane into LDS: lane i's bytes land at dst + 16 i
+// (lanes past the resource's range write zeros); the second form marks the
+// load non-temporal. Kept out of the kernel template: the host pass must not
+// see the LDS pointer argument inside it.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, lds_u8* dst, unsigned voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff,
+                                           0, 0, 0);
+}
+__device__ __forceinline__ void load_lds16_nt(__amdgpu_buffer_rsrc_t r, lds_u8* dst,
+                                              unsigned voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff,
+                                           0, 0, 2);
+}
+
+// vmcnt(n): wait until at most n vector memory operations of this wave are
+// outstanding (gfx9 encoding; lgkmcnt and expcnt left at their maximum).
+#define PA_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0F70)
 
 template <int BT, int G, int QT, int NW, int KC, bool NT>
 __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
@@ -110,10 +123,23 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
   constexpr int NP = NPC / NTH;            // pieces per thread and chunk
   constexpr int kStageBytes = KC * kRowBytes;
   static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
-  static_assert(NW == 4 || NW == 8, "waves per workgroup");
+  static_assert(NW == 4, "the load layout assumes four waves");
   static_assert(KC == 32 || KC == 64, "keys per step");
-  __shared__ __attribute__((aligned(16))) unsigned char s_k[2][kStageBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char s_v[2][kStageBytes];
+  static_assert(NP * NTH == NPC, "whole load instructions per chunk");
+  // One array per stage, always indexed at compile time: the compiler tracks
+  // loads into LDS per array and waits only where a read meets its stage.
+  __shared__ __attribute__((aligned(16))) unsigned char s_k0[kStageBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char s_v0[kStageBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char s_k1[kStageBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char s_v1[kStageBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char s_k2[kStageBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char s_v2[kStageBytes];
+  auto kst = [&](int st) -> lds_u8* {
+    return st == 0 ? (lds_u8*)s_k0 : st == 1 ? (lds_u8*)s_k1 : (lds_u8*)s_k2;
+  };
+  auto vst = [&](int st) -> lds_u8* {
+    return st == 0 ? (lds_u8*)s_v0 : st == 1 ? (lds_u8*)s_v1 : (lds_u8*)s_v2;
+  };
   const int B = BT > 0 ? BT : a.B;
   const int UPB = B / kUnitTok;
 
@@ -158,7 +184,6 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
   kend_wg = kend_wg > L ? L : kend_wg;
   kend_wg = kend_wg < 0 ? 0 : kend_wg;
   const int nchunk_wg = (kend_wg + KC - 1) / KC;
-  const int nblk = (kend_wg + B - 1) / B;
 
   // this wave's rows and the chunks it computes
   const int hq = g * G + hg * HW + wave % HW;
@@ -205,50 +230,48 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
   typedef const __attribute__((address_space(4))) int32_t* const_i32;
   const const_i32 trow = (const_i32)(a.tables + (int64_t)s * a.MB);
   // physical block of unit U, or -1 when U holds no key the workgroup needs
-  auto table_entry = [&](int U) -> int {
-    const int bi = U / UPB;
-    return U * kUnitTok < kend_wg && bi < nblk ? trow[bi] : -1;
-  };
+  // (U * 16 < kend_wg also puts its block index below nblk <= MB)
+  auto table_entry = [&](int U) -> int { return U * kUnitTok < kend_wg ? trow[U / UPB] : -1; };
 
-  auto fetch = [&](Stage<NP>& st, int c, const int (&ph)[NU]) {
+  // Loads into LDS. Instruction i of wave w carries row group i * NW + w of
+  // the chunk (4 token rows); with four waves its pool and its unit depend on
+  // i alone, and its rows in the unit are 4w .. 4w + 3 for every instruction.
+  // Lane 16 kq + m writes LDS piece slot m of row r = 4w + kq, so it loads the
+  // global piece that the swizzle places there (m ^ swizzle(r)): a fixed
+  // offset into the unit for the whole kernel. Lanes past a unit's valid
+  // tokens fall outside the resource's range and write zeros.
+  const int dr = 4 * wave + kq;
+  const unsigned voff_k = (unsigned)(dr * kRowBytes + ((m ^ (dr & 15)) << 4));
+  const unsigned voff_v = (unsigned)(dr * kRowBytes + ((m ^ ((dr & 7) << 1)) << 4));
+  const uint32_t blk_bytes = (uint32_t)a.Hkv * (uint32_t)B * kRowBytes;   // one block, all heads
+  const unsigned char* kg = (const unsigned char*)a.k_pool + (size_t)g * B * kRowBytes;
+  const unsigned char* vg = (const unsigned char*)a.v_pool + (size_t)g * B * kRowBytes;
+  auto load_chunk = [&](int c, int st, const int (&ph)[NU]) {
     int nbytes[NU];
-    int64_t base[NU];
+    uint64_t off[NU];
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       const int U = NU * c + u;
       nbytes[u] = 0;
-      base[u] = 0;
+      off[u] = 0;
       if (ph[u] >= 0) {
         const int valid = L - U * kUnitTok < kUnitTok ? L - U * kUnitTok : kUnitTok;
         nbytes[u] = valid * kRowBytes;
-        const int bi = U / UPB;
-        const int safe = (unsigned)ph[u] < (unsigned)a.NB ? ph[u] : 0;
-        base[u] = (((int64_t)safe * a.Hkv + g) * B + (U - bi * UPB) * kUnitTok) * D;
+        const uint32_t safe = (unsigned)ph[u] < (unsigned)a.NB ? (uint32_t)ph[u] : 0u;
+        off[u] = (uint64_t)safe * blk_bytes + (uint32_t)((U % UPB) * kUnitTok * kRowBytes);
       }
     }
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
-      // The wave's first piece (64 wave + i NTH) is a multiple of 64, so the
-      // unit and the pool (K or V) are the same for all its lanes; they are
-      // computed from the wave index so the compiler sees a uniform resource.
-      const int xw = wave * 64 + i * NTH;
-      const int u = (xw % (16 * KC)) >> 8;
-      const unsigned off = (unsigned)((xw + lane) & 255) * 16;
-      const _Float16* pool = xw < 16 * KC ? a.k_pool : a.v_pool;
-      st.p[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc(pool + base[u], nbytes[u]), off, 0,
-                                                      NT ? 2 : 0);
-    }
-  };
-  auto put = [&](const Stage<NP>& st, int buf) {
-#pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      const int x = tid + i * NTH;
-      const int row = (x % (16 * KC)) >> 4;
-      const int c16 = x & 15;
-      if (x < 16 * KC)
-        *(lds_u32x4*)((lds_u8*)&s_k[buf][0] + k_pos(row, c16)) = st.p[i];
-      else
-        *(lds_u32x4*)((lds_u8*)&s_v[buf][0] + v_pos(row, c16)) = st.p[i];
+      constexpr int kRG = KC / 4;                  // row groups per pool and chunk
+      const bool is_v = (i * NW) / kRG != 0;
+      const int u = ((i * NW) % kRG) / 4;
+      lds_u8* dst = (is_v ? vst(st) : kst(st)) + (u * kUnitTok + 4 * wave) * kRowBytes;
+      const unsigned char* src = (is_v ? vg : kg) + off[u];
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<unsigned char*>(src), 0, nbytes[u], kRsrcWord3);
+      if (NT) load_lds16_nt(r, dst, is_v ? voff_v : voff_k);
+      else load_lds16(r, dst, is_v ? voff_v : voff_k);
     }
   };
 
@@ -257,10 +280,10 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
   //   V, product nn: rows 4kq + m/4 (unit 0) and 16 + 4kq + m/4 (unit 1),
   //   dims 16nn + 4 (m % 4) .. +3, i.e. half (m % 2) of piece 2nn + (m % 4) / 2.
   const int v_row = 4 * kq + (m >> 2);
-  auto compute = [&](int buf, int c, auto masked_flag) {
+  auto compute = [&](int st, int c, auto masked_flag) {
     constexpr bool masked = decltype(masked_flag)::value;
-    const lds_u8* kb = (const lds_u8*)&s_k[buf][0];
-    const lds_u8* vb = (const lds_u8*)&s_v[buf][0];
+    const lds_u8* kb = kst(st);
+    const lds_u8* vb = vst(st);
     h8 ka[NU][4];
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
@@ -305,16 +328,19 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
         x[j] = v;
         mx = __builtin_fmaxf(mx, vis[j] ? v : kNegBig);
       }
-      mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16));
-      mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
       // Running maximum m (log2 domain, scaled). Lazy rescaling: m is raised,
       // and the accumulators rescaled, only when some row of the wave would
       // otherwise see p above 2^kSlack; until then p <= 2^kSlack, well inside
       // fp16's range. The result is the same softmax: the final division uses
-      // the same m for numerator and denominator.
-      const float mcand = mx > 0.5f * kNegBig ? mx * a.scale_log2 : kNegBig;
-      const bool raise = mcand > mrow[t] + kSlack;
-      if (__builtin_amdgcn_ballot_w64(raise)) {
+      // the same m for numerator and denominator. A row's maximum exceeds the
+      // bound exactly when one of its lanes' maxima does, so the decision is
+      // taken on each lane's own maximum; the row maxima are exchanged across
+      // lanes only when some row must be raised.
+      const float mloc = mx > 0.5f * kNegBig ? mx * a.scale_log2 : kNegBig;
+      if (__builtin_amdgcn_ballot_w64(mloc > mrow[t] + kSlack)) {
+        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16));
+        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
+        const float mcand = mx > 0.5f * kNegBig ? mx * a.scale_log2 : kNegBig;
         const float mnew = __builtin_fmaxf(mrow[t], mcand);
         const float alpha = __builtin_amdgcn_exp2f(mrow[t] - mnew);
         mrow[t] = mnew;
@@ -341,52 +367,46 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
     }
   };
 
-  // Pipeline: chunk k travels in register set k % 2 and is computed from LDS
-  // stage k % 2. Iteration c: barrier (chunk c is in LDS, stage (c + 1) % 2 is
-  // free), start the loads of chunk c + 2 into the register set chunk c has
-  // left, compute chunk c, store chunk c + 1 into the other stage. Two chunks
-  // are in flight while a chunk is computed. At the top of an iteration only
-  // the loads of chunk c + 1 are outstanding: with a single group in flight
-  // across the loop edge the compiler's wait counts stay exact (with two it
-  // waited for both before every store). Table entries are read one
-  // iteration before their loads. Every wave runs the same iterations
-  // (barriers); a wave whose rows end earlier skips the arithmetic of chunks
-  // it does not need. Past the last chunk the loads have an empty range: no
-  // memory is touched.
+  // Pipeline over three LDS stages: chunk k goes to stage k % 3. Iteration
+  // c: wait for this wave's loads of chunk c (those of chunk c + 1 may still
+  // be in flight), barrier (every wave's part of chunk c is in LDS and every
+  // wave has finished chunk c - 1), start the loads of chunk c + 2 into the
+  // stage chunk c - 1 used, compute chunk c. The loop is unrolled three times
+  // so that every stage index is a compile-time constant. Every wave runs the
+  // same iterations (barriers); a wave whose rows end earlier skips the
+  // arithmetic of chunks it does not need. Past the last chunk the loads have
+  // an empty range: no memory is read, the stage is filled with zeros.
   if (nchunk_wg > 0) {
-    Stage<NP> r0, r1;
     int ph[NU];
     auto entries = [&](int chunk) {
 #pragma unroll
       for (int u = 0; u < NU; ++u) ph[u] = table_entry(NU * chunk + u);
     };
     entries(0);
-    fetch(r0, 0, ph);
+    load_chunk(0, 0, ph);
     entries(1);
-    fetch(r1, 1, ph);
+    load_chunk(1, 1, ph);
     entries(2);
-    put(r0, 0);
+    auto step = [&](int c, int st) {
+      PA_WAIT_VM(NP);
+      __builtin_amdgcn_s_barrier();
+      load_chunk(c + 2, (st + 2) % 3, ph);
+      entries(c + 3);
+      if (c < nchunk) {
+        if (c >= nfull) compute(st, c, Flag<true>{});
+        else compute(st, c, Flag<false>{});
+      }
+    };
     int c = 0;
     while (true) {
-      __syncthreads();
-      fetch(r0, c + 2, ph);
-      entries(c + 3);
-      if (c < nchunk) {
-        if (c >= nfull) compute(0, c, Flag<true>{});
-        else compute(0, c, Flag<false>{});
-      }
-      put(r1, 1);
+      step(c, 0);
       if (++c >= nchunk_wg) break;
-      __syncthreads();
-      fetch(r1, c + 2, ph);
-      entries(c + 3);
-      if (c < nchunk) {
-        if (c >= nfull) compute(1, c, Flag<true>{});
-        else compute(1, c, Flag<false>{});
-      }
-      put(r0, 0);
+      step(c, 1);
+      if (++c >= nchunk_wg) break;
+      step(c, 2);
       if (++c >= nchunk_wg) break;
     }
+    PA_WAIT_VM(0);   // no load into LDS outlives the workgroup
   }
 
   // normalise and store: lane holds row m, dims 16nn + 4kq + r

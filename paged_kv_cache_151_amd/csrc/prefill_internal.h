@@ -13,11 +13,10 @@ namespace pa {
 #define PA_PREFILL_ROW_TILES 1
 #endif
 constexpr int kPrefillRowTiles = PA_PREFILL_ROW_TILES;
-// Waves per prefill workgroup (4 or 8): they share each staged key/value chunk.
-#ifndef PA_PREFILL_WAVES
-#define PA_PREFILL_WAVES 4
-#endif
-constexpr int kPrefillWaves = PA_PREFILL_WAVES;
+// Waves per prefill workgroup: they share each staged key/value chunk. The
+// load layout (each load instruction's pool and unit fixed at compile time)
+// is built for four.
+constexpr int kPrefillWaves = 4;
 // Keys per pipeline step (32 or 64).
 #ifndef PA_PREFILL_CHUNK
 #define PA_PREFILL_CHUNK 32

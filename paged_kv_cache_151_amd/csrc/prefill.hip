@@ -24,10 +24,14 @@
 //
 // Instruction budget. A wave issues at most one instruction per turn on its
 // SIMD, so every scalar or vector instruction around the 16 matrix products of
-// a 32-key step costs issue slots the products need. The loads are laid out so
-// that the pool (K or V) and the unit of every load instruction are known at
-// compile time and each lane's offset into a unit never changes; only the
-// unit's base address and valid length are computed per chunk.
+// a 32-key step costs issue slots the products need. Each wave loads one pool
+// (K or V) of one unit of every chunk, with per-lane offsets that never
+// change: per chunk it computes one unit's base address and valid length. The
+// block table is read with a vector load (scalar loads share their wait
+// counter with LDS reads, so every operand wait would also wait for them),
+// and chunks that every row of the workgroup sees in full run through a loop
+// with a single code path (no masking, no per-wave skip, no join that makes
+// the compiler copy the accumulators).
 //
 // Matrix products (v_mfma_f32_16x16x32_f16; lane l = 16 kq + m):
 //   scores   S^T = K Q^T per unit: the A operand is key token m, dims
@@ -184,6 +188,13 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
   kend_wg = kend_wg > L ? L : kend_wg;
   kend_wg = kend_wg < 0 ? 0 : kend_wg;
   const int nchunk_wg = (kend_wg + KC - 1) / KC;
+  const int nblk = (kend_wg + B - 1) / B;
+  // Chunks that every row of the workgroup sees in full (keys before the
+  // position of its first row), rounded down to whole turns of the three
+  // stages: these run through a loop with a single code path.
+  int nall = base_pos + qb * QB + 1 > 0 ? (base_pos + qb * QB + 1) / KC : 0;
+  nall = nall > nchunk_wg ? nchunk_wg : nall;
+  const int nfast = nall - nall % 3;
 
   // this wave's rows and the chunks it computes
   const int hq = g * G + hg * HW + wave % HW;
@@ -223,55 +234,69 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
     for (int nn = 0; nn < 8; ++nn) o[t][nn] = f4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Physical blocks come from the table through scalar loads (the index is
-  // uniform): they are counted apart from the vector loads, so waiting for a
-  // table entry never waits for K/V data in flight. Entries outside the pool
-  // are clamped to block 0.
-  typedef const __attribute__((address_space(4))) int32_t* const_i32;
-  const const_i32 trow = (const_i32)(a.tables + (int64_t)s * a.MB);
-  // physical block of unit U, or -1 when U holds no key the workgroup needs
-  // (U * 16 < kend_wg also puts its block index below nblk <= MB)
-  auto table_entry = [&](int U) -> int { return U * kUnitTok < kend_wg ? trow[U / UPB] : -1; };
+  // Physical blocks come from the table by a vector load per chunk (lane u
+  // reads unit u's entry, range-checked to the workgroup's nblk entries),
+  // issued just before the chunk loads of the same iteration: the wait at the
+  // top of the next iteration that lets those loads stay in flight also
+  // covers it, and no LDS wait ever waits for a table read (scalar loads share
+  // the LDS counter). Entries outside the pool are clamped to block 0.
+  const __amdgpu_buffer_rsrc_t trs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int32_t*>(a.tables + (int64_t)s * a.MB), 0, nblk * 4, kRsrcWord3);
+  auto table_load = [&](int chunk) -> int {
+    const int U = NU * chunk + (lane < NU ? lane : 0);
+    return __builtin_amdgcn_raw_buffer_load_b32(trs, (unsigned)(U / UPB) * 4u, 0, 0);
+  };
 
-  // Loads into LDS. Instruction i of wave w carries row group i * NW + w of
-  // the chunk (4 token rows); with four waves its pool and its unit depend on
-  // i alone, and its rows in the unit are 4w .. 4w + 3 for every instruction.
-  // Lane 16 kq + m writes LDS piece slot m of row r = 4w + kq, so it loads the
-  // global piece that the swizzle places there (m ^ swizzle(r)): a fixed
-  // offset into the unit for the whole kernel. Lanes past a unit's valid
+  // Loads into LDS. Wave w loads pool w / 2 (K, then V) of each chunk, units
+  // (w % 2) * NU / 2 .. + NU / 2 - 1, four row groups (4 token rows) per
+  // unit: one buffer resource per unit and wave. Lane 16 kq + m of row group
+  // i writes LDS piece slot m of row r = 4i + kq of the unit, so it loads the
+  // global piece that the swizzle places there (m ^ swizzle(r)): four fixed
+  // offsets into a unit for the whole kernel. Lanes past a unit's valid
   // tokens fall outside the resource's range and write zeros.
-  const int dr = 4 * wave + kq;
-  const unsigned voff_k = (unsigned)(dr * kRowBytes + ((m ^ (dr & 15)) << 4));
-  const unsigned voff_v = (unsigned)(dr * kRowBytes + ((m ^ ((dr & 7) << 1)) << 4));
+  static_assert(NW == 4 && NU % 2 == 0, "one pool and half the units per wave");
+  constexpr int UW = NU / 2;                      // units per wave and chunk
+  const bool w_is_v = wave >= 2;
+  const int w_u0 = (wave & 1) * UW;
+  unsigned voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * i + kq;
+    const int piece = w_is_v ? (m ^ ((r & 7) << 1)) : (m ^ (r & 15));
+    voff[i] = (unsigned)(r * kRowBytes + (piece << 4));
+  }
   const uint32_t blk_bytes = (uint32_t)a.Hkv * (uint32_t)B * kRowBytes;   // one block, all heads
-  const unsigned char* kg = (const unsigned char*)a.k_pool + (size_t)g * B * kRowBytes;
-  const unsigned char* vg = (const unsigned char*)a.v_pool + (size_t)g * B * kRowBytes;
+  const unsigned char* pg = (const unsigned char*)(w_is_v ? a.v_pool : a.k_pool) + (size_t)g * B * kRowBytes;
+  const int w_lds = w_u0 * kUnitTok * kRowBytes;
   auto load_chunk = [&](int c, int st, const int (&ph)[NU]) {
-    int nbytes[NU];
-    uint64_t off[NU];
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const int U = NU * c + u;
-      nbytes[u] = 0;
-      off[u] = 0;
-      if (ph[u] >= 0) {
-        const int valid = L - U * kUnitTok < kUnitTok ? L - U * kUnitTok : kUnitTok;
-        nbytes[u] = valid * kRowBytes;
-        const uint32_t safe = (unsigned)ph[u] < (unsigned)a.NB ? (uint32_t)ph[u] : 0u;
-        off[u] = (uint64_t)safe * blk_bytes + (uint32_t)((U % UPB) * kUnitTok * kRowBytes);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      constexpr int kRG = KC / 4;                  // row groups per pool and chunk
-      const bool is_v = (i * NW) / kRG != 0;
-      const int u = ((i * NW) % kRG) / 4;
-      lds_u8* dst = (is_v ? vst(st) : kst(st)) + (u * kUnitTok + 4 * wave) * kRowBytes;
-      const unsigned char* src = (is_v ? vg : kg) + off[u];
+    for (int j = 0; j < UW; ++j) {
+      const int U = NU * c + w_u0 + j;
+      const int valid = L - U * kUnitTok < kUnitTok ? L - U * kUnitTok : kUnitTok;
+      const int nbytes = U * kUnitTok < kend_wg ? valid * kRowBytes : 0;
+      const int phys = ph[w_u0 + j];
+      const uint32_t safe = (unsigned)phys < (unsigned)a.NB ? (uint32_t)phys : 0u;
+      const uint64_t off = (uint64_t)safe * blk_bytes + (uint32_t)((U % UPB) * kUnitTok * kRowBytes);
       const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<unsigned char*>(src), 0, nbytes[u], kRsrcWord3);
-      if (NT) load_lds16_nt(r, dst, is_v ? voff_v : voff_k);
-      else load_lds16(r, dst, is_v ? voff_v : voff_k);
+          const_cast<unsigned char*>(pg + off), 0, nbytes, kRsrcWord3);
+      // The branch is uniform; each side names its LDS array at compile time.
+      // (With the array chosen at run time the compiler cannot tell which
+      // stage a load writes and waits for every load before any LDS read.)
+      if (w_is_v) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          lds_u8* dst = vst(st) + w_lds + (j * kUnitTok + 4 * i) * kRowBytes;
+          if (NT) load_lds16_nt(r, dst, voff[i]);
+          else load_lds16(r, dst, voff[i]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          lds_u8* dst = kst(st) + w_lds + (j * kUnitTok + 4 * i) * kRowBytes;
+          if (NT) load_lds16_nt(r, dst, voff[i]);
+          else load_lds16(r, dst, voff[i]);
+        }
+      }
     }
   };
 
@@ -368,37 +393,61 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
   };
 
   // Pipeline over three LDS stages: chunk k goes to stage k % 3. Iteration
-  // c: wait for this wave's loads of chunk c (those of chunk c + 1 may still
-  // be in flight), barrier (every wave's part of chunk c is in LDS and every
-  // wave has finished chunk c - 1), start the loads of chunk c + 2 into the
-  // stage chunk c - 1 used, compute chunk c. The loop is unrolled three times
-  // so that every stage index is a compile-time constant. Every wave runs the
-  // same iterations (barriers); a wave whose rows end earlier skips the
-  // arithmetic of chunks it does not need. Past the last chunk the loads have
-  // an empty range: no memory is read, the stage is filled with zeros.
+  // c: wait for this wave's loads of chunk c and its table read for chunk
+  // c + 2 (the loads of chunk c + 1 may still be in flight), barrier (every
+  // wave's part of chunk c is in LDS and every wave has finished chunk c - 1),
+  // read chunk c + 2's entries, start the table read for chunk c + 3 and the
+  // loads of chunk c + 2 into the stage chunk c - 1 used, compute chunk c.
+  // Both loops are unrolled three times so that every stage index is a
+  // compile-time constant. The first runs the chunks every row sees in full
+  // (all waves, no mask); the second the rest, where a wave masks the keys
+  // beyond its rows and skips chunks past them. Every wave runs the same
+  // iterations (barriers). Past the last chunk the loads have an empty range:
+  // no memory is read, the stage is filled with zeros.
   if (nchunk_wg > 0) {
     int ph[NU];
-    auto entries = [&](int chunk) {
+    int tv = table_load(0);
+    auto entries = [&]() {
 #pragma unroll
-      for (int u = 0; u < NU; ++u) ph[u] = table_entry(NU * chunk + u);
+      for (int u = 0; u < NU; ++u) ph[u] = __builtin_amdgcn_readlane(tv, u);
     };
-    entries(0);
+    entries();
     load_chunk(0, 0, ph);
-    entries(1);
+    tv = table_load(1);
+    entries();
     load_chunk(1, 1, ph);
-    entries(2);
+    tv = table_load(2);
+    // every row sees chunk c in full, every wave computes it
+    auto fast = [&](int c, int st) {
+      PA_WAIT_VM(NP);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      entries();
+      tv = table_load(c + 3);
+      __builtin_amdgcn_sched_barrier(0);
+      load_chunk(c + 2, (st + 2) % 3, ph);
+      compute(st, c, Flag<false>{});
+    };
     auto step = [&](int c, int st) {
       PA_WAIT_VM(NP);
       __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      entries();
+      tv = table_load(c + 3);
+      __builtin_amdgcn_sched_barrier(0);
       load_chunk(c + 2, (st + 2) % 3, ph);
-      entries(c + 3);
       if (c < nchunk) {
         if (c >= nfull) compute(st, c, Flag<true>{});
         else compute(st, c, Flag<false>{});
       }
     };
     int c = 0;
-    while (true) {
+    for (; c < nfast; c += 3) {
+      fast(c, 0);
+      fast(c + 1, 1);
+      fast(c + 2, 2);
+    }
+    while (c < nchunk_wg) {
       step(c, 0);
       if (++c >= nchunk_wg) break;
       step(c, 1);

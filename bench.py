@@ -46,8 +46,11 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 10; prefill 50: one step is under a millisecond)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps first (default 3; prefill 50, so that the clock has "
+                         "ramped up before the timed region)")
     ap.add_argument("--workload", default="chat",
                     choices=["chat", "7b", "shared_prefix", "long_context", "tiny", "block_manager",
                              "swap", "prefill"])
@@ -66,7 +69,13 @@ def parse():
     ap.add_argument("--copy-reference-mb", type=int, default=0,
                     help="after timing, run one plain device-to-device copy of this many MiB "
                          "(a copy of known size for scaling traffic counters)")
-    return ap.parse_args()
+    args = ap.parse_args()
+    short = args.workload == "prefill"
+    if args.steps is None:
+        args.steps = 50 if short else 10
+    if args.warmup is None:
+        args.warmup = 50 if short else 3
+    return args
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pa_decode_chat_b128_traffic.json")

@@ -6,16 +6,17 @@
 namespace pa {
 
 // Query row tiles of 16 per prefill wave. More rows per wave read each
-// staged key/value chunk from LDS for more rows, but hold more registers: on
-// MI355X one tile (223 VGPRs, two waves per SIMD) measured fastest for the
-// 16-prompt chat batch (531 us, against 636 us for two tiles at one wave per SIMD).
+// staged key/value chunk from LDS for more rows, but hold more registers: one
+// tile fits in about 215 VGPRs (two waves per SIMD); two tiles need more than
+// 256 (one wave per SIMD) and measured slower on MI355X.
 #ifndef PA_PREFILL_ROW_TILES
 #define PA_PREFILL_ROW_TILES 1
 #endif
 constexpr int kPrefillRowTiles = PA_PREFILL_ROW_TILES;
 // Waves per prefill workgroup: they share each staged key/value chunk. The
-// load layout (each load instruction's pool and unit fixed at compile time)
-// is built for four.
+// load layout (each wave loads one pool, K or V, of half the units of every
+// chunk) is built for four. Eight (one workgroup per CU at two waves per
+// SIMD) measured 15 % slower: nothing covers the barrier waits.
 constexpr int kPrefillWaves = 4;
 // Keys per pipeline step (32 or 64).
 #ifndef PA_PREFILL_CHUNK

@@ -111,6 +111,18 @@ def _same_shape(a, b, names):
 _F16, _I32, _I64 = torch.float16, torch.int32, torch.int64
 
 
+def _rows(t, name, n, fn):
+    """The kernels index these arrays by sequence or token: fewer rows than the
+    sizes passed to the library would be read past their end."""
+    if t is not None and (t.dim() == 0 or t.shape[0] != n):
+        raise ValueError(f"{fn}: {name} needs {n} rows, has {tuple(t.shape)}")
+
+
+def _pairs(t, fn):
+    if t.dim() != 2 or t.shape[1] != 2:
+        raise ValueError(f"{fn}: block_mapping must be [n, 2], got {tuple(t.shape)}")
+
+
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -131,6 +143,10 @@ def pa_slot_mapping(block_tables, block_size: int, num_blocks: int, context_lens
     S, MB = block_tables.shape
     T = positions.shape[0] if positions is not None else (
         seq_ids.shape[0] if seq_ids is not None else S)
+    _rows(seq_ids, "seq_ids", T, "pa_slot_mapping")
+    _rows(positions, "positions", T, "pa_slot_mapping")
+    _rows(context_lens, "context_lens", S, "pa_slot_mapping")
+    _rows(out, "out", T, "pa_slot_mapping")
     if out is None:
         out = torch.empty(T, dtype=torch.int64, device=block_tables.device)
     _check("pa_slot_mapping", _lib.pa_slot_mapping(
@@ -147,6 +163,9 @@ def pa_write_kv(key, value, k_pool, v_pool, slot_mapping, stream=None):
     NB, _, B, _ = k_pool.shape
     _same_shape(key, value, "key/value")
     _same_shape(k_pool, v_pool, "k_pool/v_pool")
+    _rows(slot_mapping, "slot_mapping", T, "pa_write_kv")
+    if tuple(k_pool.shape[1:2]) != (Hkv,) or k_pool.shape[3] != D:
+        raise ValueError(f"pa_write_kv: key {tuple(key.shape)} does not fit pool blocks {tuple(k_pool.shape)}")
     _check("pa_write_kv", _lib.pa_write_kv(
         _arg(key, "key", _F16), _arg(value, "value", _F16), _arg(k_pool, "k_pool", _F16),
         _arg(v_pool, "v_pool", _F16), _arg(slot_mapping, "slot_mapping", _I64),
@@ -156,6 +175,7 @@ def pa_write_kv(key, value, k_pool, v_pool, slot_mapping, stream=None):
 def pa_copy_blocks(k_pool, v_pool, block_mapping, stream=None):
     """Copy whole blocks src -> dst for each row of block_mapping [n, 2] (int32)."""
     NB, Hkv, B, D = k_pool.shape
+    _pairs(block_mapping, "pa_copy_blocks")
     n = block_mapping.shape[0]
     _same_shape(k_pool, v_pool, "k_pool/v_pool")
     _check("pa_copy_blocks", _lib.pa_copy_blocks(
@@ -169,6 +189,7 @@ def pa_swap_blocks(dst_k_pool, dst_v_pool, src_k_pool, src_v_pool, block_mapping
     pinned host tensors (pin_memory=True)."""
     NB_src, Hkv, B, D = src_k_pool.shape
     NB_dst = dst_k_pool.shape[0]
+    _pairs(block_mapping, "pa_swap_blocks")
     n = block_mapping.shape[0]
     _same_shape(dst_k_pool, dst_v_pool, "dst pools")
     _same_shape(src_k_pool, src_v_pool, "src pools")
@@ -205,6 +226,8 @@ def pa_decode(query, k_pool, v_pool, block_tables, context_lens, max_context_len
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _same_shape(out, query, "out/query")
     _same_shape(k_pool, v_pool, "k_pool/v_pool")
+    _rows(block_tables, "block_tables", S, "pa_decode")
+    _rows(context_lens, "context_lens", S, "pa_decode")
     _check("pa_decode", _lib.pa_decode(
         _arg(out, "out", _F16), _arg(query, "query", _F16), _arg(k_pool, "k_pool", _F16),
         _arg(v_pool, "v_pool", _F16), _arg(block_tables, "block_tables", _I32),
@@ -236,7 +259,12 @@ def pa_prefill(query, k_pool, v_pool, block_tables, context_lens, query_start,
 
 def pa_stream_read(buffer, sink, workgroups: int = 4096, nbytes: int = None, stream=None):
     """Read-bandwidth probe: one linear pass over a device tensor (measurement utility)."""
-    n = buffer.numel() * buffer.element_size() if nbytes is None else int(nbytes)
+    size = buffer.numel() * buffer.element_size()
+    n = size if nbytes is None else int(nbytes)
+    if not 0 <= n <= size:
+        raise ValueError(f"pa_stream_read: nbytes={n} outside the buffer's {size} bytes")
+    if sink.numel() * sink.element_size() < 4:
+        raise ValueError("pa_stream_read: sink needs 4 bytes")
     _check("pa_stream_read", _lib.pa_stream_read(_arg(buffer, "buffer"), n - n % 16,
                                                  _arg(sink, "sink"), int(workgroups),
                                                  _stream(stream)))

@@ -197,9 +197,46 @@ def test_binding_refuses_tensors_it_would_misread():
         pa.pa_write_kv(key, key, pool, pool, slots)
     with pytest.raises(TypeError, match="float16"):
         pa.pa_write_kv(key.float(), key, pool, pool, slots)
+    strided = torch.zeros(4, 4, 128, dtype=torch.float16)[:, ::2]   # [4, 2, 128], not contiguous
     with pytest.raises(ValueError, match="contiguous"):
-        pa.pa_write_kv(key.transpose(0, 1), key.transpose(0, 1), pool, pool, slots)
+        pa.pa_write_kv(strided, strided, pool, pool, slots)
     with pytest.raises(ValueError, match="differ"):
         pa.pa_write_kv(key, key[:3], pool, pool, slots)
     with pytest.raises(TypeError, match="int32"):   # an int64 block mapping would be misread
         pa._arg(torch.zeros(2, 2, dtype=torch.int64), "block_mapping", torch.int32)
+
+
+def test_binding_refuses_arrays_shorter_than_the_sizes_it_passes():
+    # the kernels index these arrays by sequence, token or pair: a short one
+    # would be read past its end, so the binding refuses it (CPU tensors: the
+    # shape checks come before any device check or library call)
+    import torch
+    import paged_kv_cache_151_amd as pa
+    f16, i32, i64 = torch.float16, torch.int32, torch.int64
+    q = torch.zeros(3, 4, 128, dtype=f16)
+    pool = torch.zeros(8, 4, 16, 128, dtype=f16)
+    with pytest.raises(ValueError, match="block_tables needs 3 rows"):
+        pa.pa_decode(q, pool, pool, torch.zeros(2, 4, dtype=i32), torch.zeros(3, dtype=i32), 48, 0.1)
+    with pytest.raises(ValueError, match="context_lens needs 3 rows"):
+        pa.pa_decode(q, pool, pool, torch.zeros(3, 4, dtype=i32), torch.zeros(2, dtype=i32), 48, 0.1)
+    key = torch.zeros(5, 4, 128, dtype=f16)
+    with pytest.raises(ValueError, match="slot_mapping needs 5 rows"):
+        pa.pa_write_kv(key, key, pool, pool, torch.zeros(4, dtype=i64))
+    with pytest.raises(ValueError, match="does not fit pool blocks"):
+        pa.pa_write_kv(key[:, :2].contiguous(), key[:, :2].contiguous(), pool, pool,
+                       torch.zeros(5, dtype=i64))
+    with pytest.raises(ValueError, match=r"\[n, 2\]"):
+        pa.pa_copy_blocks(pool, pool, torch.zeros(6, dtype=i32))
+    with pytest.raises(ValueError, match=r"\[n, 2\]"):
+        pa.pa_swap_blocks(pool, pool, pool, pool, torch.zeros(3, 3, dtype=i32))
+    tables = torch.zeros(2, 4, dtype=i32)
+    with pytest.raises(ValueError, match="seq_ids needs 5 rows"):
+        pa.pa_slot_mapping(tables, 16, 8, seq_ids=torch.zeros(4, dtype=i32),
+                           positions=torch.zeros(5, dtype=i32))
+    with pytest.raises(ValueError, match="context_lens needs 2 rows"):
+        pa.pa_slot_mapping(tables, 16, 8, context_lens=torch.zeros(1, dtype=i32))
+    buf = torch.zeros(1024, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="outside the buffer"):
+        pa.pa_stream_read(buf, torch.zeros(1, dtype=i32), nbytes=2048)
+    with pytest.raises(ValueError, match="sink needs 4 bytes"):
+        pa.pa_stream_read(buf, torch.zeros(2, dtype=torch.uint8))

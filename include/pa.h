@@ -218,8 +218,9 @@ size_t pa_decode_workspace_bytes(int S, int Hq, int Hkv, int D, int B, int max_c
  *                     block)
  *   workspace         device buffer of at least pa_decode_workspace_bytes(...)
  *                     bytes, 16-byte aligned; may be NULL when that is 0
- * Supported: D = 128; B a multiple of 16 (one block per sequence of at least
- * its length is the contiguous layout); Hq / Hkv in {1, 2, 4, 8}. S = 0 is a no-op.
+ * Supported: D = 128; B = 8 or a multiple of 16 (one block per sequence of at
+ * least its length is the contiguous layout); Hq / Hkv in {1, 2, 4, 8}. S = 0 is
+ * a no-op.
  * L_s outside the stated range is a caller error: the kernels clamp to the
  * table and the launch, so no access leaves the buffers.
  */

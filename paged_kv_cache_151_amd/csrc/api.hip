@@ -274,8 +274,8 @@ pa_status pa_decode(void* out, const void* query, const void* k_pool, const void
                 partition_size, pa::kDecodeUnit);
   const int G = Hq / Hkv;
   if (D != pa::kHeadDim) return fail(PA_ERR_UNSUPPORTED, "pa_decode: D=%d (supported: 128)", D);
-  if (B % pa::kDecodeUnit)
-    return fail(PA_ERR_UNSUPPORTED, "pa_decode: B=%d (supported: multiples of %d)", B,
+  if (B != 8 && B % pa::kDecodeUnit)
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode: B=%d (supported: 8 and multiples of %d)", B,
                 pa::kDecodeUnit);
   if (G != 1 && G != 2 && G != 4 && G != 8)
     return fail(PA_ERR_UNSUPPORTED, "pa_decode: Hq/Hkv=%d (supported: 1, 2, 4, 8)", G);

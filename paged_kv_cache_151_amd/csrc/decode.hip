@@ -12,7 +12,8 @@
 // partition p). A partition is P consecutive tokens, P a multiple of 16; the
 // work unit is 16 tokens of one KV head (a 4 KiB K tile and a 4 KiB V tile),
 // so a block of B tokens is B / 16 units and a partition may start inside a
-// block. The workgroup's waves take the partition's units round-robin.
+// block. With B = 8 a unit spans two blocks: its first 8 tokens come from
+// one 2 KiB tile, the other 8 from the next block's. The workgroup's waves take the partition's units round-robin.
 // Inside a wave, lane = 16 * r + c: DPP row r (0..3) holds tokens 4i + r of
 // the unit (i = 0..3) and lane c of the row holds dims 8c .. 8c+7, so each
 // 16-byte load of a row reads 256 contiguous bytes and a wave-wide load reads
@@ -127,6 +128,30 @@ __device__ __forceinline__ void load_tile(Tile& t, const _Float16* kb, const _Fl
   }
 }
 
+// B = 8: row groups 0-1 (tokens 0-7) from the first block's tile, 2-3 (tokens
+// 8-15) from the second's, each with its own range (an empty second range
+// leaves a block the sequence does not have untouched).
+template <bool NT>
+__device__ __forceinline__ void load_tile_split(Tile& t, const _Float16* kb0, const _Float16* vb0,
+                                                int nbytes0, const _Float16* kb1,
+                                                const _Float16* vb1, int nbytes1,
+                                                unsigned lane_byte_off) {
+  const __amdgpu_buffer_rsrc_t rk0 =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16*>(kb0), 0, nbytes0, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rv0 =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16*>(vb0), 0, nbytes0, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rk1 =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16*>(kb1), 0, nbytes1, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rv1 =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16*>(vb1), 0, nbytes1, kRsrcWord3);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int so = (i & 1) * (4 * kHeadDim * 2);
+    t.k[i] = __builtin_amdgcn_raw_buffer_load_b128(i < 2 ? rk0 : rk1, lane_byte_off, so, NT ? 2 : 0);
+    t.v[i] = __builtin_amdgcn_raw_buffer_load_b128(i < 2 ? rv0 : rv1, lane_byte_off, so, NT ? 2 : 0);
+  }
+}
+
 // Online-softmax update of one lane's state for the unit in `t`.
 // tok_base = logical position of the unit's token 0 for this lane's row
 // (unit start + r); with MASK, tokens at or past `L` are excluded by
@@ -196,9 +221,10 @@ void decode_partition_kernel(const DecodeArgs a) {
   constexpr int D = kHeadDim;
   constexpr int NH = G / HPW;           // head groups
   constexpr int NU = NW / NH;           // unit subsets
-  static_assert(BT % kUnit == 0, "block size must be a multiple of 16");
+  static_assert(BT == 8 || BT % kUnit == 0, "block size must be 8 or a multiple of 16");
+  constexpr bool kSplit = BT == 8;      // a unit spans two blocks
   const int B = BT > 0 ? BT : a.B;      // BT = 0: block size known at run time only
-  const int UPB = B / kUnit;            // units per block
+  const int UPB = kSplit ? 1 : B / kUnit;   // units per block (B >= 16)
   static_assert(DEPTH == 1 || DEPTH == 2, "prefetch depth 1 or 2");
   static_assert(G % HPW == 0 && NW % NH == 0, "waves must cover the head groups");
   __shared__ float s_acc[NW][HPW][D];
@@ -241,8 +267,10 @@ void decode_partition_kernel(const DecodeArgs a) {
   // P is a multiple of 16, not necessarily of B: the partition may start
   // inside a block. U0 is its first unit counted from the sequence start.
   const int U0 = tok0 / kUnit;
-  const int blk0 = U0 / UPB;
-  const int nblk = (U0 + nunits - 1) / UPB - blk0 + 1;
+  // blocks holding the partition's tokens (B = 8: two per unit, the last
+  // possibly absent when the final unit ends within its first half)
+  const int blk0 = kSplit ? 2 * U0 : U0 / UPB;
+  const int nblk = kSplit ? (len + 7) / 8 : (U0 + nunits - 1) / UPB - blk0 + 1;
 
   const int hw0 = hq0 + hgrp * HPW;      // this wave's first query head
   u32x4 q[HPW];
@@ -277,8 +305,8 @@ void decode_partition_kernel(const DecodeArgs a) {
     const int ce = cb + 64 < nblk ? cb + 64 : nblk;
     const int tbl = cb + lane < ce ? trow[cb + lane] : -1;
     // the partition's units (counted from its start) whose block is in [cb, ce)
-    const int ub0 = (blk0 + cb) * UPB - U0;
-    const int ue0 = (blk0 + ce) * UPB - U0;
+    const int ub0 = kSplit ? cb / 2 : (blk0 + cb) * UPB - U0;
+    const int ue0 = kSplit ? (ce + 1) / 2 : (blk0 + ce) * UPB - U0;
     const int ub = ub0 > 0 ? ub0 : 0;
     const int ue = ue0 < nunits ? ue0 : nunits;
     auto locate = [&](int u) -> int64_t {
@@ -288,14 +316,35 @@ void decode_partition_kernel(const DecodeArgs a) {
       const int safe = (unsigned)phys < (unsigned)a.NB ? phys : 0;
       return (((int64_t)safe * a.Hkv + g) * B + (au - bi * UPB) * kUnit) * D;
     };
+    // B = 8: tile base of block j (0, 1) of unit u. The chunk's 64 entries
+    // hold whole units (units start at even block indices), so both lanes
+    // read here are in the chunk; an entry past the partition's blocks is -1
+    // and is clamped to block 0, with an empty range.
+    auto locate_half = [&](int u, int j) -> int64_t {
+      const int phys = __builtin_amdgcn_readlane(tbl, 2 * u + j - cb);
+      const int safe = (unsigned)phys < (unsigned)a.NB ? phys : 0;
+      return ((int64_t)safe * a.Hkv + g) * B * D;
+    };
     // Loads unit u, or issues a no-op load when u is past the wave's last unit.
     auto fetch = [&](Tile& t, int u) {
       const bool live = u < ue;
       const int uu = live ? u : ue - 1;
-      const int64_t base = locate(uu);
-      const int valid = len - uu * kUnit;
-      const int nbytes = !live ? 0 : (valid >= kUnit ? kUnitBytes : valid * (kHeadDim * 2));
-      load_tile<NT>(t, a.k_pool + base, a.v_pool + base, nbytes, lane_off);
+      if constexpr (kSplit) {
+        const int valid = len - uu * kUnit;
+        const int64_t b0 = locate_half(uu, 0);
+        const int64_t b1 = locate_half(uu, 1);
+        const int v0 = valid < 8 ? valid : 8;
+        const int v1 = valid - 8 < 0 ? 0 : (valid - 8 > 8 ? 8 : valid - 8);
+        const int n0 = live ? v0 * (kHeadDim * 2) : 0;
+        const int n1 = live ? v1 * (kHeadDim * 2) : 0;
+        load_tile_split<NT>(t, a.k_pool + b0, a.v_pool + b0, n0, a.k_pool + b1, a.v_pool + b1, n1,
+                            lane_off);
+      } else {
+        const int64_t base = locate(uu);
+        const int valid = len - uu * kUnit;
+        const int nbytes = !live ? 0 : (valid >= kUnit ? kUnitBytes : valid * (kHeadDim * 2));
+        load_tile<NT>(t, a.k_pool + base, a.v_pool + base, nbytes, lane_off);
+      }
     };
     auto step = [&](const Tile& t, int u) {
       if (u < n_full) {
@@ -461,6 +510,7 @@ hipError_t launch_partition_g(const DecodeArgs& a, int G, hipStream_t stream) {
 hipError_t launch_decode(const DecodeArgs& a, int B, int G, hipStream_t stream) {
   hipError_t e;
   switch (B) {   // the common block sizes are compile-time specialisations
+    case 8: e = launch_partition_g<8>(a, G, stream); break;
     case 16: e = launch_partition_g<16>(a, G, stream); break;
     case 32: e = launch_partition_g<32>(a, G, stream); break;
     default: e = launch_partition_g<0>(a, G, stream); break;

@@ -69,7 +69,8 @@ def test_decode_host_validation(lib):
     assert b"null" in lib.pa_last_error()
     assert decode(lib, Hq=6, Hkv=4) == PA_ERR_SHAPE
     assert decode(lib, D=64) == PA_ERR_UNSUPPORTED
-    assert decode(lib, B=8, NB=16, MB=6) == PA_ERR_UNSUPPORTED
+    assert decode(lib, B=24, NB=16, MB=2) == PA_ERR_UNSUPPORTED   # 8 and multiples of 16 only
+    assert decode(lib, B=8, NB=16, MB=6, out=None) == PA_ERR_NULL   # B = 8 passes validation
     assert decode(lib, Hq=48, Hkv=4) == PA_ERR_UNSUPPORTED      # group of 12
     assert decode(lib, maxL=49) == PA_ERR_SHAPE                 # beyond MB * B
     assert decode(lib, P=24) == PA_ERR_SHAPE                    # not a multiple of 16

@@ -287,6 +287,72 @@ def test_other_block_sizes_and_partitions_inside_blocks(pa, B, G):
         check_case(pa, c, partition_size=ps)
 
 
+
+B8_LENS = [1, 7, 8, 9, 15, 16, 17, 31, 32, 33, 63, 64, 65, 129, 1030]
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_block_size_8_units_spanning_two_blocks(pa, G):
+    """B = 8: every 16-token work unit reads two blocks; lengths end in either
+    half of a unit, and partitions of 16 to 2048 tokens (over 64 blocks: two
+    table chunks) start on unit boundaries."""
+    c = W.make_case(f"B8_G{G}", 2200 + G, B8_LENS, Hq=2 * G, Hkv=2, B=8)
+    for ps in (0, 16, 48, 1024, 2048):
+        check_case(pa, c, partition_size=ps)
+
+
+def relayout(c, B):
+    """The same logical keys and values in a fresh pool of block size B (blocks
+    handed out in order), with the case's new tokens and queries."""
+    S = c.S
+    rows = [oracle.blocks_for(int(L), B) for L in c.context_lens]
+    NB = sum(rows) + 1
+    MB = max(rows)
+    tables = np.full((S, MB), -1, np.int32)
+    kp = np.zeros((NB, c.Hkv, B, c.D), np.float16)
+    vp = np.zeros_like(kp)
+    nxt = 0
+    for s, L in enumerate(c.context_lens.tolist()):
+        K = oracle.gather(c.k_pool, c.block_tables[s], L, c.B)
+        V = oracle.gather(c.v_pool, c.block_tables[s], L, c.B)
+        for j in range(rows[s]):
+            tables[s, j] = nxt
+            n = min(B, L - j * B)
+            kp[nxt, :, :n] = K[:, j * B:j * B + n]
+            vp[nxt, :, :n] = V[:, j * B:j * B + n]
+            nxt += 1
+    return W.DecodeCase(**{**c.__dict__, "B": B, "NB": NB, "block_tables": tables,
+                           "k_pool": kp, "v_pool": vp})
+
+
+@pytest.mark.parametrize("G", [1, 4])
+def test_block_size_8_is_bit_identical_to_16(pa, G):
+    # the arithmetic order depends only on logical positions, so the same
+    # tokens give the same bits whatever the block size
+    c8 = W.make_case(f"B8_vs_16_G{G}", 2300 + G, B8_LENS, Hq=2 * G, Hkv=2, B=8)
+    c16 = relayout(c8, 16)
+    for ps in (0, 16, 64):
+        say(f"B=8 vs B=16, G={G}, P={ps}")
+        a, _ = decode_step(pa, c8, dev(c8.k_pool), dev(c8.v_pool), partition_size=ps)
+        b, _ = decode_step(pa, c16, dev(c16.k_pool), dev(c16.v_pool), partition_size=ps)
+        assert np.array_equal(u16(a), u16(b))
+
+
+def test_block_size_8_unused_slots_and_blocks_never_reach_the_output(pa):
+    c = W.make_case("B8_poison", 2400, B8_LENS, Hq=4, Hkv=2, B=8)
+    clean, _ = decode_step(pa, c, dev(c.k_pool), dev(c.v_pool), partition_size=48)
+    keep = np.zeros(c.NB * c.B, bool)
+    for s, L in enumerate(c.context_lens):
+        for t in range(int(L)):
+            keep[oracle.slot_of(c.block_tables[s], t, c.B)] = True
+    kp, vp = c.k_pool.copy(), c.v_pool.copy()
+    mask = ~keep.reshape(c.NB, c.B)
+    kp.transpose(0, 2, 1, 3)[mask] = np.float16(np.nan)
+    vp.transpose(0, 2, 1, 3)[mask] = np.float16(np.inf)
+    say("B=8 poison")
+    got, _ = decode_step(pa, c, dev(kp), dev(vp), partition_size=48)
+    assert np.array_equal(u16(clean), u16(got))
+
 def test_contiguous_layout_one_block_per_sequence(pa):
     # the pre-paging layout: every sequence in one block as long as the longest
     lens = [1000, 37, 512, 999, 640]

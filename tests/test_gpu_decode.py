@@ -7,6 +7,7 @@ import pytest
 import oracle
 import workloads as W
 from gpu_util import assert_attention_close, dev, host, pa_module, say, u16
+from host_validate import decode_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -34,6 +35,7 @@ def oracle_step(case, k_pool, v_pool):
 
 def check_case(pa, case, partition_size=0):
     say(case.name, f"S={case.S} Hq={case.Hq} Hkv={case.Hkv} B={case.B} P={partition_size}")
+    decode_inputs(case.block_tables, case.context_lens, case.B, case.NB, case.max_context_len)
     kp, vp = dev(case.k_pool), dev(case.v_pool)
     got, slots = decode_step(pa, case, kp, vp, partition_size)
     ref, ref_slots = oracle_step(case, case.k_pool, case.v_pool)

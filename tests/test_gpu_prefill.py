@@ -9,6 +9,7 @@ import pytest
 import oracle
 import workloads as W
 from gpu_util import assert_attention_close, dev, host, pa_module, say, u16
+from host_validate import prefill_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -37,6 +38,7 @@ def ref(c, k_pool=None, v_pool=None, tables=None):
 
 def check(pa, c):
     say(c.name, f"S={c.S} T={c.T} Hq={c.Hq} Hkv={c.Hkv} B={c.B} new={c.new_lens.tolist()}")
+    prefill_inputs(c.block_tables, c.context_lens, c.query_start, c.T, c.B, c.NB, c.max_query_len)
     return assert_attention_close(run(pa, c), ref(c), c.name)
 
 

@@ -25,8 +25,8 @@
 // Instruction budget. A wave issues at most one instruction per turn on its
 // SIMD, so every scalar or vector instruction around the 16 matrix products of
 // a 32-key step costs issue slots the products need. Each wave loads one pool
-// (K or V) of one unit of every chunk, with per-lane offsets that never
-// change: per chunk it computes one unit's base address and valid length. The
+// (K or V) of half the units of every chunk, with per-lane offsets that never
+// change: per chunk it computes those units' base addresses and valid lengths. The
 // block table is read with a vector load (scalar loads share their wait
 // counter with LDS reads, so every operand wait would also wait for them),
 // and chunks that every row of the workgroup sees in full run through a loop
@@ -46,8 +46,9 @@
 //            address of lane 4e + i / 4 as its element e). Lane l ends with
 //            O[row m][dims 16n + 4kq + r].
 // Every per-row softmax quantity (running max, sum, rescale factor) lives in
-// the lanes of that row, so the only cross-lane steps are the two row-max
-// exchanges per chunk and the final sum.
+// the lanes of that row, so the only cross-lane steps are the row-max
+// exchanges when a row's running maximum must be raised (rare) and the final
+// sum.
 //
 // LDS layout: a chunk is KC token rows of 256 bytes for K and for V, each row
 // split into 16 pieces of 16 bytes. Piece c of row r is stored at position

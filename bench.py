@@ -63,6 +63,10 @@ def parse():
                     help="other workloads: input copies rotated over steps (0 = enough to "
                          "exceed the 256 MB last-level cache; 1 = cache-warm)")
     ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--graph", action="store_true",
+                    help="decode workloads: capture each input set's step (all layers: slot "
+                         "mapping, K/V store, decode) in a HIP graph and time graph replays; the "
+                         "per-call roofline events stay eager")
     ap.add_argument("--prompts", type=int, default=16, help="prefill workload: prompts per step")
     ap.add_argument("--cpu-sample-layers", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -519,8 +523,23 @@ def main():
             if events is not None:
                 events[i][1].record(stream)
 
+    graphs = None
+    if args.graph:
+        # one graph per input set, captured after an eager run of every set
+        for k in range(len(steps_inputs)):
+            step(k)
+        torch.cuda.synchronize()
+        graphs = []
+        for k in range(len(steps_inputs)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(k)
+            graphs.append(g)
+        torch.cuda.synchronize()
+    run_step = (lambda k: graphs[k % len(graphs)].replay()) if graphs else step
+
     for k in range(args.warmup):
-        step(k)
+        run_step(k)
     torch.cuda.synchronize()
 
     # timed region: K whole steps
@@ -528,7 +547,7 @@ def main():
     torch.cuda.synchronize()
     start.record(stream)
     for k in range(args.steps):
-        step(k)
+        run_step(k)
     end.record(stream)
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / args.steps
@@ -566,6 +585,7 @@ def main():
         "head_dim": c0.D, "block_size": c0.B, "pool_blocks_per_layer": c0.NB,
         "tokens_per_layer": int(c0.context_lens.sum()), "max_context": maxL, "partition_size": P,
         "kv_bytes_per_step": int(kv_bytes_step),
+        "launch": "HIP graph replay per step" if graphs else "eager calls",
     }
     if "replicas" in extra:
         config["input_replicas_rotated"] = extra["replicas"]

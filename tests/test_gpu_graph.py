@@ -1,0 +1,86 @@
+"""Decode and prefill steps captured in a HIP graph (torch.cuda.CUDAGraph around
+the binding's calls, which launch on torch's current stream) replay bit for bit
+like the same calls run eagerly. Each replay follows eager work on the same
+buffers (the output is cleared and the pool entries the step writes are
+overwritten), so a replay that reused stale state would show."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_util import assert_attention_close, dev, host, pa_module, say, u16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pa():
+    return pa_module()
+
+
+def test_decode_step_replays_bit_identical(pa):
+    import torch
+    c = W.seven_b_single_layer()
+    say(c.name, "decode step in a graph")
+    kp, vp = dev(c.k_pool), dev(c.v_pool)
+    tables, lens = dev(c.block_tables), dev(c.context_lens)
+    q, k_new, v_new = dev(c.query), dev(c.key_new), dev(c.value_new)
+    P = 256                                   # several partitions: the reduce kernel and workspace are in the graph
+    ws = torch.empty(max(pa.pa_decode_workspace_bytes(c.S, c.Hq, c.Hkv, c.D, c.B,
+                                                      c.max_context_len, P), 16),
+                     dtype=torch.uint8, device="cuda")
+    slots = torch.empty(c.S, dtype=torch.int64, device="cuda")
+    out = torch.empty_like(q)
+
+    def step():
+        pa.pa_slot_mapping(tables, c.B, c.NB, context_lens=lens, out=slots)
+        pa.pa_write_kv(k_new, v_new, kp, vp, slots)
+        pa.pa_decode(q, kp, vp, tables, lens, c.max_context_len, c.scale, partition_size=P,
+                     out=out, workspace=ws)
+
+    step()
+    eager = host(out).copy()
+    ref = oracle.decode(c.query, *oracle.write_kv(c.k_pool, c.v_pool, c.key_new, c.value_new,
+                                                  oracle.decode_slots(c.block_tables, c.context_lens,
+                                                                      c.B, c.NB)),
+                        c.block_tables, c.context_lens, c.scale)
+    assert_attention_close(eager, ref, "eager decode")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for r in range(3):
+        out.zero_()
+        slots.fill_(-1)
+        kp.view(-1)[:4096].zero_()            # unrelated eager writes to the pool between replays
+        kp.view(-1)[:4096] = dev(c.k_pool).view(-1)[:4096]
+        g.replay()
+        got = host(out)
+        assert np.array_equal(u16(got), u16(eager)), f"replay {r}"
+        assert np.array_equal(host(slots), oracle.decode_slots(c.block_tables, c.context_lens, c.B, c.NB))
+
+
+def test_prefill_step_replays_bit_identical(pa):
+    import torch
+    c = W.make_prefill_case("graph_prefill", 3900, [70, 200, 9], [30, 0, 300], Hq=8, Hkv=2, B=16)
+    say(c.name, "prefill in a graph")
+    kp, vp = dev(c.k_pool), dev(c.v_pool)
+    args = (dev(c.query), kp, vp, dev(c.block_tables), dev(c.context_lens), dev(c.query_start))
+    out = torch.empty_like(args[0])
+
+    def step():
+        pa.pa_prefill(*args, c.max_query_len, c.scale, out=out)
+
+    step()
+    eager = host(out).copy()
+    assert_attention_close(eager, oracle.prefill(c.query, c.k_pool, c.v_pool, c.block_tables,
+                                                 c.context_lens, c.query_start, c.scale),
+                           "eager prefill")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for r in range(3):
+        out.fill_(7.0)
+        g.replay()
+        assert np.array_equal(u16(host(out)), u16(eager)), f"replay {r}"

@@ -78,11 +78,11 @@ def test_long_context_b32(pa):
     say(c.name, "device pools")
     kp, vp = W.device_pools(c.NB, c.Hkv, c.B, c.D, seed=c.seed * 1000)
     c.k_pool, c.v_pool = host(kp), host(vp)
-    for P in (0, 1024):
+    ref, _ = oracle_step(c, c.k_pool, c.v_pool)
+    for P in (0, 512, 1024):          # 512: 8 partitions per sequence
         kp2, vp2 = kp.clone(), vp.clone()
         say(c.name, f"P={P}")
         got, _ = decode_step(pa, c, kp2, vp2, P)
-        ref, _ = oracle_step(c, c.k_pool, c.v_pool)
         assert_attention_close(got, ref, f"long_context P={P}")
 
 

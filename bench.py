@@ -20,6 +20,13 @@ time. `roofline` prices one pa_decode call (partition + reduce kernels), timed
 with HIP events on the stream it runs on, against 8 TB/s. `cpu_baseline` times
 the CPU oracle on a bounded sample of the same workload.
 
+Prefill (`--workload prefill`: 16 chat prompts, nothing cached; `--workload
+prefix_prefill`: 64 suffixes after a shared cached prompt, grouped heads) times
+the prompt tokens' K/V stores and pa_prefill per step and prices the pa_prefill
+launch against the fp16 matrix-core peak. `--workload swap` and
+`--workload block_manager` time pa_swap_blocks and the host block manager.
+`--graph` replays each decode step as a HIP graph.
+
     python bench.py [--workload chat] [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
 from __future__ import annotations
@@ -53,7 +60,7 @@ def parse():
                          "ramped up before the timed region)")
     ap.add_argument("--workload", default="chat",
                     choices=["chat", "7b", "shared_prefix", "long_context", "tiny", "block_manager",
-                             "swap", "prefill"])
+                             "swap", "prefill", "prefix_prefill"])
     ap.add_argument("--layers", type=int, default=32, help="chat workload: layers per step")
     ap.add_argument("--block-size", type=int, default=16, help="chat workload: tokens per block")
     ap.add_argument("--contiguous", action="store_true",
@@ -74,7 +81,7 @@ def parse():
                     help="after timing, run one plain device-to-device copy of this many MiB "
                          "(a copy of known size for scaling traffic counters)")
     args = ap.parse_args()
-    short = args.workload == "prefill"
+    short = args.workload in ("prefill", "prefix_prefill")
     if args.steps is None:
         args.steps = 50 if short else 10
     if args.warmup is None:
@@ -433,26 +440,113 @@ def bench_prefill(args):
         "cpu_baseline": cpu}), flush=True)
 
 
-def cpu_baseline_prefill(c, flops_total):
-    """Oracle attention (fp64, numpy) for 48 evenly spaced new tokens of every
+def cpu_baseline_prefill(c, flops_total, rows=48):
+    """Oracle attention (fp64, numpy) for `rows` evenly spaced new tokens of every
     prompt, every head, over the keys each one sees; rate = their flops / time."""
     import oracle
     t_total, f_total = 0.0, 0
+    group = c.Hq // c.Hkv
     for s in range(c.S):
         L, n, q0 = int(c.context_lens[s]), int(c.new_lens[s]), int(c.query_start[s])
+        if n == 0:
+            continue
         t = time.perf_counter()
         K = oracle.gather(c.k_pool, c.block_tables[s], L, c.B)
         V = oracle.gather(c.v_pool, c.block_tables[s], L, c.B)
-        for j in np.linspace(0, n - 1, 48).astype(int):
+        for j in np.linspace(0, n - 1, rows).astype(int):
             p = L - n + int(j)
             for h in range(c.Hq):
-                oracle.attend(c.query[q0 + j, h], K[h, :p + 1], V[h, :p + 1], c.scale)
+                oracle.attend(c.query[q0 + j, h], K[h // group, :p + 1], V[h // group, :p + 1], c.scale)
             f_total += 4 * c.D * c.Hq * (p + 1)
         t_total += time.perf_counter() - t
     return {"value": round(f_total / t_total / 1e12, 6), "unit": "TFLOP/s",
             "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
-            "sample": f"oracle attention of 48 evenly spaced new tokens per prompt x {c.Hq} heads "
-                      f"({c.S * 48 * c.Hq} rows, {f_total / 1e9:.2f} GFLOP), {t_total:.1f} s"}
+            "sample": f"oracle attention of {rows} evenly spaced new tokens per prompt x {c.Hq} heads "
+                      f"({c.S * rows * c.Hq} rows, {f_total / 1e9:.2f} GFLOP), {t_total:.1f} s"}
+
+
+def bench_prefix_prefill(args):
+    """The shared-prefix flow as prefill (grouped heads 32/8, B = 16): 64
+    sequences share a cached 500-token prompt; per step, one pa_copy_blocks
+    call (each sequence's private copy of the partly filled prompt block), the
+    suffix tokens' slots and K/V stores, and pa_prefill over the 64 suffixes
+    (U[50, 500] new tokens each, attending to the prompt and their own tokens)."""
+    import torch
+    import oracle
+    import paged_kv_cache_151_amd as pa
+    import workloads as W
+    torch.cuda.set_device(0)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    t0 = time.time()
+    d = W.prefix_prefill()
+    S, B, NB = d["S"], d["B"], d["NB"]
+    seq = np.concatenate([np.full(n, s, np.int32) for s, n in enumerate(d["new_lens"])])
+    pos = np.concatenate([np.arange(d["prefix_len"], L, dtype=np.int32) for L in d["context_lens"]])
+    kp, vp = dev(d["k_pool"]), dev(d["v_pool"])
+    tables, lens, qs = dev(d["tables"]), dev(d["context_lens"]), dev(d["query_start"])
+    pairs, q = dev(d["copy_pairs"]), dev(d["prefill_query"])
+    ks, vs = dev(np.concatenate(d["suffix_k"])), dev(np.concatenate(d["suffix_v"]))
+    seq_d, pos_d = dev(seq), dev(pos)
+    slots = torch.empty(len(seq), dtype=torch.int64, device="cuda")
+    out = torch.empty_like(q)
+    maxq = int(d["new_lens"].max())
+    stream = torch.cuda.current_stream()
+    flops = prefill_flops(d["new_lens"], d["context_lens"], d["Hq"], d["D"])
+    log(f"setup {time.time() - t0:.1f}s: prefix prefill, T={len(seq)}, NB={NB}, {flops / 1e9:.1f} GFLOP")
+
+    def step(ev=None):
+        pa.pa_copy_blocks(kp, vp, pairs)
+        pa.pa_slot_mapping(tables, B, NB, seq_ids=seq_d, positions=pos_d, out=slots)
+        pa.pa_write_kv(ks, vs, kp, vp, slots)
+        if ev is not None:
+            ev[0].record(stream)
+        pa.pa_prefill(q, kp, vp, tables, lens, qs, maxq, d["scale"], out=out)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for e in ev:
+        step(e)
+    torch.cuda.synchronize()
+    launch_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    achieved = flops / (launch_ms * 1e-3) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        rk, rv = oracle.copy_blocks(d["k_pool"], d["v_pool"], d["copy_pairs"])
+        rk, rv = oracle.write_kv(rk, rv, np.concatenate(d["suffix_k"]), np.concatenate(d["suffix_v"]),
+                                 oracle.token_slots(d["tables"], seq, pos, B, NB))
+        c = W.PrefillCase(name="prefix_prefill", seed=4, S=S, Hq=d["Hq"], Hkv=d["Hkv"], D=d["D"], B=B,
+                          NB=NB, context_lens=d["context_lens"], new_lens=d["new_lens"],
+                          query_start=d["query_start"], block_tables=d["tables"],
+                          query=d["prefill_query"], k_pool=rk, v_pool=rv, scale=d["scale"])
+        cpu = cpu_baseline_prefill(c, flops, rows=12)
+    print(json.dumps({
+        "metric": "paged-prefill attention TFLOP/s (% of fp16 MFMA peak) + prompt tokens/s",
+        "value": round(flops / (ms_per_step * 1e-3) / 1e12, 1), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "accumulate": "f32", "data": "synthetic",
+        "prompt_tokens_per_s": round(len(seq) / (ms_per_step * 1e-3), 1),
+        "config": {"workload": "prefix prefill: 64 suffixes of U[50,500] tokens after a shared cached "
+                               "500-token prompt, 32 query / 8 KV heads x 128 dims fp16, B=16",
+                   "prompts": S, "new_tokens": len(seq), "max_new": maxq, "pool_blocks": NB,
+                   "flops_per_step": int(flops)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_F16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
+                     "traffic": None, "kernel": "pa_prefill (one launch per step)",
+                     "avg_launch_us": round(launch_ms * 1e3, 2), "flops_per_launch": int(flops)},
+        "cpu_baseline": cpu}), flush=True)
 
 
 def main():
@@ -464,6 +558,9 @@ def main():
         sys.exit(2)
     if args.workload == "prefill":
         bench_prefill(args)
+        return
+    if args.workload == "prefix_prefill":
+        bench_prefix_prefill(args)
         return
     if args.workload == "block_manager":
         bench_block_manager(args)

@@ -96,25 +96,27 @@ struct Flag {
 };
 
 // 16-byte buffer load of each lane into LDS: lane i's bytes land at dst + 16 i
-// (lanes past the resource's range write zeros); the second form marks the
-// load non-temporal. Kept out of the kernel template: the host pass must not
-// see the LDS pointer argument inside it.
+// (lanes past the resource's range write zeros). Plain cache policy: the row
+// blocks of one sequence and KV head read the same chunks side by side on one
+// XCD, and its L2 serves the repeats (the non-temporal hint measured 3 %
+// slower). Kept out of the kernel template: the host pass must not see the
+// LDS pointer argument inside it.
 __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, lds_u8* dst, unsigned voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff,
                                            0, 0, 0);
-}
-__device__ __forceinline__ void load_lds16_nt(__amdgpu_buffer_rsrc_t r, lds_u8* dst,
-                                              unsigned voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff,
-                                           0, 0, 2);
 }
 
 // vmcnt(n): wait until at most n vector memory operations of this wave are
 // outstanding (gfx9 encoding; lgkmcnt and expcnt left at their maximum).
 #define PA_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0F70)
+// lgkmcnt(0): every LDS read this wave issued has returned its data (vmcnt and
+// expcnt left at their maximum).
+#define PA_WAIT_LDS() __builtin_amdgcn_s_waitcnt(0xC07F)
 
-template <int BT, int G, int QT, int NW, int KC, bool NT>
-__global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
+// Three waves per SIMD (at most 168 VGPRs; one row tile fits in about 150).
+template <int BT, int G, int QT, int NW, int KC>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(QT == 1 ? 3 : 1)))
+void prefill_kernel(const PrefillArgs a) {
   constexpr int D = kHeadDim;
   constexpr int HW = G < NW ? G : NW;      // query heads in a workgroup
   constexpr int RW = NW / HW;              // row tiles per head in a workgroup
@@ -206,8 +208,6 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
   kend = kend > L ? L : kend;
   kend = kend < 0 ? 0 : kend;
   const int nchunk = wave_rows ? (kend + KC - 1) / KC : 0;
-  int nfull = base_pos + j0 + 1 >= 0 ? (base_pos + j0 + 1) / KC : 0;
-  nfull = nfull > nchunk ? nchunk : nfull;
 
   // query rows as B operands
   h8 qf[QT][4];
@@ -287,15 +287,13 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           lds_u8* dst = vst(st) + w_lds + (j * kUnitTok + 4 * i) * kRowBytes;
-          if (NT) load_lds16_nt(r, dst, voff[i]);
-          else load_lds16(r, dst, voff[i]);
+          load_lds16(r, dst, voff[i]);
         }
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           lds_u8* dst = kst(st) + w_lds + (j * kUnitTok + 4 * i) * kRowBytes;
-          if (NT) load_lds16_nt(r, dst, voff[i]);
-          else load_lds16(r, dst, voff[i]);
+          load_lds16(r, dst, voff[i]);
         }
       }
     }
@@ -394,17 +392,25 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
   };
 
   // Pipeline over three LDS stages: chunk k goes to stage k % 3. Iteration
-  // c: wait for this wave's loads of chunk c and its table read for chunk
-  // c + 2 (the loads of chunk c + 1 may still be in flight), barrier (every
-  // wave's part of chunk c is in LDS and every wave has finished chunk c - 1),
-  // read chunk c + 2's entries, start the table read for chunk c + 3 and the
-  // loads of chunk c + 2 into the stage chunk c - 1 used, compute chunk c.
+  // c: wait until this wave's LDS reads have returned their data and its
+  // loads of chunk c and table read for chunk c + 2 are done (the loads of
+  // chunk c + 1 may still be in flight), barrier (every wave's part of chunk
+  // c is in LDS, and no wave still reads the stage of chunk c - 1), read chunk
+  // c + 2's entries, start the table read for chunk c + 3 and the loads of
+  // chunk c + 2 into the stage chunk c - 1 used, compute chunk c.
+  // The LDS wait is explicit: the barrier instruction does not wait for
+  // outstanding reads, and the compiler is free to schedule the value products
+  // of chunk c - 1, with the waits for their operand reads, below the barrier;
+  // the scheduling fence keeps those reads above the wait. Without it a wave
+  // could still be reading a stage when another wave's loads refill it.
   // Both loops are unrolled three times so that every stage index is a
   // compile-time constant. The first runs the chunks every row sees in full
   // (all waves, no mask); the second the rest, where a wave masks the keys
-  // beyond its rows and skips chunks past them. Every wave runs the same
-  // iterations (barriers). Past the last chunk the loads have an empty range:
-  // no memory is read, the stage is filled with zeros.
+  // beyond its rows (one masked code path: a second, unmasked copy there
+  // costs the registers of a third wave per SIMD) and skips chunks past them.
+  // Every wave runs the same iterations (barriers). Past the last chunk the
+  // loads have an empty range: no memory is read, the stage is filled with
+  // zeros.
   if (nchunk_wg > 0) {
     int ph[NU];
     int tv = table_load(0);
@@ -420,6 +426,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
     tv = table_load(2);
     // every row sees chunk c in full, every wave computes it
     auto fast = [&](int c, int st) {
+      __builtin_amdgcn_sched_barrier(0);
+      PA_WAIT_LDS();
       PA_WAIT_VM(NP);
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
@@ -430,6 +438,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
       compute(st, c, Flag<false>{});
     };
     auto step = [&](int c, int st) {
+      __builtin_amdgcn_sched_barrier(0);
+      PA_WAIT_LDS();
       PA_WAIT_VM(NP);
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
@@ -437,10 +447,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
       tv = table_load(c + 3);
       __builtin_amdgcn_sched_barrier(0);
       load_chunk(c + 2, (st + 2) % 3, ph);
-      if (c < nchunk) {
-        if (c >= nfull) compute(st, c, Flag<true>{});
-        else compute(st, c, Flag<false>{});
-      }
+      if (c < nchunk) compute(st, c, Flag<true>{});
     };
     int c = 0;
     for (; c < nfast; c += 3) {
@@ -482,7 +489,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillArgs a) {
 
 template <int BT, int G>
 hipError_t launch_g(const PrefillArgs& a, int64_t grid, hipStream_t stream) {
-  prefill_kernel<BT, G, kPrefillRowTiles, kPrefillWaves, kPrefillChunk, kDecodeNontemporal>
+  prefill_kernel<BT, G, kPrefillRowTiles, kPrefillWaves, kPrefillChunk>
       <<<(unsigned)grid, kPrefillWaves * 64, 0, stream>>>(a);
   return hipGetLastError();
 }

@@ -7,8 +7,8 @@ namespace pa {
 
 // Query row tiles of 16 per prefill wave. More rows per wave read each
 // staged key/value chunk from LDS for more rows, but hold more registers: one
-// tile fits in about 215 VGPRs (two waves per SIMD); two tiles need about 300
-// (one wave per SIMD), and held to 256 they spill and measured 30 % slower.
+// tile fits in about 150 VGPRs (three waves per SIMD); two tiles need about
+// 300 (one wave per SIMD), and held to 256 they spill and measured 30 % slower.
 #ifndef PA_PREFILL_ROW_TILES
 #define PA_PREFILL_ROW_TILES 1
 #endif

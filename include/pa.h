@@ -260,7 +260,7 @@ pa_status pa_decode(void* out, const void* query, const void* k_pool, const void
  *   query_start       device int32 [S + 1], non-decreasing, query_start[S] <= T
  *   max_query_len     host bound on every n_s (sizes the launch)
  *   scale             softmax scale, finite and >= 0, usually 1/sqrt(D)
- * Supported: D = 128; B a multiple of 16; Hq / Hkv in {1, 2, 4, 8}. S = 0 or
+ * Supported: D = 128; B = 8 or a multiple of 16; Hq / Hkv in {1, 2, 4, 8}. S = 0 or
  * max_query_len = 0 is a no-op. Caller errors the kernel can see are contained,
  * never an access outside the buffers: a sequence whose query range leaves
  * [0, T] is skipped, L_s is clamped to [0, MB * B], a sequence with

@@ -346,8 +346,8 @@ pa_status pa_prefill(void* out, const void* query, const void* k_pool, const voi
     return fail(PA_ERR_SHAPE, "pa_prefill: max_query_len=%d outside [0, T=%d]", max_query_len, T);
   const int G = Hq / Hkv;
   if (D != pa::kHeadDim) return fail(PA_ERR_UNSUPPORTED, "pa_prefill: D=%d (supported: 128)", D);
-  if (B % pa::kDecodeUnit)
-    return fail(PA_ERR_UNSUPPORTED, "pa_prefill: B=%d (supported: multiples of %d)", B,
+  if (B != 8 && B % pa::kDecodeUnit)
+    return fail(PA_ERR_UNSUPPORTED, "pa_prefill: B=%d (supported: 8 or multiples of %d)", B,
                 pa::kDecodeUnit);
   if (G != 1 && G != 2 && G != 4 && G != 8)
     return fail(PA_ERR_UNSUPPORTED, "pa_prefill: Hq/Hkv=%d (supported: 1, 2, 4, 8)", G);

@@ -148,7 +148,11 @@ void prefill_kernel(const PrefillArgs a) {
     return st == 0 ? (lds_u8*)s_v0 : st == 1 ? (lds_u8*)s_v1 : (lds_u8*)s_v2;
   };
   const int B = BT > 0 ? BT : a.B;
-  const int UPB = B / kUnitTok;
+  // B = 8: a 16-token unit spans two blocks (two half tiles of 2 KiB), so it
+  // takes two table entries and two buffer resources.
+  constexpr bool kSplit = BT == 8;
+  constexpr int NE = kSplit ? 2 : 1;       // table entries per unit
+  const int UPB = kSplit ? 1 : B / kUnitTok;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -244,6 +248,10 @@ void prefill_kernel(const PrefillArgs a) {
   const __amdgpu_buffer_rsrc_t trs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int32_t*>(a.tables + (int64_t)s * a.MB), 0, nblk * 4, kRsrcWord3);
   auto table_load = [&](int chunk) -> int {
+    if constexpr (kSplit) {   // lane 2u + h reads the block of half h of unit u
+      const int e = 2 * NU * chunk + (lane < 2 * NU ? lane : 0);
+      return __builtin_amdgcn_raw_buffer_load_b32(trs, (unsigned)e * 4u, 0, 0);
+    }
     const int U = NU * chunk + (lane < NU ? lane : 0);
     return __builtin_amdgcn_raw_buffer_load_b32(trs, (unsigned)(U / UPB) * 4u, 0, 0);
   };
@@ -269,17 +277,43 @@ void prefill_kernel(const PrefillArgs a) {
   const uint32_t blk_bytes = (uint32_t)a.Hkv * (uint32_t)B * kRowBytes;   // one block, all heads
   const unsigned char* pg = (const unsigned char*)(w_is_v ? a.v_pool : a.k_pool) + (size_t)g * B * kRowBytes;
   const int w_lds = w_u0 * kUnitTok * kRowBytes;
-  auto load_chunk = [&](int c, int st, const int (&ph)[NU]) {
+  auto load_chunk = [&](int c, int st, const int (&ph)[NE * NU]) {
 #pragma unroll
     for (int j = 0; j < UW; ++j) {
       const int U = NU * c + w_u0 + j;
-      const int valid = L - U * kUnitTok < kUnitTok ? L - U * kUnitTok : kUnitTok;
-      const int nbytes = U * kUnitTok < kend_wg ? valid * kRowBytes : 0;
-      const int phys = ph[w_u0 + j];
-      const uint32_t safe = (unsigned)phys < (unsigned)a.NB ? (uint32_t)phys : 0u;
-      const uint64_t off = (uint64_t)safe * blk_bytes + (uint32_t)((U % UPB) * kUnitTok * kRowBytes);
-      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<unsigned char*>(pg + off), 0, nbytes, kRsrcWord3);
+      // one resource and offset per row group (rows 4i .. 4i + 3 of the unit)
+      __amdgpu_buffer_rsrc_t rs[4];
+      unsigned vo[4];
+      if constexpr (kSplit) {
+        // half h holds unit tokens 8h .. 8h + 7: row groups 2h and 2h + 1
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int t0 = U * kUnitTok + 8 * h;
+          const int valid = L - t0 < 8 ? L - t0 : 8;
+          const int nbytes = t0 < kend_wg ? valid * kRowBytes : 0;
+          const int phys = ph[2 * (w_u0 + j) + h];
+          const uint32_t safe = (unsigned)phys < (unsigned)a.NB ? (uint32_t)phys : 0u;
+          const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+              const_cast<unsigned char*>(pg + (uint64_t)safe * blk_bytes), 0, nbytes, kRsrcWord3);
+          rs[2 * h] = r;
+          rs[2 * h + 1] = r;
+          vo[2 * h] = voff[2 * h] - h * 8 * kRowBytes;
+          vo[2 * h + 1] = voff[2 * h + 1] - h * 8 * kRowBytes;
+        }
+      } else {
+        const int valid = L - U * kUnitTok < kUnitTok ? L - U * kUnitTok : kUnitTok;
+        const int nbytes = U * kUnitTok < kend_wg ? valid * kRowBytes : 0;
+        const int phys = ph[w_u0 + j];
+        const uint32_t safe = (unsigned)phys < (unsigned)a.NB ? (uint32_t)phys : 0u;
+        const uint64_t off = (uint64_t)safe * blk_bytes + (uint32_t)((U % UPB) * kUnitTok * kRowBytes);
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<unsigned char*>(pg + off), 0, nbytes, kRsrcWord3);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          rs[i] = r;
+          vo[i] = voff[i];
+        }
+      }
       // The branch is uniform; each side names its LDS array at compile time.
       // (With the array chosen at run time the compiler cannot tell which
       // stage a load writes and waits for every load before any LDS read.)
@@ -287,13 +321,13 @@ void prefill_kernel(const PrefillArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           lds_u8* dst = vst(st) + w_lds + (j * kUnitTok + 4 * i) * kRowBytes;
-          load_lds16(r, dst, voff[i]);
+          load_lds16(rs[i], dst, vo[i]);
         }
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           lds_u8* dst = kst(st) + w_lds + (j * kUnitTok + 4 * i) * kRowBytes;
-          load_lds16(r, dst, voff[i]);
+          load_lds16(rs[i], dst, vo[i]);
         }
       }
     }
@@ -412,11 +446,11 @@ void prefill_kernel(const PrefillArgs a) {
   // loads have an empty range: no memory is read, the stage is filled with
   // zeros.
   if (nchunk_wg > 0) {
-    int ph[NU];
+    int ph[NE * NU];
     int tv = table_load(0);
     auto entries = [&]() {
 #pragma unroll
-      for (int u = 0; u < NU; ++u) ph[u] = __builtin_amdgcn_readlane(tv, u);
+      for (int u = 0; u < NE * NU; ++u) ph[u] = __builtin_amdgcn_readlane(tv, u);
     };
     entries();
     load_chunk(0, 0, ph);
@@ -528,6 +562,7 @@ hipError_t launch_prefill(const PrefillArgs& a, int B, int G, int max_query_len,
   const int64_t grid = 8 * b.per_xcd;
   if (b.n_work == 0) return hipSuccess;
   switch (B) {
+    case 8: return launch_bt<8>(b, G, grid, stream);
     case 16: return launch_bt<16>(b, G, grid, stream);
     case 32: return launch_bt<32>(b, G, grid, stream);
     default: return launch_bt<0>(b, G, grid, stream);

@@ -144,7 +144,8 @@ def test_prefill_host_validation(lib):
     assert prefill(lib, qs=None) == PA_ERR_NULL
     assert prefill(lib, Hq=6, Hkv=4) == PA_ERR_SHAPE
     assert prefill(lib, D=64) == PA_ERR_UNSUPPORTED
-    assert prefill(lib, B=8, MB=6) == PA_ERR_UNSUPPORTED
+    assert prefill(lib, B=24, MB=2) == PA_ERR_UNSUPPORTED
+    assert prefill(lib, B=8, MB=6, out=None) == PA_ERR_NULL     # B = 8 passes validation
     assert prefill(lib, Hq=12, Hkv=4) == PA_ERR_UNSUPPORTED    # group of 3
     assert prefill(lib, maxq=41) == PA_ERR_SHAPE               # more rows than T
     assert prefill(lib, maxq=-1) == PA_ERR_SHAPE

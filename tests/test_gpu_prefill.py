@@ -1,6 +1,6 @@
 """Parity of pa_prefill (HIP, MFMA) against the fp64 CPU oracle: ragged chunks of
 new tokens with and without a cached prefix, every grouped-query size, block
-sizes 16/32/48, the shared-prefix flow (copy-on-write, suffix writes, prefill),
+sizes 8/16/32/48, the shared-prefix flow (copy-on-write, suffix writes, prefill),
 and the invariants that hold bit for bit on the GPU (relabelling blocks,
 poison in unused slots, chunked versus one-pass prefill)."""
 import numpy as np
@@ -46,7 +46,7 @@ NEW = [1, 15, 16, 17, 33, 64, 65, 130]
 CACHED = [0, 0, 5, 100, 0, 31, 16, 7]
 
 
-@pytest.mark.parametrize("B", [16, 32, 48])
+@pytest.mark.parametrize("B", [8, 16, 32, 48])
 @pytest.mark.parametrize("G", [1, 2, 4, 8])
 def test_ragged_chunks_all_groups_and_block_sizes(pa, G, B):
     c = W.make_prefill_case(f"ragged_G{G}_B{B}", 3000 + 10 * G + B, NEW, CACHED,
@@ -93,8 +93,9 @@ def test_relabelling_physical_blocks_is_bit_identical(pa):
 
 
 @pytest.mark.parametrize("poison", [np.float16(np.nan), np.float16(np.inf)])
-def test_unused_slots_and_blocks_never_reach_the_output(pa, poison):
-    c = W.make_prefill_case("poison", 3400, [40, 77], [3, 0], Hq=4, Hkv=2, B=32)
+@pytest.mark.parametrize("B", [32, 8])
+def test_unused_slots_and_blocks_never_reach_the_output(pa, poison, B):
+    c = W.make_prefill_case(f"poison_B{B}", 3400 + (B == 8), [40, 77], [3, 0], Hq=4, Hkv=2, B=B)
     clean = run(pa, c)
     kp, vp = c.k_pool.copy(), c.v_pool.copy()
     used = np.zeros(c.NB, bool)
@@ -110,6 +111,40 @@ def test_unused_slots_and_blocks_never_reach_the_output(pa, poison):
     vp[~used] = poison
     dirty = run(pa, c, kp, vp)
     assert np.array_equal(u16(dirty), u16(clean))
+
+
+def relayout(c, B):
+    """The same logical keys and values in a fresh pool of block size B (blocks
+    handed out in order), with the case's queries."""
+    rows = [oracle.blocks_for(int(L), B) for L in c.context_lens]
+    NB = sum(rows) + 1
+    tables = np.full((c.S, max(rows)), -1, np.int32)
+    kp = np.zeros((NB, c.Hkv, B, c.D), np.float16)
+    vp = np.zeros_like(kp)
+    nxt = 0
+    for s, L in enumerate(c.context_lens.tolist()):
+        K = oracle.gather(c.k_pool, c.block_tables[s], L, c.B)
+        V = oracle.gather(c.v_pool, c.block_tables[s], L, c.B)
+        for j in range(rows[s]):
+            tables[s, j] = nxt
+            n = min(B, L - j * B)
+            kp[nxt, :, :n] = K[:, j * B:j * B + n]
+            vp[nxt, :, :n] = V[:, j * B:j * B + n]
+            nxt += 1
+    return W.PrefillCase(**{**c.__dict__, "name": f"{c.name}_as_B{B}", "B": B, "NB": NB,
+                            "block_tables": tables, "k_pool": kp, "v_pool": vp})
+
+
+@pytest.mark.parametrize("G", [1, 4])
+def test_block_size_8_is_bit_identical_to_16(pa, G):
+    # a 16-token unit of the kernel is then two blocks; the staged keys and
+    # values, and so every output bit, are those of the same tokens at B = 16
+    c16 = W.make_prefill_case(f"b8_vs_b16_G{G}", 3450 + G, [1, 9, 16, 40, 77, 130],
+                              [0, 8, 7, 16, 3, 100], Hq=2 * G, Hkv=2, B=16)
+    c8 = relayout(c16, 8)
+    check(pa, c16)
+    check(pa, c8)
+    assert np.array_equal(u16(run(pa, c8)), u16(run(pa, c16)))
 
 
 def test_empty_and_out_of_range_sequences_leave_their_rows_alone(pa):

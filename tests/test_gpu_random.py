@@ -56,7 +56,7 @@ def test_random_prefill_shapes(pa, seed):
     rng = np.random.default_rng(7300 + seed)
     G = int(rng.choice([1, 2, 4, 8]))
     Hkv = int(rng.choice([1, 2]))
-    B = int(rng.choice([16, 32, 48, 64]))
+    B = int(rng.choice([8, 16, 32, 48, 64]))
     S = int(rng.integers(1, 8))
     new = [int(x) for x in rng.integers(0, 300, S)]
     new = [int(rng.choice([1, 15, 16, 17, 63, 64, 65])) if rng.random() < 0.3 else x for x in new]

@@ -225,23 +225,30 @@ pa_status pa_swap_blocks(void* dst_k_pool, void* dst_v_pool, const void* src_k_p
   return ok();
 }
 
+// Compute units of the MI355X: the default decode partition keeps at least
+// one workgroup per CU.
+constexpr int64_t kComputeUnits = 256;
+
 int pa_decode_partition_size(int S, int Hq, int Hkv, int B, int max_context_len,
                              int partition_size) {
   const int U = pa::kDecodeUnit;
   if (B <= 0 || partition_size < 0 || (partition_size > 0 && partition_size % U)) return -1;
   if (partition_size > 0) return partition_size;
   // Default: 1024 tokens (64 blocks of 16, one table chunk), halved while the
-  // launch would give fewer than 2048 waves (8 per CU), down to 64 tokens.
-  // Measured on MI355X: for the batch-128 chat workload 1024 beats 512 by 4 %
-  // (fewer partials, longer load streams per wave); for the 32/8-head shared
-  // prefix workload one 1024-token partition per sequence (no reduce) beats
-  // 512 by 20 %.
-  const int G = (Hkv > 0 && Hq >= Hkv && Hq % Hkv == 0) ? Hq / Hkv : 1;
-  const int64_t waves = pa::decode_waves(G);
+  // launch would have fewer workgroups than the MI355X has compute units
+  // (256), down to 64 tokens. Splitting a sequence further costs a reduce
+  // launch and more partials, which outweighs the extra parallelism once every
+  // CU has a workgroup. Measured on MI355X (one call replayed in a HIP graph):
+  // for the batch-128 chat workload 1024 beats 512 by 4 %; for the 32/8-head
+  // shared-prefix workload one 1024-token partition per sequence (no reduce)
+  // beats 512 by 20 %; for 8 sequences of at most 853 tokens x 32 heads one
+  // partition takes 19.3 us against 20.6 at 256 tokens; for one sequence of
+  // 4000 tokens x 32 heads 512 tokens take 17.5 us against 20.3 at 128.
+  (void)Hq;
   int P = 1024;
   const int64_t units = (int64_t)(S > 0 ? S : 1) * (Hkv > 0 ? Hkv : 1);
   const int maxL = max_context_len > 0 ? max_context_len : 1;
-  while (P > 4 * U && units * ceil_div(maxL, P) * waves < 2048) P /= 2;
+  while (P > 4 * U && units * ceil_div(maxL, P) < kComputeUnits) P /= 2;
   return P;
 }
 

@@ -123,56 +123,106 @@ def test_calls_with_zero_work_are_no_ops(pa):
     assert not host(kp).any()
 
 
+class Managed:
+    """The native block manager with device pools, and the oracle's manager with
+    host pools, stepped together: every token's slot and every copy pair of the
+    native manager drive pa_copy_blocks and pa_write_kv on the GPU, and must
+    equal what the oracle's manager decides for the same step."""
+
+    def __init__(self, pa, rng, NB, H, B, D):
+        self.pa, self.rng, self.H, self.D = pa, rng, H, D
+        kpool = W.f16_normal(rng, (NB, H, B, D))
+        vpool = W.f16_normal(rng, (NB, H, B, D))
+        self.kp, self.vp = dev(kpool), dev(vpool)
+        self.rk, self.rv = kpool, vpool
+        self.nat = pa.BlockManager(NB, B)
+        self.ref = oracle.BlockManager(NB, B)
+
+    def step(self, nat_ids, ref_tables):
+        """One token for each listed sequence: copies first, then the write."""
+        keys = W.f16_normal(self.rng, (len(nat_ids), self.H, self.D))
+        vals = W.f16_normal(self.rng, (len(nat_ids), self.H, self.D))
+        slots, copies = self.nat.append_tokens(nat_ids)
+        c0 = len(self.ref.copies)
+        ref_slots = [self.ref.append_token(t) for t in ref_tables]
+        assert slots.tolist() == ref_slots
+        assert [tuple(p) for p in copies.tolist()] == self.ref.copies[c0:]
+        if len(copies):
+            self.pa.pa_copy_blocks(self.kp, self.vp, dev(copies))
+            self.rk, self.rv = oracle.copy_blocks(self.rk, self.rv, copies)
+        self.pa.pa_write_kv(dev(keys), dev(vals), self.kp, self.vp, dev(slots))
+        self.rk, self.rv = oracle.write_kv(self.rk, self.rv, keys, vals, np.array(ref_slots))
+
+    def check_decode(self, nat_ids, ref_tables, MB, what):
+        """Pools bit-exact against the oracle, then decode over the sequences."""
+        from gpu_util import assert_attention_close
+        tables, lens = self.nat.export(nat_ids, MB)
+        assert np.array_equal(u16(host(self.kp)), u16(self.rk))
+        assert np.array_equal(u16(host(self.vp)), u16(self.rv))
+        q = W.f16_normal(self.rng, (len(nat_ids), self.H, self.D))
+        out = host(self.pa.pa_decode(dev(q), self.kp, self.vp, dev(tables), dev(lens),
+                                     int(lens.max()), 0.088))
+        want = oracle.decode(q, self.rk, self.rv,
+                             np.array([t + [-1] * (MB - len(t)) for t in ref_tables], np.int32),
+                             lens, 0.088)
+        assert_attention_close(out, want, what)
+        return tables, lens
+
+
 def test_native_block_manager_drives_the_device_path(pa):
     """Prompt -> fork into samples -> each sample generates tokens, all through
     the native manager (host), whose slots and copy pairs drive pa_copy_blocks,
     pa_write_kv and pa_decode on the GPU. The oracle replays the same steps
     with its own manager, write, copy and decode."""
-    rng = np.random.default_rng(77)
-    NB, H, B, D = 96, 4, 16, 128
-    kpool = W.f16_normal(rng, (NB, H, B, D))
-    vpool = W.f16_normal(rng, (NB, H, B, D))
-    kp, vp = dev(kpool), dev(vpool)
-    rk, rv = kpool, vpool
-    nat = pa.BlockManager(NB, B)
-    ref = oracle.BlockManager(NB, B)
-
-    def step(nat_ids, ref_tables):
-        """One token for each listed sequence: copies first, then the write."""
-        nonlocal rk, rv
-        keys = W.f16_normal(rng, (len(nat_ids), H, D))
-        vals = W.f16_normal(rng, (len(nat_ids), H, D))
-        slots, copies = nat.append_tokens(nat_ids)
-        c0 = len(ref.copies)
-        ref_slots = [ref.append_token(t) for t in ref_tables]
-        assert slots.tolist() == ref_slots
-        assert [tuple(p) for p in copies.tolist()] == ref.copies[c0:]
-        if len(copies):
-            pa.pa_copy_blocks(kp, vp, dev(copies))
-            rk, rv = oracle.copy_blocks(rk, rv, copies)
-        pa.pa_write_kv(dev(keys), dev(vals), kp, vp, dev(slots))
-        rk, rv = oracle.write_kv(rk, rv, keys, vals, np.array(ref_slots))
-
-    prompt = nat.add_sequence()
+    m = Managed(pa, np.random.default_rng(77), 96, 4, 16, 128)
+    prompt = m.nat.add_sequence()
     rprompt = []
     say("native manager: 37-token prompt, 5 samples, 21 steps")
     for _ in range(37):
-        step([prompt], [rprompt])
-    samples = [nat.fork(prompt) for _ in range(5)]
-    rsamples = [ref.fork(rprompt) for _ in range(5)]
-    nat.release(prompt)
-    ref.release(rprompt)
+        m.step([prompt], [rprompt])
+    samples = [m.nat.fork(prompt) for _ in range(5)]
+    rsamples = [m.ref.fork(rprompt) for _ in range(5)]
+    m.nat.release(prompt)
+    m.ref.release(rprompt)
     for _ in range(21):
-        step(samples, rsamples)
-    tables, lens = nat.export(samples, 6)
+        m.step(samples, rsamples)
+    _, lens = m.check_decode(samples, rsamples, 6, "managed samples")
     assert (lens == 37 + 21).all()
-    q = W.f16_normal(rng, (5, H, D))
-    out = host(pa.pa_decode(dev(q), kp, vp, dev(tables), dev(lens), int(lens.max()), 0.088))
-    assert np.array_equal(u16(host(kp)), u16(rk)) and np.array_equal(u16(host(vp)), u16(rv))
-    want = oracle.decode(q, rk, rv, np.array([t + [-1] * (6 - len(t)) for t in rsamples], np.int32),
-                         lens, 0.088)
-    from gpu_util import assert_attention_close
-    assert_attention_close(out, want, "managed samples")
+
+
+def test_beam_search_flow_drives_the_device_path(pa):
+    """Beam search through the native manager ([L] "Memory sharing across
+    requests": candidate beams share their common prefix blocks and diverge at
+    the end). A 29-token prompt forks into 4 beams; every step each live beam
+    appends a token (a write into a shared partial block copies it first); every
+    4 steps beams 1 and 3 are dropped and each survivor forks again. Slots, copy
+    pairs, free blocks, the pools and the final decode over the live beams match
+    the oracle replaying the same steps, and the prompt's full first block stays
+    shared by every live beam."""
+    NB = 128
+    m = Managed(pa, np.random.default_rng(78), NB, 4, 16, 128)
+    prompt = m.nat.add_sequence()
+    rprompt = []
+    say("beam search: 29-token prompt, 4 beams, 12 steps, prune and refork every 4")
+    for _ in range(29):
+        m.step([prompt], [rprompt])
+    beams = [m.nat.fork(prompt) for _ in range(4)]
+    rbeams = [m.ref.fork(rprompt) for _ in range(4)]
+    m.nat.release(prompt)
+    m.ref.release(rprompt)
+    for t in range(12):
+        m.step(beams, rbeams)
+        if t % 4 == 3:
+            for i in (1, 3):
+                m.nat.release(beams[i])
+                m.ref.release(rbeams[i])
+            beams, rbeams = [beams[0], beams[2]], [rbeams[0], rbeams[2]]
+            beams += [m.nat.fork(b) for b in beams]
+            rbeams += [m.ref.fork(r) for r in rbeams]
+        assert m.nat.num_free() == NB - m.ref.blocks_in_use()
+    tables, lens = m.check_decode(beams, rbeams, 4, "beams")
+    assert (lens == 29 + 12).all()
+    assert len({int(t[0]) for t in tables}) == 1 and m.nat.refcount(int(tables[0][0])) == len(beams)
 
 
 def test_swap_out_to_pinned_host_and_back_in(pa):

@@ -98,6 +98,23 @@ def test_workspace_and_partition_sizing(lib):
     assert ws(2, 4, 4, 128, 16, 48, 16) == 2 * 4 * 3 * 130 * 4
 
 
+def test_default_partition_keeps_a_workgroup_per_compute_unit(lib):
+    # the library's choice: 1024 tokens, halved while the launch (partitions x
+    # sequences x KV heads) would have fewer workgroups than the 256 CUs, down
+    # to 64; these are the measured best choices for each batch shape
+    ps = lib.pa_decode_partition_size
+    shapes = [  # S, Hq, Hkv, max_context_len, chosen P
+        (1, 32, 32, 1000, 128), (1, 32, 32, 4000, 512), (1, 32, 32, 16000, 1024),
+        (4, 32, 32, 2000, 1024), (8, 32, 32, 853, 1024), (8, 32, 8, 2000, 512),
+        (16, 32, 32, 4096, 1024), (128, 32, 32, 2400, 1024), (2, 4, 4, 48, 64)]
+    for S, Hq, Hkv, L, want in shapes:
+        P = ps(S, Hq, Hkv, 16, L, 0)
+        assert P == want, (S, Hq, Hkv, L, P)
+        wgs = lambda p: S * Hkv * -(-L // p)
+        assert P == 64 or wgs(P) >= 256
+        assert P == 1024 or wgs(2 * P) < 256
+
+
 def test_write_copy_slot_validation(lib):
     v = ctypes.c_void_p
     assert lib.pa_write_kv(v(FAKE), v(FAKE), v(FAKE), v(FAKE), None, 4, 2, 128, 16, 8, None) == PA_ERR_NULL

@@ -185,7 +185,8 @@ int pa_decode_partition_size(int S, int Hq, int Hkv, int B, int max_context_len,
  * pa_decode_workspace_bytes — device workspace pa_decode needs: partial
  * results of every context partition, S * Hq * ceil(max_context_len / P)
  * * (D + 2) * 4 bytes, or 0 when one partition covers every sequence.
- * Returns 0 for invalid arguments as well; pa_decode then reports the error.
+ * Returns 0 for invalid arguments, and when the size does not fit in size_t,
+ * as well; pa_decode then reports the error.
  */
 size_t pa_decode_workspace_bytes(int S, int Hq, int Hkv, int D, int B, int max_context_len,
                                  int partition_size);

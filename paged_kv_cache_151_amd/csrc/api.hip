@@ -258,7 +258,12 @@ size_t pa_decode_workspace_bytes(int S, int Hq, int Hkv, int D, int B, int max_c
   if (P <= 0 || S <= 0 || Hq <= 0 || D <= 0 || max_context_len <= 0) return 0;
   const int64_t Pmax = ceil_div(max_context_len, P);
   if (Pmax <= 1) return 0;
-  return (size_t)S * Hq * Pmax * (D + 2) * sizeof(float);
+  size_t n = 0;   // S * Hq * Pmax * (D + 2) floats; 0 when that overflows
+  if (__builtin_mul_overflow((size_t)S, (size_t)Hq, &n) ||
+      __builtin_mul_overflow(n, (size_t)Pmax, &n) ||
+      __builtin_mul_overflow(n, ((size_t)D + 2) * sizeof(float), &n))
+    return 0;
+  return n;
 }
 
 pa_status pa_decode(void* out, const void* query, const void* k_pool, const void* v_pool,

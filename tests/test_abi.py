@@ -98,6 +98,28 @@ def test_workspace_and_partition_sizing(lib):
     assert ws(2, 4, 4, 128, 16, 48, 16) == 2 * 4 * 3 * 130 * 4
 
 
+def test_workspace_size_is_exact_or_zero(lib):
+    # S * Hq * ceil(L / P) * (D + 2) fp32 values when more than one partition,
+    # 0 for one partition, invalid sizes, or a product past 64 bits
+    ws = lib.pa_decode_workspace_bytes
+    rng = __import__("numpy").random.default_rng(11)
+    big = (1 << 31) - 1
+    cases = [(1, 1, 1, 128, 16, 4096, 16), (big, big, 1, big, 16, big, 16), (big, 32, 32, 128, 16, big, 16),
+             (0, 32, 32, 128, 16, 100, 16), (4, 32, 32, -5, 16, 100, 16), (4, 32, 32, 128, 16, 100, 24)]
+    for _ in range(300):
+        cases.append((int(rng.integers(0, big)), int(rng.integers(1, 1 << int(rng.integers(1, 31)))), 1,
+                      int(rng.integers(1, 1 << int(rng.integers(1, 31)))), 16,
+                      int(rng.integers(1, big)), 16 * int(rng.integers(1, 64))))
+    for S, Hq, Hkv, D, B, L, P in cases:
+        got = ws(S, Hq, Hkv, D, B, L, P)
+        if P % 16 or S <= 0 or Hq <= 0 or D <= 0 or L <= 0:
+            assert got == 0
+            continue
+        parts = -(-L // P)
+        want = S * Hq * parts * (D + 2) * 4 if parts > 1 else 0
+        assert got == (want if want < (1 << 64) else 0), (S, Hq, D, L, P, got, want)
+
+
 def test_default_partition_keeps_a_workgroup_per_compute_unit(lib):
     # the library's choice: 1024 tokens, halved while the launch (partitions x
     # sequences x KV heads) would have fewer workgroups than the 256 CUs, down

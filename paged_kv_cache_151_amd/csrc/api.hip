@@ -92,7 +92,7 @@ const char* pa_status_str(int status) {
 
 const char* pa_last_error(void) { return pa::last_error(); }
 
-int pa_version(void) { return 100; }
+int pa_version(void) { return 200; }
 
 pa_status pa_slot_mapping(int64_t* slot_mapping, const int32_t* block_tables,
                           const int32_t* seq_ids, const int32_t* positions,

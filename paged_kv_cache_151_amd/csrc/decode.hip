@@ -500,7 +500,10 @@ hipError_t launch_partition_g(const DecodeArgs& a, int G, hipStream_t stream) {
     case 1: return launch_partition<BT, 1>(a, stream);
     case 2: return launch_partition<BT, 2>(a, stream);
     case 4: return launch_partition<BT, 4>(a, stream);
-    case 8: return launch_partition<BT, 8>(a, stream);
+    case 8:
+      // groups of 8 on the matrix cores (B = 8 keeps the vector path)
+      if constexpr (BT != 8) return launch_decode_group8(a, BT > 0 ? BT : a.B, stream);
+      else return launch_partition<BT, 8>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

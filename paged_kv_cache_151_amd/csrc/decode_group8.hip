@@ -1,0 +1,328 @@
+// Grouped-query decode on the matrix cores, for groups of 8 query heads.
+//
+// [L] "Paged Attention: OS-Inspired Memory Management for KV Caches",
+//     "How PagedAttention works", step 4: walk the block table, load each
+//     block's keys and values, attend exactly as over contiguous memory.
+//
+// With 8 query heads per KV head every loaded K/V tile meets 8 queries, and
+// the vector path's arithmetic (dot products, row sums, P.V per head) becomes
+// the bound. Here the 8 heads are the rows of a 16-row matrix tile (rows 8-15
+// are zero queries whose results are discarded) and each 16-token unit costs
+// four score products and eight value products:
+//   scores   S^T = K Q^T (v_mfma_f32_16x16x32_f16, lane l = 16 kq + m): the A
+//            operand is key token m, dims 32c + 8kq .. +7, loaded from the
+//            pool straight into registers; the B operand is query head m, the
+//            same dims, held in registers; lane l receives S for head m and
+//            tokens 4kq + r of the unit.
+//   output   O^T = V^T P^T per 16-dim tile n (v_mfma_f32_16x16x16_f16): the B
+//            operand is P as the score product left it (head m, tokens
+//            4kq .. 4kq + 3); the A operand, V for the same tokens at dim
+//            16n + m, comes from the unit's V tile staged in LDS by one
+//            transposing read (ds_read_b64_tr_b16: in each 16-lane group, lane
+//            i receives 16-bit word i % 4 from the address of lane 4e + i / 4
+//            as its element e). Lane l ends with O[head m][dims 16n + 4kq + r].
+// Each head's softmax state lives in the four lanes of its row (m, kq = 0..3);
+// rescaling is lazy, as in the prefill kernel: the running maximum is raised,
+// and the accumulators rescaled, only when some head's new scores exceed it
+// by 2^8, decided on lane maxima (a head exceeds the bound exactly when one of
+// its lanes does).
+//
+// Everything else is the partition kernel's: one workgroup per (partition,
+// sequence, KV head) in the same order, the same length clamping and empty
+// sequence, block-table chunks of 64 entries handed out by v_readlane, units
+// dealt round-robin to the waves and fetched one unit ahead with empty-range
+// no-op loads past a wave's last unit, the same cross-wave merge and the same
+// partials for the reduce kernel. V tiles go to a per-wave LDS double buffer
+// by buffer loads that write LDS directly; piece c of V row r sits at
+// c ^ 2 (r % 8), which keeps the transposing reads free of bank conflicts.
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef short s4 __attribute__((ext_vector_type(4)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) s4 lds_s4;
+
+constexpr float kNegBigG = -1.0e30f;      // "no token yet"; exp2 of it is 0
+constexpr float kSlackG = 8.0f;           // lazy rescaling slack, log2 units
+constexpr int kGroup = 8;                 // query heads per KV head
+constexpr int kRowBytesG = kHeadDim * 2;  // one token row of one KV head
+constexpr int kTileBytesG = kDecodeUnit * kRowBytesG;
+constexpr int kRsrcWord3G = 0x00020000;   // raw buffer, gfx9 family
+
+// lgkmcnt(0): every LDS read this wave issued has returned its data.
+#define PA_G_WAIT_LDS() __builtin_amdgcn_s_waitcnt(0xC07F)
+// vmcnt(0): every vector memory operation of this wave has completed.
+#define PA_G_WAIT_VM0() __builtin_amdgcn_s_waitcnt(0x0F70)
+
+template <int S>
+struct Stage {
+  static constexpr int value = S;
+};
+
+// 16-byte buffer loads of each lane into LDS (lane i's bytes at dst + 16 i;
+// lanes past the resource's range write zeros), plain and non-temporal.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, lds_u8* dst, unsigned voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff,
+                                           0, 0, 0);
+}
+__device__ __forceinline__ void dma16_nt(__amdgpu_buffer_rsrc_t r, lds_u8* dst, unsigned voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff,
+                                           0, 0, 2);
+}
+
+template <int BT, int NW, bool NT>
+__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeArgs a) {
+  constexpr int G = kGroup;
+  constexpr int D = kHeadDim;
+  constexpr int U = kDecodeUnit;
+  static_assert(BT == 0 || BT % U == 0, "block size a multiple of 16");
+  const int B = BT > 0 ? BT : a.B;
+  const int UPB = B / U;
+  // per-wave V tile buffers, one array per stage (the compiler tracks loads
+  // into LDS per array and waits only where a read meets its stage)
+  __shared__ __attribute__((aligned(16))) unsigned char s_v0[NW * kTileBytesG];
+  __shared__ __attribute__((aligned(16))) unsigned char s_v1[NW * kTileBytesG];
+  __shared__ float s_acc[NW][G][D];
+  __shared__ float s_ml[NW][G][2];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int m = lane & 15;
+  const int kq = lane >> 4;
+
+  int id = blockIdx.x;
+  const int g = id % a.Hkv;
+  id /= a.Hkv;
+  const int s = id % a.S;
+  const int p = id / a.S;
+
+  int L = a.lens[s];
+  L = L < 0 ? 0 : L;
+  L = L > a.MB * B ? a.MB * B : L;
+  L = L > a.Pmax * a.P ? a.Pmax * a.P : L;
+  const int tok0 = p * a.P;
+  const int hq0 = g * G;
+  if (tok0 >= L) {
+    if (p == 0) {  // empty sequence: zero output
+      for (int e = threadIdx.x; e < G * D; e += NW * 64) {
+        a.out[((int64_t)s * a.Hq + hq0 + e / D) * D + (e % D)] = (_Float16)0.f;
+      }
+    }
+    return;
+  }
+  const int nparts = (L + a.P - 1) / a.P;
+  const int len = (tok0 + a.P < L ? tok0 + a.P : L) - tok0;
+  const int nunits = (len + U - 1) / U;
+  const int U0 = tok0 / U;
+  const int blk0 = U0 / UPB;
+  const int nblk = (U0 + nunits - 1) / UPB - blk0 + 1;
+
+  // query heads as B operands: slice c holds dims 32c + 8kq .. +7 of head m
+  h8 qf[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const u32x4 raw = m < G ? *reinterpret_cast<const u32x4*>(
+                                  a.q + ((int64_t)s * a.Hq + hq0 + m) * D + 32 * c + 8 * kq)
+                            : u32x4{0, 0, 0, 0};
+    qf[c] = __builtin_bit_cast(h8, raw);
+  }
+  f4 o[8];
+#pragma unroll
+  for (int n = 0; n < 8; ++n) o[n] = f4{0.f, 0.f, 0.f, 0.f};
+  float mrow = kNegBigG, lsum = 0.f;
+
+  // K operand: token m, dims 32c + 8kq (c in the scalar offset)
+  const unsigned k_off = (unsigned)(m * kRowBytesG + 16 * kq);
+  // V into LDS: lane 16kq + m of row group i writes piece slot m of row
+  // 4i + kq, so it loads the global piece the swizzle places there
+  unsigned v_dma[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * i + kq;
+    v_dma[i] = (unsigned)(r * kRowBytesG + ((m ^ ((r & 7) << 1)) << 4));
+  }
+  // transposing read of tile n: lane 4e + q of group kq reads row 4kq + e,
+  // dims 16n + 4q .. +3
+  const int te = (lane & 15) >> 2, tq = lane & 3;
+  const int vr = 4 * kq + te;
+  int v_rd[8];
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    const int piece = 2 * n + (tq >> 1);
+    v_rd[n] = vr * kRowBytesG + ((piece ^ ((vr & 7) << 1)) << 4) + (tq & 1) * 8;
+  }
+  const int wbase = wave * kTileBytesG;
+
+  const int32_t* trow = a.tables + (int64_t)s * a.MB + blk0;
+  for (int cb = 0; cb < nblk; cb += 64) {
+    const int ce = cb + 64 < nblk ? cb + 64 : nblk;
+    const int tbl = cb + lane < ce ? trow[cb + lane] : -1;
+    const int ub0 = (blk0 + cb) * UPB - U0;
+    const int ue0 = (blk0 + ce) * UPB - U0;
+    const int ub = ub0 > 0 ? ub0 : 0;
+    const int ue = ue0 < nunits ? ue0 : nunits;
+    auto locate = [&](int u) -> int64_t {
+      const int au = U0 + u;
+      const int bi = au / UPB;
+      const int phys = __builtin_amdgcn_readlane(tbl, bi - blk0 - cb);
+      const int safe = (unsigned)phys < (unsigned)a.NB ? phys : 0;
+      return (((int64_t)safe * a.Hkv + g) * B + (au - bi * UPB) * U) * D;
+    };
+    // K of unit u into ka, V into the wave's buffer of this stage; past the
+    // wave's last unit the loads have an empty range (zeros, no memory read)
+    auto fetch = [&](h8 (&ka)[4], int u, auto stage) {
+      const bool live = u < ue;
+      const int uu = live ? u : ue - 1;
+      const int64_t base = locate(uu);
+      const int valid = len - uu * U;
+      const int nbytes = !live ? 0 : (valid >= U ? kTileBytesG : valid * kRowBytesG);
+      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<_Float16*>(a.k_pool + base), 0, nbytes, kRsrcWord3G);
+      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<_Float16*>(a.v_pool + base), 0, nbytes, kRsrcWord3G);
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        ka[c] = __builtin_bit_cast(
+            h8, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off, 64 * c, NT ? 2 : 0));
+      // the wave last read this stage two units ago: its reads must have
+      // returned before the buffer is refilled
+      __builtin_amdgcn_sched_barrier(0);
+      PA_G_WAIT_LDS();
+      lds_u8* vb = (decltype(stage)::value == 0 ? (lds_u8*)s_v0 : (lds_u8*)s_v1) + wbase;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (NT) dma16_nt(rv, vb + i * 1024, v_dma[i]);
+        else dma16(rv, vb + i * 1024, v_dma[i]);
+      }
+    };
+    auto step = [&](const h8 (&ka)[4], int u, auto stage) {
+      const lds_u8* vb = (decltype(stage)::value == 0 ? (lds_u8*)s_v0 : (lds_u8*)s_v1) + wbase;
+      f4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[c], qf[c], sc, 0, 0, 0);
+      const int valid = len - u * U;
+      bool vis[4];
+      float mx = kNegBigG;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        vis[r] = 4 * kq + r < valid;
+        mx = __builtin_fmaxf(mx, vis[r] ? sc[r] : kNegBigG);
+      }
+      const float mloc = mx > 0.5f * kNegBigG ? mx * a.scale_log2 : kNegBigG;
+      if (__builtin_amdgcn_ballot_w64(mloc > mrow + kSlackG)) {
+        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16));
+        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
+        const float mcand = mx > 0.5f * kNegBigG ? mx * a.scale_log2 : kNegBigG;
+        const float mnew = __builtin_fmaxf(mrow, mcand);
+        const float alpha = __builtin_amdgcn_exp2f(mrow - mnew);
+        mrow = mnew;
+        lsum *= alpha;
+#pragma unroll
+        for (int n = 0; n < 8; ++n) o[n] *= alpha;
+      }
+      h4 pb;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], a.scale_log2, -mrow));
+        pr = vis[r] ? pr : 0.f;
+        lsum += pr;
+        pb[r] = (_Float16)pr;
+      }
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const s4 raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(vb + v_rd[n]));
+        o[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h4, raw), pb, o[n], 0, 0, 0);
+      }
+    };
+    int u = ub + wave;
+    if (u >= ue) continue;
+    h8 k0[4], k1[4];
+    fetch(k0, u, Stage<0>{});
+    while (true) {
+      int un = u + NW;
+      fetch(k1, un, Stage<1>{});
+      step(k0, u, Stage<0>{});
+      if (un >= ue) break;
+      u = un;
+      un = u + NW;
+      fetch(k0, un, Stage<0>{});
+      step(k1, u, Stage<1>{});
+      if (un >= ue) break;
+      u = un;
+    }
+    // the last fetch was a no-op into a stage: let it land before the next
+    // chunk's first load writes that stage
+    PA_G_WAIT_VM0();
+  }
+  PA_G_WAIT_VM0();   // no load into LDS outlives the wave
+
+  // the four lanes of a head hold its sum in parts and the same maximum
+  float lt = lsum + __shfl_xor(lsum, 16);
+  lt += __shfl_xor(lt, 32);
+  if (m < G) {
+    if (kq == 0) {
+      s_ml[wave][m][0] = mrow;
+      s_ml[wave][m][1] = lt;
+    }
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s_acc[wave][m][16 * n + 4 * kq + r] = o[n][r];
+    }
+  }
+  __syncthreads();
+
+  // combine the waves: thread e handles output element (head h, dim d)
+  for (int e = threadIdx.x; e < G * D; e += NW * 64) {
+    const int h = e / D;
+    const int d = e % D;
+    float mx = s_ml[0][h][0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) mx = __builtin_fmaxf(mx, s_ml[w][h][0]);
+    float den = 0.f, num = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float f = __builtin_amdgcn_exp2f(s_ml[w][h][0] - mx);
+      den += f * s_ml[w][h][1];
+      num += f * s_acc[w][h][d];
+    }
+    const int hq = hq0 + h;
+    if (nparts == 1) {
+      const float ov = den > 0.f ? num / den : 0.f;
+      a.out[((int64_t)s * a.Hq + hq) * D + d] = (_Float16)ov;
+    } else {
+      const int64_t row = ((int64_t)s * a.Hq + hq) * a.Pmax + p;
+      a.part_acc[row * D + d] = num;
+      if (d == 0) {
+        a.part_ml[row * 2] = mx;
+        a.part_ml[row * 2 + 1] = den;
+      }
+    }
+  }
+}
+
+template <int BT>
+hipError_t launch_bt(const DecodeArgs& a, hipStream_t stream) {
+  constexpr int NW = 4;
+  const int64_t grid = (int64_t)a.Pmax * a.S * a.Hkv;
+  decode_mfma_kernel<BT, NW, kDecodeNontemporal><<<(unsigned)grid, NW * 64, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_group8(const DecodeArgs& a, int B, hipStream_t stream) {
+  switch (B) {
+    case 16: return launch_bt<16>(a, stream);
+    case 32: return launch_bt<32>(a, stream);
+    default: return launch_bt<0>(a, stream);
+  }
+}
+
+}  // namespace pa

@@ -151,27 +151,20 @@ def test_shared_prefix_gqa_and_private_twin_bit_identical(pa):
     assert np.array_equal(u16(out), u16(out2))
 
 
-def test_relabelling_physical_blocks_is_bit_identical(pa):
-    c = W.seven_b_single_layer()
-    say("relabel physical ids")
-    base, _ = decode_step(pa, c, dev(c.k_pool), dev(c.v_pool))
-    rng = np.random.default_rng(99)
-    perm = rng.permutation(c.NB)          # new id of old block b is perm[b]
+def relabelled(c, seed):
+    """The same case with every physical block id permuted."""
+    perm = np.random.default_rng(seed).permutation(c.NB)   # new id of old block b is perm[b]
     k2 = np.empty_like(c.k_pool)
     v2 = np.empty_like(c.v_pool)
     k2[perm] = c.k_pool
     v2[perm] = c.v_pool
     t2 = np.where(c.block_tables >= 0, perm[np.maximum(c.block_tables, 0)], -1).astype(np.int32)
-    c2 = W.DecodeCase(**{**c.__dict__, "block_tables": t2, "k_pool": k2, "v_pool": v2})
-    got, _ = decode_step(pa, c2, dev(k2), dev(v2))
-    assert np.array_equal(u16(base), u16(got))
+    return W.DecodeCase(**{**c.__dict__, "block_tables": t2, "k_pool": k2, "v_pool": v2})
 
 
-@pytest.mark.parametrize("poison", [np.float16(np.nan), np.float16(np.inf), np.float16(-np.inf)])
-def test_unused_slots_and_blocks_never_reach_the_output(pa, poison):
-    c = W.make_case("poison", 31, [1, 15, 16, 17, 33, 200, 511, 513], Hq=8, Hkv=4, B=16)
-    clean, _ = decode_step(pa, c, dev(c.k_pool), dev(c.v_pool), partition_size=64)
-    # poison every slot that is not one of the sequences' first L tokens
+def poisoned_pools(c, poison):
+    """Pools with every slot that is not one of the sequences' first L tokens
+    (the slot this step writes included) set to poison."""
     keep = np.zeros(c.NB * c.B, bool)
     for s, L in enumerate(c.context_lens):
         for t in range(int(L)):
@@ -180,9 +173,62 @@ def test_unused_slots_and_blocks_never_reach_the_output(pa, poison):
     mask = ~keep.reshape(c.NB, c.B)
     kp.transpose(0, 2, 1, 3)[mask] = poison
     vp.transpose(0, 2, 1, 3)[mask] = poison
+    return kp, vp
+
+
+def test_relabelling_physical_blocks_is_bit_identical(pa):
+    c = W.seven_b_single_layer()
+    say("relabel physical ids")
+    base, _ = decode_step(pa, c, dev(c.k_pool), dev(c.v_pool))
+    c2 = relabelled(c, 99)
+    got, _ = decode_step(pa, c2, dev(c2.k_pool), dev(c2.v_pool))
+    assert np.array_equal(u16(base), u16(got))
+
+
+@pytest.mark.parametrize("poison", [np.float16(np.nan), np.float16(np.inf), np.float16(-np.inf)])
+def test_unused_slots_and_blocks_never_reach_the_output(pa, poison):
+    c = W.make_case("poison", 31, [1, 15, 16, 17, 33, 200, 511, 513], Hq=8, Hkv=4, B=16)
+    clean, _ = decode_step(pa, c, dev(c.k_pool), dev(c.v_pool), partition_size=64)
+    kp, vp = poisoned_pools(c, poison)
     say(f"poison {poison}")
     got, _ = decode_step(pa, c, dev(kp), dev(vp), partition_size=64)
     assert np.array_equal(u16(clean), u16(got))
+
+
+# Groups of 8 query heads run on the matrix cores when B is a multiple of 16:
+# the edge cases and invariants again for that kernel.
+
+@pytest.mark.parametrize("B", [16, 32, 48])
+def test_group8_lengths_partitions_and_table_chunks(pa, B):
+    # empty sequences, partial units, partitions starting inside blocks, the
+    # reduce, and single partitions longer than 64 blocks (several table chunks)
+    lens = [0, 1, 15, 16, 17, 100, 1025, 64 * B + 17, 2 * 64 * 16 + 5]
+    c = W.make_case(f"group8_B{B}", 5000 + B, lens, Hq=16, Hkv=2, B=B)
+    for ps in (0, 48, 1040, 4096):
+        check_case(pa, c, partition_size=ps)
+
+
+@pytest.mark.parametrize("B", [16, 32])
+@pytest.mark.parametrize("poison", [np.float16(np.nan), np.float16(np.inf), np.float16(-np.inf)])
+def test_group8_unused_slots_and_blocks_never_reach_the_output(pa, poison, B):
+    c = W.make_case(f"group8_poison_B{B}", 5100 + B, [1, 15, 16, 17, 33, 200, 511, 513],
+                    Hq=16, Hkv=2, B=B)
+    clean, _ = decode_step(pa, c, dev(c.k_pool), dev(c.v_pool), partition_size=64)
+    kp, vp = poisoned_pools(c, poison)
+    say(f"group of 8, B={B}, poison {poison}")
+    got, _ = decode_step(pa, c, dev(kp), dev(vp), partition_size=64)
+    assert np.array_equal(u16(clean), u16(got))
+
+
+def test_group8_relabelling_physical_blocks_is_bit_identical(pa):
+    c = W.make_case("group8_relabel", 5200, [700, 90, 1023, 5, 2000], Hq=64, Hkv=8, B=16)
+    say("group of 8: relabel physical ids")
+    base, _ = decode_step(pa, c, dev(c.k_pool), dev(c.v_pool))
+    c2 = relabelled(c, 98)
+    got, _ = decode_step(pa, c2, dev(c2.k_pool), dev(c2.v_pool))
+    assert np.array_equal(u16(base), u16(got))
+    ref, _ = oracle_step(c, c.k_pool, c.v_pool)
+    assert_attention_close(base, ref, "group8_relabel")
 
 
 EDGE_B16 = [1, 15, 16, 17, 63, 64, 65, 128, 131]

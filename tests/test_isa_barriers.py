@@ -47,7 +47,8 @@ def _assembly(src: str, out_dir) -> str:
         return f.read()
 
 
-@pytest.mark.parametrize("src,min_kernels", [("prefill.hip", 12), ("decode.hip", 4)])
+@pytest.mark.parametrize("src,min_kernels", [("prefill.hip", 12), ("decode.hip", 4),
+                                              ("decode_group8.hip", 3)])
 def test_no_barrier_reached_with_lds_reads_in_flight(src, min_kernels, tmp_path):
     text = _assembly(src, tmp_path)
     assert kernel_count(text) >= min_kernels

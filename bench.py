@@ -91,7 +91,7 @@ def parse():
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pa_decode_chat_b128_traffic.json")
 DECODE_SOURCES = [os.path.join(ROOT, "paged_kv_cache_151_amd", "csrc", f)
-                  for f in ("decode.hip", "pa_internal.h")]
+                  for f in ("decode.hip", "decode_mfma.hip", "pa_internal.h")]
 
 
 def decode_source_hash() -> str:

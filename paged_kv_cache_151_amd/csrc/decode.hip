@@ -499,10 +499,12 @@ hipError_t launch_partition_g(const DecodeArgs& a, int G, hipStream_t stream) {
   switch (G) {
     case 1: return launch_partition<BT, 1>(a, stream);
     case 2: return launch_partition<BT, 2>(a, stream);
-    case 4: return launch_partition<BT, 4>(a, stream);
+    case 4:
+      // groups of 4 and 8 on the matrix cores (B = 8 keeps the vector path)
+      if constexpr (BT != 8) return launch_decode_mfma(a, BT > 0 ? BT : a.B, 4, stream);
+      else return launch_partition<BT, 4>(a, stream);
     case 8:
-      // groups of 8 on the matrix cores (B = 8 keeps the vector path)
-      if constexpr (BT != 8) return launch_decode_group8(a, BT > 0 ? BT : a.B, stream);
+      if constexpr (BT != 8) return launch_decode_mfma(a, BT > 0 ? BT : a.B, 8, stream);
       else return launch_partition<BT, 8>(a, stream);
     default: return hipErrorInvalidValue;
   }

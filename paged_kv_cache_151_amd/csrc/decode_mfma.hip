@@ -1,4 +1,4 @@
-// Grouped-query decode on the matrix cores, for groups of 8 query heads.
+// Grouped-query decode on the matrix cores, for groups of 4 and 8 query heads.
 //
 // [L] "Paged Attention: OS-Inspired Memory Management for KV Caches",
 //     "How PagedAttention works", step 4: walk the block table, load each
@@ -6,9 +6,9 @@
 //
 // With 8 query heads per KV head every loaded K/V tile meets 8 queries, and
 // the vector path's arithmetic (dot products, row sums, P.V per head) becomes
-// the bound. Here the 8 heads are the rows of a 16-row matrix tile (rows 8-15
-// are zero queries whose results are discarded) and each 16-token unit costs
-// four score products and eight value products:
+// the bound; with 4 it is close to it. Here the G heads are the rows of a
+// 16-row matrix tile (rows G-15 are zero queries whose results are discarded)
+// and each 16-token unit costs four score products and eight value products:
 //   scores   S^T = K Q^T (v_mfma_f32_16x16x32_f16, lane l = 16 kq + m): the A
 //            operand is key token m, dims 32c + 8kq .. +7, loaded from the
 //            pool straight into registers; the B operand is query head m, the
@@ -50,7 +50,6 @@ typedef __attribute__((address_space(3))) s4 lds_s4;
 
 constexpr float kNegBigG = -1.0e30f;      // "no token yet"; exp2 of it is 0
 constexpr float kSlackG = 8.0f;           // lazy rescaling slack, log2 units
-constexpr int kGroup = 8;                 // query heads per KV head
 constexpr int kRowBytesG = kHeadDim * 2;  // one token row of one KV head
 constexpr int kTileBytesG = kDecodeUnit * kRowBytesG;
 constexpr int kRsrcWord3G = 0x00020000;   // raw buffer, gfx9 family
@@ -76,9 +75,9 @@ __device__ __forceinline__ void dma16_nt(__amdgpu_buffer_rsrc_t r, lds_u8* dst, 
                                            0, 0, 2);
 }
 
-template <int BT, int NW, bool NT>
+template <int BT, int G, int NW, bool NT>
 __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeArgs a) {
-  constexpr int G = kGroup;
+  static_assert(G == 4 || G == 8, "groups of 4 or 8 query heads");
   constexpr int D = kHeadDim;
   constexpr int U = kDecodeUnit;
   static_assert(BT == 0 || BT % U == 0, "block size a multiple of 16");
@@ -307,21 +306,30 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeArgs a
   }
 }
 
-template <int BT>
+template <int BT, int G>
 hipError_t launch_bt(const DecodeArgs& a, hipStream_t stream) {
   constexpr int NW = 4;
   const int64_t grid = (int64_t)a.Pmax * a.S * a.Hkv;
-  decode_mfma_kernel<BT, NW, kDecodeNontemporal><<<(unsigned)grid, NW * 64, 0, stream>>>(a);
+  decode_mfma_kernel<BT, G, NW, kDecodeNontemporal><<<(unsigned)grid, NW * 64, 0, stream>>>(a);
   return hipGetLastError();
+}
+
+template <int G>
+hipError_t launch_g(const DecodeArgs& a, int B, hipStream_t stream) {
+  switch (B) {
+    case 16: return launch_bt<16, G>(a, stream);
+    case 32: return launch_bt<32, G>(a, stream);
+    default: return launch_bt<0, G>(a, stream);
+  }
 }
 
 }  // namespace
 
-hipError_t launch_decode_group8(const DecodeArgs& a, int B, hipStream_t stream) {
-  switch (B) {
-    case 16: return launch_bt<16>(a, stream);
-    case 32: return launch_bt<32>(a, stream);
-    default: return launch_bt<0>(a, stream);
+hipError_t launch_decode_mfma(const DecodeArgs& a, int B, int G, hipStream_t stream) {
+  switch (G) {
+    case 4: return launch_g<4>(a, B, stream);
+    case 8: return launch_g<8>(a, B, stream);
+    default: return hipErrorInvalidValue;
   }
 }
 

@@ -48,7 +48,7 @@ def _assembly(src: str, out_dir) -> str:
 
 
 @pytest.mark.parametrize("src,min_kernels", [("prefill.hip", 12), ("decode.hip", 4),
-                                              ("decode_group8.hip", 3)])
+                                              ("decode_mfma.hip", 6)])
 def test_no_barrier_reached_with_lds_reads_in_flight(src, min_kernels, tmp_path):
     text = _assembly(src, tmp_path)
     assert kernel_count(text) >= min_kernels

@@ -225,9 +225,8 @@ pa_status pa_swap_blocks(void* dst_k_pool, void* dst_v_pool, const void* src_k_p
   return ok();
 }
 
-// Compute units of the MI355X: the default decode partition keeps at least
-// one workgroup per CU.
-constexpr int64_t kComputeUnits = 256;
+// The default decode partition keeps at least one workgroup per compute unit
+// (kComputeUnits).
 
 int pa_decode_partition_size(int S, int Hq, int Hkv, int B, int max_context_len,
                              int partition_size) {
@@ -248,7 +247,7 @@ int pa_decode_partition_size(int S, int Hq, int Hkv, int B, int max_context_len,
   int P = 1024;
   const int64_t units = (int64_t)(S > 0 ? S : 1) * (Hkv > 0 ? Hkv : 1);
   const int maxL = max_context_len > 0 ? max_context_len : 1;
-  while (P > 4 * U && units * ceil_div(maxL, P) < kComputeUnits) P /= 2;
+  while (P > 4 * U && units * ceil_div(maxL, P) < pa::kComputeUnits) P /= 2;
   return P;
 }
 

@@ -489,6 +489,13 @@ hipError_t launch_partition(const DecodeArgs& a, hipStream_t stream) {
   constexpr int NH = G / HPW;
   constexpr int NW = decode_waves(G) > NH ? decode_waves(G) : NH;
   const int64_t grid = (int64_t)a.Pmax * a.S * a.Hkv;
+  if constexpr (G <= 2) {
+    if (grid <= kSmallLaunchWorkgroups) {
+      decode_partition_kernel<BT, G, HPW, 2 * NW, kDecodeDepth, kDecodeNontemporal>
+          <<<(unsigned)grid, 2 * NW * 64, 0, stream>>>(a);
+      return hipGetLastError();
+    }
+  }
   decode_partition_kernel<BT, G, HPW, NW, kDecodeDepth, kDecodeNontemporal>
       <<<(unsigned)grid, NW * 64, 0, stream>>>(a);
   return hipGetLastError();

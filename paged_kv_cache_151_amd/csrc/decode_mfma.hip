@@ -80,9 +80,10 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeArgs a
   static_assert(G == 4 || G == 8, "groups of 4 or 8 query heads");
   constexpr int D = kHeadDim;
   constexpr int U = kDecodeUnit;
-  static_assert(BT == 0 || BT % U == 0, "block size a multiple of 16");
+  static_assert(BT == 0 || BT == 8 || BT % U == 0, "block size 8 or a multiple of 16");
+  constexpr bool kSplit = BT == 8;      // a unit spans two blocks
   const int B = BT > 0 ? BT : a.B;
-  const int UPB = B / U;
+  const int UPB = kSplit ? 1 : B / U;   // units per block (B >= 16)
   // per-wave V tile buffers, one array per stage (the compiler tracks loads
   // into LDS per array and waits only where a read meets its stage)
   __shared__ __attribute__((aligned(16))) unsigned char s_v0[NW * kTileBytesG];
@@ -119,8 +120,8 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeArgs a
   const int len = (tok0 + a.P < L ? tok0 + a.P : L) - tok0;
   const int nunits = (len + U - 1) / U;
   const int U0 = tok0 / U;
-  const int blk0 = U0 / UPB;
-  const int nblk = (U0 + nunits - 1) / UPB - blk0 + 1;
+  const int blk0 = kSplit ? 2 * U0 : U0 / UPB;
+  const int nblk = kSplit ? (len + 7) / 8 : (U0 + nunits - 1) / UPB - blk0 + 1;
 
   // query heads as B operands: slice c holds dims 32c + 8kq .. +7 of head m
   h8 qf[4];
@@ -138,6 +139,12 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeArgs a
 
   // K operand: token m, dims 32c + 8kq (c in the scalar offset)
   const unsigned k_off = (unsigned)(m * kRowBytesG + 16 * kq);
+  // B = 8: rows 0-7 come from the unit's first block, rows 8-15 from its
+  // second; a lane's offset into the other block's resource is out of range,
+  // so that load returns zeros without reading memory
+  constexpr unsigned kOutOfRange = 0x80000000u;
+  const unsigned k_off_lo = m < 8 ? k_off : kOutOfRange;
+  const unsigned k_off_hi = m < 8 ? kOutOfRange : k_off - 8 * kRowBytesG;
   // V into LDS: lane 16kq + m of row group i writes piece slot m of row
   // 4i + kq, so it loads the global piece the swizzle places there
   unsigned v_dma[4];
@@ -162,8 +169,8 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeArgs a
   for (int cb = 0; cb < nblk; cb += 64) {
     const int ce = cb + 64 < nblk ? cb + 64 : nblk;
     const int tbl = cb + lane < ce ? trow[cb + lane] : -1;
-    const int ub0 = (blk0 + cb) * UPB - U0;
-    const int ue0 = (blk0 + ce) * UPB - U0;
+    const int ub0 = kSplit ? cb / 2 : (blk0 + cb) * UPB - U0;
+    const int ue0 = kSplit ? (ce + 1) / 2 : (blk0 + ce) * UPB - U0;
     const int ub = ub0 > 0 ? ub0 : 0;
     const int ue = ue0 < nunits ? ue0 : nunits;
     auto locate = [&](int u) -> int64_t {
@@ -173,31 +180,63 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeArgs a
       const int safe = (unsigned)phys < (unsigned)a.NB ? phys : 0;
       return (((int64_t)safe * a.Hkv + g) * B + (au - bi * UPB) * U) * D;
     };
+    // B = 8: tile base of block j (0, 1) of unit u. The chunk's 64 entries
+    // hold whole units (units start at even block indices), so both lanes
+    // read here are in the chunk; an entry past the partition's blocks is -1
+    // and is clamped to block 0, with an empty range.
+    auto locate_half = [&](int u, int j) -> int64_t {
+      const int phys = __builtin_amdgcn_readlane(tbl, 2 * u + j - cb);
+      const int safe = (unsigned)phys < (unsigned)a.NB ? phys : 0;
+      return ((int64_t)safe * a.Hkv + g) * B * D;
+    };
     // K of unit u into ka, V into the wave's buffer of this stage; past the
     // wave's last unit the loads have an empty range (zeros, no memory read)
     auto fetch = [&](h8 (&ka)[4], int u, auto stage) {
       const bool live = u < ue;
       const int uu = live ? u : ue - 1;
-      const int64_t base = locate(uu);
       const int valid = len - uu * U;
-      const int nbytes = !live ? 0 : (valid >= U ? kTileBytesG : valid * kRowBytesG);
-      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<_Float16*>(a.k_pool + base), 0, nbytes, kRsrcWord3G);
-      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<_Float16*>(a.v_pool + base), 0, nbytes, kRsrcWord3G);
+      __amdgpu_buffer_rsrc_t rk, rv, rk1, rv1;
+      if constexpr (kSplit) {
+        const int64_t b0 = locate_half(uu, 0);
+        const int64_t b1 = locate_half(uu, 1);
+        const int v0 = valid < 8 ? valid : 8;
+        const int v1 = valid - 8 < 0 ? 0 : (valid - 8 > 8 ? 8 : valid - 8);
+        const int n0 = live ? v0 * kRowBytesG : 0;
+        const int n1 = live ? v1 * kRowBytesG : 0;
+        rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16*>(a.k_pool + b0), 0, n0, kRsrcWord3G);
+        rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16*>(a.v_pool + b0), 0, n0, kRsrcWord3G);
+        rk1 = __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16*>(a.k_pool + b1), 0, n1, kRsrcWord3G);
+        rv1 = __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16*>(a.v_pool + b1), 0, n1, kRsrcWord3G);
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        ka[c] = __builtin_bit_cast(
-            h8, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off, 64 * c, NT ? 2 : 0));
+        for (int c = 0; c < 4; ++c) {
+          const u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(rk, k_off_lo, 64 * c, NT ? 2 : 0);
+          const u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(rk1, k_off_hi, 64 * c, NT ? 2 : 0);
+          ka[c] = __builtin_bit_cast(h8, lo | hi);
+        }
+      } else {
+        const int64_t base = locate(uu);
+        const int nbytes = !live ? 0 : (valid >= U ? kTileBytesG : valid * kRowBytesG);
+        rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16*>(a.k_pool + base), 0, nbytes, kRsrcWord3G);
+        rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16*>(a.v_pool + base), 0, nbytes, kRsrcWord3G);
+        rv1 = rv;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          ka[c] = __builtin_bit_cast(
+              h8, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off, 64 * c, NT ? 2 : 0));
+      }
       // the wave last read this stage two units ago: its reads must have
       // returned before the buffer is refilled
       __builtin_amdgcn_sched_barrier(0);
       PA_G_WAIT_LDS();
       lds_u8* vb = (decltype(stage)::value == 0 ? (lds_u8*)s_v0 : (lds_u8*)s_v1) + wbase;
+      // row groups 0-1 hold rows 0-7, groups 2-3 rows 8-15 (the second block at B = 8)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (NT) dma16_nt(rv, vb + i * 1024, v_dma[i]);
-        else dma16(rv, vb + i * 1024, v_dma[i]);
+        const bool second = kSplit && i >= 2;
+        const __amdgpu_buffer_rsrc_t r = second ? rv1 : rv;
+        const unsigned off = second ? v_dma[i] - 8 * kRowBytesG : v_dma[i];
+        if (NT) dma16_nt(r, vb + i * 1024, off);
+        else dma16(r, vb + i * 1024, off);
       }
     };
     auto step = [&](const h8 (&ka)[4], int u, auto stage) {
@@ -317,6 +356,9 @@ hipError_t launch_bt(const DecodeArgs& a, hipStream_t stream) {
 template <int G>
 hipError_t launch_g(const DecodeArgs& a, int B, hipStream_t stream) {
   switch (B) {
+    case 8:
+      if constexpr (G == 8) return launch_bt<8, G>(a, stream);
+      else return hipErrorInvalidValue;
     case 16: return launch_bt<16, G>(a, stream);
     case 32: return launch_bt<32, G>(a, stream);
     default: return launch_bt<0, G>(a, stream);

@@ -506,11 +506,8 @@ hipError_t launch_partition_g(const DecodeArgs& a, int G, hipStream_t stream) {
   switch (G) {
     case 1: return launch_partition<BT, 1>(a, stream);
     case 2: return launch_partition<BT, 2>(a, stream);
-    // groups of 4 and 8 on the matrix cores, except groups of 4 at B = 8:
-    // there a unit's two K loads cost more than the matrix cores save
-    case 4:
-      if constexpr (BT != 8) return launch_decode_mfma(a, BT > 0 ? BT : a.B, 4, stream);
-      else return launch_partition<BT, 4>(a, stream);
+    // groups of 4 and 8 on the matrix cores
+    case 4: return launch_decode_mfma(a, BT > 0 ? BT : a.B, 4, stream);
     case 8: return launch_decode_mfma(a, BT > 0 ? BT : a.B, 8, stream);
     default: return hipErrorInvalidValue;
   }

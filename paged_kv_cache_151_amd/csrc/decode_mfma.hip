@@ -140,11 +140,8 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeArgs a
   // K operand: token m, dims 32c + 8kq (c in the scalar offset)
   const unsigned k_off = (unsigned)(m * kRowBytesG + 16 * kq);
   // B = 8: rows 0-7 come from the unit's first block, rows 8-15 from its
-  // second; a lane's offset into the other block's resource is out of range,
-  // so that load returns zeros without reading memory
-  constexpr unsigned kOutOfRange = 0x80000000u;
-  const unsigned k_off_lo = m < 8 ? k_off : kOutOfRange;
-  const unsigned k_off_hi = m < 8 ? kOutOfRange : k_off - 8 * kRowBytesG;
+  // second, through per-lane addresses (element offset inside the block)
+  const int k_elt8 = (m & 7) * D + 8 * kq;
   // V into LDS: lane 16kq + m of row group i writes piece slot m of row
   // 4i + kq, so it loads the global piece the swizzle places there
   unsigned v_dma[4];
@@ -195,7 +192,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeArgs a
       const bool live = u < ue;
       const int uu = live ? u : ue - 1;
       const int valid = len - uu * U;
-      __amdgpu_buffer_rsrc_t rk, rv, rk1, rv1;
+      __amdgpu_buffer_rsrc_t rk, rv, rv1;
       if constexpr (kSplit) {
         const int64_t b0 = locate_half(uu, 0);
         const int64_t b1 = locate_half(uu, 1);
@@ -203,15 +200,18 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeArgs a
         const int v1 = valid - 8 < 0 ? 0 : (valid - 8 > 8 ? 8 : valid - 8);
         const int n0 = live ? v0 * kRowBytesG : 0;
         const int n1 = live ? v1 * kRowBytesG : 0;
-        rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16*>(a.k_pool + b0), 0, n0, kRsrcWord3G);
         rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16*>(a.v_pool + b0), 0, n0, kRsrcWord3G);
-        rk1 = __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16*>(a.k_pool + b1), 0, n1, kRsrcWord3G);
         rv1 = __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16*>(a.v_pool + b1), 0, n1, kRsrcWord3G);
+        // K rows past the valid tokens are read from their (clamped, in-pool)
+        // block but never used: their scores are masked by selection
+        if (live) {
+          const u32x4* kr = reinterpret_cast<const u32x4*>(a.k_pool + (m < 8 ? b0 : b1) + k_elt8);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(rk, k_off_lo, 64 * c, NT ? 2 : 0);
-          const u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(rk1, k_off_hi, 64 * c, NT ? 2 : 0);
-          ka[c] = __builtin_bit_cast(h8, lo | hi);
+          for (int c = 0; c < 4; ++c)
+            ka[c] = __builtin_bit_cast(h8, NT ? __builtin_nontemporal_load(kr + 4 * c) : kr[4 * c]);
+        } else {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) ka[c] = h8{};
         }
       } else {
         const int64_t base = locate(uu);
@@ -356,9 +356,7 @@ hipError_t launch_bt(const DecodeArgs& a, hipStream_t stream) {
 template <int G>
 hipError_t launch_g(const DecodeArgs& a, int B, hipStream_t stream) {
   switch (B) {
-    case 8:
-      if constexpr (G == 8) return launch_bt<8, G>(a, stream);
-      else return hipErrorInvalidValue;
+    case 8: return launch_bt<8, G>(a, stream);
     case 16: return launch_bt<16, G>(a, stream);
     case 32: return launch_bt<32, G>(a, stream);
     default: return launch_bt<0, G>(a, stream);

@@ -90,8 +90,8 @@ hipError_t launch_copy_blocks(void* k_dst, void* v_dst, const void* k_src, const
 hipError_t launch_decode(const DecodeArgs& a, int B, int G, hipStream_t stream);
 
 // Partition kernel for groups of G = 4 or 8 query heads on the matrix cores
-// (B a multiple of 16, or B = 8 for G = 8); same grid, outputs and partials
-// as the vector kernel.
+// (B = 8 or a multiple of 16); same grid, outputs and partials as the vector
+// kernel.
 hipError_t launch_decode_mfma(const DecodeArgs& a, int B, int G, hipStream_t stream);
 
 }  // namespace pa

@@ -196,8 +196,7 @@ def test_unused_slots_and_blocks_never_reach_the_output(pa, poison):
 
 
 # Groups of 4 and 8 query heads run on the matrix cores: the edge cases and
-# invariants again for that kernel (at B = 8, where each 16-token unit reads
-# two blocks, only groups of 8 take it; groups of 4 take the vector path).
+# invariants again for that kernel (at B = 8 each 16-token unit reads two blocks).
 
 @pytest.mark.parametrize("B", [8, 16, 32, 48])
 @pytest.mark.parametrize("G", [4, 8])
@@ -377,12 +376,10 @@ def relayout(c, B):
                            "k_pool": kp, "v_pool": vp})
 
 
-@pytest.mark.parametrize("G", [1, 2, 8])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
 def test_block_size_8_is_bit_identical_to_16(pa, G):
     # the arithmetic order depends only on logical positions, so the same
-    # tokens give the same bits whatever the block size (for groups that run
-    # on the same kernel at both sizes: groups of 4 take the matrix cores at
-    # B = 16 but the vector path at B = 8)
+    # tokens give the same bits whatever the block size
     c8 = W.make_case(f"B8_vs_16_G{G}", 2300 + G, B8_LENS, Hq=2 * G, Hkv=2, B=8)
     c16 = relayout(c8, 16)
     for ps in (0, 16, 64):

@@ -25,13 +25,14 @@ from .geometry import (blocks_for, logical_block, block_offset, slot_of, empty_s
                        kv_bytes_per_token, contiguous_waste, paged_waste, decode_slots,
                        token_slots)
 from .cache import gather, write_kv, copy_blocks, swap_blocks
-from .attention import decode, prefill, attend, attend_partial, merge_partials
+from .attention import (decode, prefill, attend, attend_partial, merge_partials,
+                        causal_attention)
 from .block_manager import BlockManager, PoolExhausted
 
 __all__ = [
     "blocks_for", "logical_block", "block_offset", "slot_of", "empty_slots",
     "kv_bytes_per_token", "contiguous_waste", "paged_waste", "decode_slots", "token_slots",
     "gather", "write_kv", "copy_blocks", "swap_blocks",
-    "decode", "prefill", "attend", "attend_partial", "merge_partials",
+    "decode", "prefill", "attend", "attend_partial", "merge_partials", "causal_attention",
     "BlockManager", "PoolExhausted",
 ]

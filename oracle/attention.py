@@ -102,6 +102,27 @@ def merge_partials(parts):
     return num / den
 
 
+def causal_attention(Q, K, V, first_pos: int, scale) -> np.ndarray:
+    """Softmax attention of n query rows over L keys/values, causal, in fp64.
+
+    Row i is the token at position first_pos + i and sees keys 0 .. first_pos + i:
+    scores = scale * Q K^T with the keys after each row's position removed from
+    its softmax, then weights = exp(scores - row max) / row sum and
+    out = weights V. Every row must see at least one key (first_pos >= 0).
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    n, L = Q.shape[0], K.shape[0]
+    if first_pos < 0 or first_pos + n > L:
+        raise ValueError("rows must sit at positions 0 .. L - 1")
+    scores = float(scale) * (Q @ K.T)
+    visible = np.arange(L)[None, :] <= (first_pos + np.arange(n))[:, None]
+    scores = np.where(visible, scores, -np.inf)
+    w = np.exp(scores - scores.max(axis=1, keepdims=True))   # exp(-inf) = 0
+    return (w @ V) / w.sum(axis=1, keepdims=True)
+
+
 def prefill(query, k_pool, v_pool, block_tables, context_lens, query_start, scale) -> np.ndarray:
     """Paged attention of a chunk of new tokens per sequence (fp64, [T, Hq, D]).
 
@@ -112,6 +133,7 @@ def prefill(query, k_pool, v_pool, block_tables, context_lens, query_start, scal
     positions 0 .. L-n+j: every earlier token of the sequence, cached prefix
     included, and itself ([L], "How PagedAttention works", step 1: the prompt
     is stored in the request's blocks; step 4: attention walks the table).
+    Written per (sequence, query head) as one masked attention of all n rows.
     """
     T, Hq, D = query.shape
     NB, Hkv, B, Dk = k_pool.shape
@@ -129,9 +151,8 @@ def prefill(query, k_pool, v_pool, block_tables, context_lens, query_start, scal
             continue
         Kc = gather(k_pool, block_tables[s], L, B).astype(np.float64)
         Vc = gather(v_pool, block_tables[s], L, B).astype(np.float64)
-        for j in range(n):
-            pos = L - n + j
-            for h in range(Hq):
-                g = h // G
-                out[qs[s] + j, h] = attend(query[qs[s] + j, h], Kc[g, :pos + 1], Vc[g, :pos + 1], scale)
+        rows = slice(int(qs[s]), int(qs[s]) + n)
+        for h in range(Hq):
+            g = h // G
+            out[rows, h] = causal_attention(query[rows, h], Kc[g], Vc[g], L - n, scale)
     return out

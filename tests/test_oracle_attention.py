@@ -235,7 +235,10 @@ def _prefill_case(rng, lens, nq, Hq, Hkv, B, D=16, extra_blocks=3):
 def test_prefill_of_one_token_is_decode():
     rng = np.random.default_rng(20)
     q, kp, vp, t, L, qs = _prefill_case(rng, [17, 40, 5], [1, 1, 1], 4, 2, 4)
-    assert np.array_equal(oracle.prefill(q, kp, vp, t, L, qs, 0.3), oracle.decode(q, kp, vp, t, L, 0.3))
+    # prefill works on all rows of a sequence at once, decode on one query:
+    # the same sums in another order, equal to rounding
+    assert np.allclose(oracle.prefill(q, kp, vp, t, L, qs, 0.3), oracle.decode(q, kp, vp, t, L, 0.3),
+                       rtol=1e-13, atol=1e-15)
 
 
 def test_prompt_prefill_equals_causal_sdpa():
@@ -257,7 +260,7 @@ def test_chunked_prefill_rows_match_full_prefill():
     q, kp, vp, t, lens, qs = _prefill_case(rng, [45], [45], 4, 4, 8)
     full = oracle.prefill(q, kp, vp, t, lens, qs, 0.4)
     tail = oracle.prefill(q[30:], kp, vp, t, lens, np.array([0, 15]), 0.4)
-    assert np.array_equal(tail, full[30:])
+    assert np.allclose(tail, full[30:], rtol=1e-13, atol=1e-15)
 
 
 def test_prefill_last_row_sees_everything_first_row_sees_the_prefix():
@@ -286,3 +289,17 @@ def test_prefill_brute_force_tables_and_poison():
         vp = place(V, table, B, nb + 2, fill=np.nan)
         out = oracle.prefill(q, kp, vp, np.array([table]), np.array([L]), np.array([0, 3]), 0.7)
         assert np.allclose(out, ref.transpose(1, 0, 2), rtol=1e-12, atol=1e-14)
+
+
+def test_causal_attention_rows_are_attend_over_their_prefix():
+    # row i of a causal block is plain attention over keys 0 .. first + i
+    rng = np.random.default_rng(25)
+    Q = rng.standard_normal((6, 8))
+    K = rng.standard_normal((11, 8))
+    V = rng.standard_normal((11, 8))
+    out = oracle.causal_attention(Q, K, V, 5, 0.6)
+    for i in range(6):
+        ref = oracle.attend(Q[i], K[:6 + i], V[:6 + i], 0.6)
+        assert np.allclose(out[i], ref, rtol=1e-13, atol=1e-15)
+    with pytest.raises(ValueError):
+        oracle.causal_attention(Q, K, V, 6, 0.6)     # the last row would sit past the keys

@@ -200,7 +200,12 @@ size_t pa_decode_workspace_bytes(int S, int Hq, int Hkv, int D, int B, int max_c
  *
  * where K_t, V_t are token t's rows for KV head h / (Hq/Hkv), read from
  * physical block block_tables[s][t / B] at offset t % B. fp16 inputs, fp32
- * arithmetic, fp16 output rounded to nearest even. L_s = 0 gives zeros.
+ * scores, maxima and sums, fp16 output rounded to nearest even. For groups of
+ * one or two query heads per KV head the weighted sum of values is fp32 as
+ * well; for groups of four and eight (the matrix-core path) each softmax
+ * weight, at most 2^8 before normalisation, is rounded to fp16 for the
+ * product with V (fp32 accumulation). L_s = 0 gives zeros. Any finite scale,
+ * of either sign, is supported.
  * Slots past L_s in the last block and blocks the table does not name are
  * never read into the result, whatever they hold (NaN and Inf included).
  * The summation order depends only on logical token positions, so relabelling
@@ -213,7 +218,7 @@ size_t pa_decode_workspace_bytes(int S, int Hq, int Hkv, int D, int B, int max_c
  *   block_tables      device int32 [S][MB]
  *   context_lens      device int32 [S], 0 <= L_s <= min(max_context_len, MB * B)
  *   max_context_len   host bound on every L_s (sizes the launch)
- *   scale             softmax scale, usually 1/sqrt(D)
+ *   scale             softmax scale, finite (either sign), usually 1/sqrt(D)
  *   partition_size    tokens per context partition: 0 = library choice, else a
  *                     positive multiple of 16 (a partition may start inside a
  *                     block)
@@ -247,8 +252,9 @@ pa_status pa_decode(void* out, const void* query, const void* k_pool, const void
  *
  * with K_t, V_t read for KV head h / (Hq/Hkv) from block block_tables[s][t / B]
  * at offset t % B. A cached prefix (L_s > n_s) is attended in full. fp16
- * inputs, fp32 scores and sums, softmax weights rounded to fp16 for the
- * weighted sum of values (fp32 accumulation), fp16 output. Slots past L_s are
+ * inputs, fp32 scores and sums, softmax weights (at most 2^8 before
+ * normalisation) rounded to fp16 for the weighted sum of values (fp32
+ * accumulation), fp16 output. Slots past L_s are
  * never read into the result, whatever they hold; keys and values of the
  * tokens 0 .. L_s - 1 must be finite.
  *
@@ -260,7 +266,7 @@ pa_status pa_decode(void* out, const void* query, const void* k_pool, const void
  *   context_lens      device int32 [S], n_s <= L_s <= MB * B
  *   query_start       device int32 [S + 1], non-decreasing, query_start[S] <= T
  *   max_query_len     host bound on every n_s (sizes the launch)
- *   scale             softmax scale, finite and >= 0, usually 1/sqrt(D)
+ *   scale             softmax scale, finite (either sign), usually 1/sqrt(D)
  * Supported: D = 128; B = 8 or a multiple of 16; Hq / Hkv in {1, 2, 4, 8}. S = 0 or
  * max_query_len = 0 is a no-op. Caller errors the kernel can see are contained,
  * never an access outside the buffers: a sequence whose query range leaves

@@ -45,7 +45,6 @@ _lib.pa_decode_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i]
 _lib.pa_decode.restype = _i
 _lib.pa_decode.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i,
                            ctypes.c_float, _i, _p, ctypes.c_size_t, _p]
-
 _lib.pa_prefill.restype = _i
 _lib.pa_prefill.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _i,
                             ctypes.c_float, _p]
@@ -116,6 +115,21 @@ def _rows(t, name, n, fn):
     sizes passed to the library would be read past their end."""
     if t is not None and (t.dim() == 0 or t.shape[0] != n):
         raise ValueError(f"{fn}: {name} needs {n} rows, has {tuple(t.shape)}")
+
+
+def _dims(t, n, name, fn):
+    if t.dim() != n:
+        raise ValueError(f"{fn}: {name} must have {n} dimensions, got {tuple(t.shape)}")
+
+
+def _pools_fit(k_pool, v_pool, D, fn):
+    """Both pools [NB, Hkv, B, D] with the head dimension of the query: a pool
+    whose rows are shorter than the query's would be read past its end."""
+    _dims(k_pool, 4, "k_pool", fn)
+    _same_shape(k_pool, v_pool, "k_pool/v_pool")
+    if k_pool.shape[3] != D:
+        raise ValueError(f"{fn}: pool rows of {k_pool.shape[3]} values do not match the query's "
+                         f"head dimension {D}")
 
 
 def _pairs(t, fn):
@@ -215,7 +229,10 @@ def pa_decode_workspace_bytes(S, Hq, Hkv, D, B, max_context_len, partition_size=
 def pa_decode(query, k_pool, v_pool, block_tables, context_lens, max_context_len: int,
               scale: float, partition_size: int = 0, out=None, workspace=None, stream=None):
     """Paged decode attention; returns out fp16 [S, Hq, D]."""
+    _dims(query, 3, "query", "pa_decode")
+    _dims(block_tables, 2, "block_tables", "pa_decode")
     S, Hq, D = query.shape
+    _pools_fit(k_pool, v_pool, D, "pa_decode")
     NB, Hkv, B, _ = k_pool.shape
     MB = block_tables.shape[1]
     if out is None:
@@ -240,14 +257,18 @@ def pa_decode(query, k_pool, v_pool, block_tables, context_lens, max_context_len
 def pa_prefill(query, k_pool, v_pool, block_tables, context_lens, query_start,
                max_query_len: int, scale: float, out=None, stream=None):
     """Paged causal prefill attention of packed new tokens; returns out fp16 [T, Hq, D]."""
+    _dims(query, 3, "query", "pa_prefill")
+    _dims(block_tables, 2, "block_tables", "pa_prefill")
     T, Hq, D = query.shape
+    _pools_fit(k_pool, v_pool, D, "pa_prefill")
     NB, Hkv, B, _ = k_pool.shape
     S, MB = block_tables.shape
     if out is None:
         out = torch.empty_like(query)
     _same_shape(out, query, "out/query")
     _same_shape(k_pool, v_pool, "k_pool/v_pool")
-    if context_lens.shape[0] != S or query_start.shape[0] != S + 1:
+    if context_lens.dim() != 1 or query_start.dim() != 1 or context_lens.shape[0] != S or \
+            query_start.shape[0] != S + 1:
         raise ValueError("pa_prefill: context_lens needs S entries and query_start S + 1")
     _check("pa_prefill", _lib.pa_prefill(
         _arg(out, "out", _F16), _arg(query, "query", _F16), _arg(k_pool, "k_pool", _F16),
@@ -363,4 +384,5 @@ class BlockManager:
 
 __all__ = ["PaError", "lib", "LIB_PATH", "pa_version", "pa_slot_mapping", "pa_write_kv",
            "pa_copy_blocks", "pa_decode_partition_size", "pa_decode_workspace_bytes",
-           "pa_decode", "pa_prefill", "pa_swap_blocks", "pa_stream_read", "BlockManager"]
+           "pa_decode", "pa_prefill",
+           "pa_swap_blocks", "pa_stream_read", "BlockManager"]

@@ -362,8 +362,7 @@ pa_status pa_prefill(void* out, const void* query, const void* k_pool, const voi
                 pa::kDecodeUnit);
   if (G != 1 && G != 2 && G != 4 && G != 8)
     return fail(PA_ERR_UNSUPPORTED, "pa_prefill: Hq/Hkv=%d (supported: 1, 2, 4, 8)", G);
-  if (!std::isfinite(scale) || scale < 0.f)
-    return fail(PA_ERR_SHAPE, "pa_prefill: scale must be finite and >= 0");
+  if (!std::isfinite(scale)) return fail(PA_ERR_SHAPE, "pa_prefill: scale is not finite");
   // workgroups of kPrefillWaves waves, padded to a multiple of 8 at launch
   const int64_t grid = pa::prefill_work_items(G, S, Hkv, max_query_len);
   if (!dispatch_fits(grid + 7, pa::kPrefillWaves * 64))

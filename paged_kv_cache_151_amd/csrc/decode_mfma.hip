@@ -123,6 +123,14 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeArgs a
   const int blk0 = kSplit ? 2 * U0 : U0 / UPB;
   const int nblk = kSplit ? (len + 7) / 8 : (U0 + nunits - 1) / UPB - blk0 + 1;
 
+  // The lazy maximum below is taken on unscaled scores, which keeps their
+  // order only for a scale >= 0. A negative scale is applied as |scale| to the
+  // negated queries instead: flipping the fp16 sign bits is exact, so every
+  // score changes sign exactly and scale * score is unchanged.
+  const bool neg_scale = a.scale_log2 < 0.f;
+  const float sl2 = neg_scale ? -a.scale_log2 : a.scale_log2;
+  const unsigned qflip = neg_scale ? 0x80008000u : 0u;
+
   // query heads as B operands: slice c holds dims 32c + 8kq .. +7 of head m
   h8 qf[4];
 #pragma unroll
@@ -130,7 +138,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeArgs a
     const u32x4 raw = m < G ? *reinterpret_cast<const u32x4*>(
                                   a.q + ((int64_t)s * a.Hq + hq0 + m) * D + 32 * c + 8 * kq)
                             : u32x4{0, 0, 0, 0};
-    qf[c] = __builtin_bit_cast(h8, raw);
+    qf[c] = __builtin_bit_cast(h8, raw ^ qflip);
   }
   f4 o[8];
 #pragma unroll
@@ -252,11 +260,11 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeArgs a
         vis[r] = 4 * kq + r < valid;
         mx = __builtin_fmaxf(mx, vis[r] ? sc[r] : kNegBigG);
       }
-      const float mloc = mx > 0.5f * kNegBigG ? mx * a.scale_log2 : kNegBigG;
+      const float mloc = mx > 0.5f * kNegBigG ? mx * sl2 : kNegBigG;
       if (__builtin_amdgcn_ballot_w64(mloc > mrow + kSlackG)) {
         mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16));
         mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
-        const float mcand = mx > 0.5f * kNegBigG ? mx * a.scale_log2 : kNegBigG;
+        const float mcand = mx > 0.5f * kNegBigG ? mx * sl2 : kNegBigG;
         const float mnew = __builtin_fmaxf(mrow, mcand);
         const float alpha = __builtin_amdgcn_exp2f(mrow - mnew);
         mrow = mnew;
@@ -267,7 +275,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeArgs a
       h4 pb;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], a.scale_log2, -mrow));
+        float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], sl2, -mrow));
         pr = vis[r] ? pr : 0.f;
         lsum += pr;
         pb[r] = (_Float16)pr;

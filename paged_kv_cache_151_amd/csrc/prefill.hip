@@ -213,6 +213,14 @@ void prefill_kernel(const PrefillArgs a) {
   kend = kend < 0 ? 0 : kend;
   const int nchunk = wave_rows ? (kend + KC - 1) / KC : 0;
 
+  // The lazy maximum below is taken on unscaled scores, which keeps their
+  // order only for a scale >= 0. A negative scale is applied as |scale| to the
+  // negated queries instead: flipping the fp16 sign bits is exact, so every
+  // score changes sign exactly and scale * score is unchanged.
+  const bool neg_scale = a.scale_log2 < 0.f;
+  const float sl2 = neg_scale ? -a.scale_log2 : a.scale_log2;
+  const unsigned qflip = neg_scale ? 0x80008000u : 0u;
+
   // query rows as B operands
   h8 qf[QT][4];
   int pos[QT];
@@ -225,7 +233,7 @@ void prefill_kernel(const PrefillArgs a) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const u32x4 raw = ok ? *reinterpret_cast<const u32x4*>(qrow + 32 * c) : u32x4{0, 0, 0, 0};
-      qf[t][c] = __builtin_bit_cast(h8, raw);
+      qf[t][c] = __builtin_bit_cast(h8, raw ^ qflip);
     }
   }
 
@@ -373,9 +381,9 @@ void prefill_kernel(const PrefillArgs a) {
           acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[u][cc], qf[t][cc], acc, 0, 0, 0);
         sc[u] = acc;
       }
-      // Raw scores; the maximum is taken before scaling (the scale is
-      // non-negative, so the order is kept) and p = 2^(scale_log2 * s - m) is
-      // one fused multiply-add and one exp2 per score.
+      // Raw scores; the maximum is taken before scaling (sl2 >= 0, so the
+      // order is kept) and p = 2^(sl2 * s - m) is one fused multiply-add and
+      // one exp2 per score.
       float x[4 * NU];
       bool vis[4 * NU];
       float mx = kNegBig;
@@ -394,11 +402,11 @@ void prefill_kernel(const PrefillArgs a) {
       // bound exactly when one of its lanes' maxima does, so the decision is
       // taken on each lane's own maximum; the row maxima are exchanged across
       // lanes only when some row must be raised.
-      const float mloc = mx > 0.5f * kNegBig ? mx * a.scale_log2 : kNegBig;
+      const float mloc = mx > 0.5f * kNegBig ? mx * sl2 : kNegBig;
       if (__builtin_amdgcn_ballot_w64(mloc > mrow[t] + kSlack)) {
         mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16));
         mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
-        const float mcand = mx > 0.5f * kNegBig ? mx * a.scale_log2 : kNegBig;
+        const float mcand = mx > 0.5f * kNegBig ? mx * sl2 : kNegBig;
         const float mnew = __builtin_fmaxf(mrow[t], mcand);
         const float alpha = __builtin_amdgcn_exp2f(mrow[t] - mnew);
         mrow[t] = mnew;
@@ -410,7 +418,7 @@ void prefill_kernel(const PrefillArgs a) {
       h8 pb[NKS];
 #pragma unroll
       for (int j = 0; j < 4 * NU; ++j) {
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(x[j], a.scale_log2, -mrow[t]));
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(x[j], sl2, -mrow[t]));
         p = vis[j] ? p : 0.f;
         ls += p;
         pb[j / 8][j % 8] = (_Float16)p;

@@ -77,6 +77,10 @@ def test_decode_host_validation(lib):
     assert decode(lib, B=40, NB=16, MB=2) == PA_ERR_UNSUPPORTED   # block not a multiple of 16
     assert decode(lib, q=FAKE + 4) == PA_ERR_ALIGN
     assert decode(lib, scale=float("inf")) == PA_ERR_SHAPE
+    assert decode(lib, scale=float("nan")) == PA_ERR_SHAPE
+    # any finite scale, of either sign, passes validation (the next check fails)
+    assert decode(lib, scale=-1.0, out=None) == PA_ERR_NULL
+    assert decode(lib, scale=-1.0, Hq=16, Hkv=2, out=None) == PA_ERR_NULL
     # two partitions need a workspace
     assert decode(lib, P=16) == PA_ERR_WORKSPACE
     assert decode(lib, S=-1) == PA_ERR_SHAPE
@@ -192,7 +196,8 @@ def test_prefill_host_validation(lib):
     assert prefill(lib, out=FAKE + 2) == PA_ERR_ALIGN
     assert prefill(lib, qs=FAKE + 2) == PA_ERR_ALIGN
     assert prefill(lib, scale=float("nan")) == PA_ERR_SHAPE
-    assert prefill(lib, scale=-0.5) == PA_ERR_SHAPE
+    # any finite scale, of either sign, passes validation (the next check fails)
+    assert prefill(lib, scale=-0.5, out=None) == PA_ERR_NULL
     assert prefill(lib, S=0) == PA_OK
     assert prefill(lib, maxq=0, out=None) == PA_OK
 
@@ -281,3 +286,30 @@ def test_binding_refuses_arrays_shorter_than_the_sizes_it_passes():
         pa.pa_stream_read(buf, torch.zeros(1, dtype=i32), nbytes=2048)
     with pytest.raises(ValueError, match="sink needs 4 bytes"):
         pa.pa_stream_read(buf, torch.zeros(2, dtype=torch.uint8))
+
+
+def test_binding_refuses_pools_that_do_not_fit_the_query():
+    # a pool whose rows are shorter than the query's head dimension would be
+    # read past its end by the kernels; a 3-D pool or query is misread
+    import torch
+    import paged_kv_cache_151_amd as pa
+    f16, i32 = torch.float16, torch.int32
+    q = torch.zeros(3, 4, 128, dtype=f16)
+    short = torch.zeros(8, 4, 16, 64, dtype=f16)
+    pool = torch.zeros(8, 4, 16, 128, dtype=f16)
+    tables, lens = torch.zeros(3, 4, dtype=i32), torch.zeros(3, dtype=i32)
+    with pytest.raises(ValueError, match="head dimension 128"):
+        pa.pa_decode(q, short, short, tables, lens, 48, 0.1)
+    with pytest.raises(ValueError, match="differ"):
+        pa.pa_decode(q, pool, short, tables, lens, 48, 0.1)
+    with pytest.raises(ValueError, match="k_pool must have 4 dimensions"):
+        pa.pa_decode(q, pool[0], pool[0], tables, lens, 48, 0.1)
+    with pytest.raises(ValueError, match="query must have 3 dimensions"):
+        pa.pa_decode(q[0], pool, pool, tables, lens, 48, 0.1)
+    qs = torch.zeros(4, dtype=i32)
+    with pytest.raises(ValueError, match="head dimension 128"):
+        pa.pa_prefill(q, short, short, tables, lens, qs, 1, 0.1)
+    with pytest.raises(ValueError, match="block_tables must have 2 dimensions"):
+        pa.pa_prefill(q, pool, pool, tables[0], lens, qs, 1, 0.1)
+    with pytest.raises(ValueError, match="query_start S"):
+        pa.pa_prefill(q, pool, pool, tables, lens, qs[:3], 1, 0.1)

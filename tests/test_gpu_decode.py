@@ -298,35 +298,27 @@ def test_device_errors_are_reported(pa):
         pa.pa_decode(q, pool, pool, dev(c.block_tables), dev(c.context_lens), 48, 0.1)
 
 
-def test_chat_batch128_full_size_sampled(pa):
-    """Full-size layers of the batch-128 chat workload in the benchmark's launch
-    configuration (default partition size); every slot checked bit-exactly,
-    the outputs of sampled sequences (all heads) against the oracle, which gets
-    the pre-write blocks of those sequences and performs its own write."""
+def test_chat_batch128_full_size_every_output(pa):
+    """Full-size layers 0 and 31 of the batch-128 chat workload in the
+    benchmark's launch configuration (default partition size): every slot
+    checked bit-exactly, every (sequence, head, dimension) of the output
+    against the oracle, which gets the pools as they were before the step and
+    performs its own write of the new tokens."""
     lengths = W.chat_lengths()
-    order = np.argsort(lengths)
-    sample = sorted({int(order[0]), int(order[-1]), int(order[len(order) // 2]), 5, 77, 126})
     for layer in (0, W.CHAT_LAYERS - 1):
         c = W.chat_layer(layer, lengths=lengths)
         say(c.name, f"NB={c.NB} maxL={c.max_context_len}")
         kp, vp = W.device_pools(c.NB, c.Hkv, c.B, c.D, seed=W.chat_pool_seed(layer))
-        before = {}
-        for s in sample:
-            ids = c.block_tables[s, :oracle.blocks_for(int(c.context_lens[s]), c.B)]
-            idx = dev(ids.astype(np.int64))
-            before[s] = (ids, host(kp[idx]), host(vp[idx]))
+        k_before, v_before = host(kp), host(vp)
         got, slots = decode_step(pa, c, kp, vp)
-        assert np.array_equal(slots, oracle.decode_slots(c.block_tables, c.context_lens, c.B, c.NB))
-        for s in sample:
-            ids, kb, vb = before[s]
-            nb = len(ids)
-            table = np.arange(nb, dtype=np.int32)[None, :]
-            L = c.context_lens[s:s + 1]
-            sl = oracle.decode_slots(table, L, c.B, nb)
-            k1, v1 = oracle.write_kv(kb, vb, c.key_new[s:s + 1], c.value_new[s:s + 1], sl)
-            ref = oracle.decode(c.query[s:s + 1], k1, v1, table, L, c.scale)
-            assert_attention_close(got[s:s + 1], ref, f"{c.name} seq {s}")
         del kp, vp
+        ref_slots = oracle.decode_slots(c.block_tables, c.context_lens, c.B, c.NB)
+        assert np.array_equal(slots, ref_slots)
+        rk, rv = oracle.write_kv(k_before, v_before, c.key_new, c.value_new, ref_slots)
+        del k_before, v_before
+        ref = oracle.decode(c.query, rk, rv, c.block_tables, c.context_lens, c.scale)
+        del rk, rv
+        assert_attention_close(got, ref, c.name)
 
 
 @pytest.mark.parametrize("B", [48, 64, 128, 256])

@@ -202,27 +202,14 @@ def test_shared_prefix_flow_copy_write_prefill(pa):
     assert_attention_close(got, want, "prefix_prefill")
 
 
-def test_chat_prefill_full_size_sampled(pa):
+def test_chat_prefill_full_size_every_row(pa):
     """The benchmark's batch (16 prompts of 100-2000 tokens, 32 heads, B = 16)
-    in its launch configuration; sampled rows (first, around row-block edges,
-    last) of four sequences, every head, against the oracle's attention over
-    the gathered keys and values."""
+    in its launch configuration: every row, head and dimension of the output
+    against the oracle."""
     c = W.chat_prefill()
     say(c.name, f"T={c.T} NB={c.NB}")
     got = run(pa, c)
-    assert np.all(np.isfinite(got.astype(np.float32)))
-    order = np.argsort(c.new_lens)
-    for s in sorted({int(order[0]), int(order[-1]), int(order[len(order) // 2]), 3}):
-        L, n, q0 = int(c.context_lens[s]), int(c.new_lens[s]), int(c.query_start[s])
-        K = oracle.gather(c.k_pool, c.block_tables[s], L, c.B)
-        V = oracle.gather(c.v_pool, c.block_tables[s], L, c.B)
-        rows = sorted({0, 1, 31, 32, 127, 128, n // 2, n - 2, n - 1})
-        want = np.empty((len(rows), c.Hq, c.D))
-        for i, j in enumerate(rows):
-            p = L - n + j
-            for h in range(c.Hq):
-                want[i, h] = oracle.attend(c.query[q0 + j, h], K[h, :p + 1], V[h, :p + 1], c.scale)
-        assert_attention_close(got[[q0 + j for j in rows]], want, f"chat prefill seq {s}")
+    assert_attention_close(got, ref(c), c.name)
 
 
 def test_long_prompt_after_long_cached_prefix_sampled(pa):

@@ -237,6 +237,28 @@ pa_status pa_decode(void* out, const void* query, const void* k_pool, const void
                     hipStream_t stream);
 
 /*
+ * pa_decode_static — pa_decode for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation. Same arguments, kernels and results (bit for bit) as
+ * pa_decode, minus the workspace: the partials of split sequences go to a
+ * scratch array inside the library, one per GPU, of
+ * pa_decode_static_scratch_bytes() bytes (32 MiB), held from the first call
+ * on that GPU until the process ends. The call allocates nothing (the
+ * array's device address is looked up once per GPU, on the first call made
+ * with that GPU current).
+ *   Returns PA_ERR_WORKSPACE, enqueueing nothing, when the call's partials
+ *   (pa_decode_workspace_bytes of the same sizes) exceed the array.
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one
+ *   GPU (on different streams, or from different threads without ordering)
+ *   race and give unspecified results. Calls ordered on one stream are safe.
+ */
+size_t pa_decode_static_scratch_bytes(void);
+pa_status pa_decode_static(void* out, const void* query, const void* k_pool, const void* v_pool,
+                           const int32_t* block_tables, const int32_t* context_lens, int S,
+                           int Hq, int Hkv, int D, int B, int NB, int MB, int max_context_len,
+                           float scale, int partition_size, hipStream_t stream);
+
+/*
  * pa_prefill — attention of a chunk of new tokens per sequence through the
  * block table, causal ([L], "How PagedAttention works", step 1: the prompt's
  * keys and values live in the blocks the manager handed out; step 4: attend

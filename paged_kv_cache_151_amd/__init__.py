@@ -45,6 +45,12 @@ _lib.pa_decode_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i]
 _lib.pa_decode.restype = _i
 _lib.pa_decode.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i,
                            ctypes.c_float, _i, _p, ctypes.c_size_t, _p]
+_lib.pa_decode_static.restype = _i
+_lib.pa_decode_static.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i,
+                                  ctypes.c_float, _i, _p]
+_lib.pa_decode_static_scratch_bytes.restype = ctypes.c_size_t
+_lib.pa_decode_static_scratch_bytes.argtypes = []
+
 _lib.pa_prefill.restype = _i
 _lib.pa_prefill.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _i,
                             ctypes.c_float, _p]
@@ -254,6 +260,34 @@ def pa_decode(query, k_pool, v_pool, block_tables, context_lens, max_context_len
     return out
 
 
+def pa_decode_static_scratch_bytes() -> int:
+    return _lib.pa_decode_static_scratch_bytes()
+
+
+def pa_decode_static(query, k_pool, v_pool, block_tables, context_lens, max_context_len: int,
+                     scale: float, partition_size: int = 0, out=None, stream=None):
+    """pa_decode with the partials in the library's per-GPU scratch array
+    instead of a workspace (the C call allocates nothing; `out` is allocated
+    here only when not passed). Calls that overlap on one GPU race."""
+    _dims(query, 3, "query", "pa_decode_static")
+    _dims(block_tables, 2, "block_tables", "pa_decode_static")
+    S, Hq, D = query.shape
+    _pools_fit(k_pool, v_pool, D, "pa_decode_static")
+    NB, Hkv, B, _ = k_pool.shape
+    MB = block_tables.shape[1]
+    if out is None:
+        out = torch.empty_like(query)
+    _same_shape(out, query, "out/query")
+    _rows(block_tables, "block_tables", S, "pa_decode_static")
+    _rows(context_lens, "context_lens", S, "pa_decode_static")
+    _check("pa_decode_static", _lib.pa_decode_static(
+        _arg(out, "out", _F16), _arg(query, "query", _F16), _arg(k_pool, "k_pool", _F16),
+        _arg(v_pool, "v_pool", _F16), _arg(block_tables, "block_tables", _I32),
+        _arg(context_lens, "context_lens", _I32), S, Hq, Hkv, D, B, NB, MB,
+        int(max_context_len), float(scale), int(partition_size), _stream(stream)))
+    return out
+
+
 def pa_prefill(query, k_pool, v_pool, block_tables, context_lens, query_start,
                max_query_len: int, scale: float, out=None, stream=None):
     """Paged causal prefill attention of packed new tokens; returns out fp16 [T, Hq, D]."""
@@ -384,5 +418,5 @@ class BlockManager:
 
 __all__ = ["PaError", "lib", "LIB_PATH", "pa_version", "pa_slot_mapping", "pa_write_kv",
            "pa_copy_blocks", "pa_decode_partition_size", "pa_decode_workspace_bytes",
-           "pa_decode", "pa_prefill",
+           "pa_decode", "pa_decode_static", "pa_decode_static_scratch_bytes", "pa_prefill",
            "pa_swap_blocks", "pa_stream_read", "BlockManager"]

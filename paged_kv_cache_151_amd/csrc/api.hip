@@ -7,6 +7,7 @@
 
 #include "pa.h"
 #include "pa_error.h"
+#include "decode_call.h"
 #include "pa_internal.h"
 #include "prefill_internal.h"
 
@@ -72,6 +73,95 @@ int64_t block_chunks(int Hkv, int B, int D) {
 }
 
 }  // namespace
+
+namespace pa {
+
+pa_status decode_prepare(const char* fn, void* out, const void* query, const void* k_pool,
+                         const void* v_pool, const int32_t* block_tables,
+                         const int32_t* context_lens, int S, int Hq, int Hkv, int D, int B, int NB,
+                         int MB, int max_context_len, float scale, int partition_size,
+                         DecodeCall* call) {
+  call->a.S = 0;
+  if (S < 0) return fail(PA_ERR_SHAPE, "%s: S=%d must be >= 0", fn, S);
+  if (Hq <= 0 || Hkv <= 0 || D <= 0 || B <= 0 || NB <= 0 || MB <= 0)
+    return fail(PA_ERR_SHAPE, "%s: Hq=%d Hkv=%d D=%d B=%d NB=%d MB=%d must be > 0", fn, Hq, Hkv,
+                D, B, NB, MB);
+  if (Hq % Hkv) return fail(PA_ERR_SHAPE, "%s: Hq=%d not a multiple of Hkv=%d", fn, Hq, Hkv);
+  if ((int64_t)MB * B >= ((int64_t)1 << 31))
+    return fail(PA_ERR_SHAPE, "%s: MB*B=%lld exceeds int32", fn, (long long)MB * B);
+  if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)MB * B)
+    return fail(PA_ERR_SHAPE, "%s: max_context_len=%d outside [0, MB*B=%lld]", fn,
+                max_context_len, (long long)MB * B);
+  if (partition_size < 0 || (partition_size > 0 && partition_size % kDecodeUnit))
+    return fail(PA_ERR_SHAPE, "%s: partition_size=%d must be 0 or a multiple of %d", fn,
+                partition_size, kDecodeUnit);
+  const int G = Hq / Hkv;
+  if (D != kHeadDim) return fail(PA_ERR_UNSUPPORTED, "%s: D=%d (supported: 128)", fn, D);
+  if (B != 8 && B % kDecodeUnit)
+    return fail(PA_ERR_UNSUPPORTED, "%s: B=%d (supported: 8 and multiples of %d)", fn, B,
+                kDecodeUnit);
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(PA_ERR_UNSUPPORTED, "%s: Hq/Hkv=%d (supported: 1, 2, 4, 8)", fn, G);
+  if (!std::isfinite(scale)) return fail(PA_ERR_SHAPE, "%s: scale is not finite", fn);
+  const int P = pa_decode_partition_size(S, Hq, Hkv, B, max_context_len, partition_size);
+  const int Pmax = max_context_len > 0 ? ceil_div(max_context_len, P) : 1;
+  if (Pmax > kMaxPartitions)
+    return fail(PA_ERR_SHAPE, "%s: %d partitions exceed %d", fn, Pmax, kMaxPartitions);
+  // partition kernel: one workgroup per (partition, sequence, KV head) of
+  // max(waves for the group size, heads / heads per wave) waves; reduce
+  // kernel: one wave per (sequence, query head)
+  const int hpw = G < kDecodeHeadsPerWave ? G : kDecodeHeadsPerWave;
+  const int waves = decode_waves(G) > G / hpw ? decode_waves(G) : G / hpw;
+  const int64_t wgs = (int64_t)Pmax * S * Hkv;
+  if (!dispatch_fits(wgs, waves * 64) || !dispatch_fits((int64_t)S * Hq, 64))
+    return fail(PA_ERR_SHAPE, "%s: launch too large (S=%d Hq=%d, %lld workgroups)", fn, S, Hq,
+                (long long)wgs);
+  if (S == 0) return ok();
+  if (!out || !query || !k_pool || !v_pool || !block_tables || !context_lens)
+    return fail(PA_ERR_NULL, "%s: null pointer argument", fn);
+  if (!aligned(out, 16) || !aligned(query, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16))
+    return fail(PA_ERR_ALIGN, "%s: out/query/pools must be 16-byte aligned", fn);
+  if (!aligned(block_tables, 4) || !aligned(context_lens, 4))
+    return fail(PA_ERR_ALIGN, "%s: block_tables/context_lens misaligned", fn);
+
+  DecodeArgs& a = call->a;
+  a.out = static_cast<_Float16*>(out);
+  a.q = static_cast<const _Float16*>(query);
+  a.k_pool = static_cast<const _Float16*>(k_pool);
+  a.v_pool = static_cast<const _Float16*>(v_pool);
+  a.tables = block_tables;
+  a.lens = context_lens;
+  a.part_acc = nullptr;
+  a.part_ml = nullptr;
+  a.S = S;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.NB = NB;
+  a.MB = MB;
+  a.B = B;
+  a.P = P;
+  a.Pmax = Pmax;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  call->G = G;
+  call->partials_bytes = pa_decode_workspace_bytes(S, Hq, Hkv, D, B, max_context_len, P);
+  if (Pmax > 1 && call->partials_bytes == 0)
+    return fail(PA_ERR_SHAPE, "%s: partials of %d partitions do not fit in size_t", fn, Pmax);
+  return ok();
+}
+
+pa_status decode_enqueue(const char* fn, DecodeCall& call, void* partials, hipStream_t stream) {
+  DecodeArgs& a = call.a;
+  if (call.partials_bytes > 0) {
+    float* ws = static_cast<float*>(partials);
+    a.part_acc = ws;
+    a.part_ml = ws + (size_t)a.S * a.Hq * a.Pmax * kHeadDim;
+  }
+  const hipError_t e = launch_decode(a, a.B, call.G, stream);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "%s launch: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace pa
 
 extern "C" {
 
@@ -270,76 +360,19 @@ pa_status pa_decode(void* out, const void* query, const void* k_pool, const void
                     int Hkv, int D, int B, int NB, int MB, int max_context_len, float scale,
                     int partition_size, void* workspace, size_t workspace_bytes,
                     hipStream_t stream) {
-  if (S < 0) return fail(PA_ERR_SHAPE, "pa_decode: S=%d must be >= 0", S);
-  if (Hq <= 0 || Hkv <= 0 || D <= 0 || B <= 0 || NB <= 0 || MB <= 0)
-    return fail(PA_ERR_SHAPE, "pa_decode: Hq=%d Hkv=%d D=%d B=%d NB=%d MB=%d must be > 0", Hq,
-                Hkv, D, B, NB, MB);
-  if (Hq % Hkv) return fail(PA_ERR_SHAPE, "pa_decode: Hq=%d not a multiple of Hkv=%d", Hq, Hkv);
-  if ((int64_t)MB * B >= ((int64_t)1 << 31))
-    return fail(PA_ERR_SHAPE, "pa_decode: MB*B=%lld exceeds int32", (long long)MB * B);
-  if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)MB * B)
-    return fail(PA_ERR_SHAPE, "pa_decode: max_context_len=%d outside [0, MB*B=%lld]",
-                max_context_len, (long long)MB * B);
-  if (partition_size < 0 || (partition_size > 0 && partition_size % pa::kDecodeUnit))
-    return fail(PA_ERR_SHAPE, "pa_decode: partition_size=%d must be 0 or a multiple of %d",
-                partition_size, pa::kDecodeUnit);
-  const int G = Hq / Hkv;
-  if (D != pa::kHeadDim) return fail(PA_ERR_UNSUPPORTED, "pa_decode: D=%d (supported: 128)", D);
-  if (B != 8 && B % pa::kDecodeUnit)
-    return fail(PA_ERR_UNSUPPORTED, "pa_decode: B=%d (supported: 8 and multiples of %d)", B,
-                pa::kDecodeUnit);
-  if (G != 1 && G != 2 && G != 4 && G != 8)
-    return fail(PA_ERR_UNSUPPORTED, "pa_decode: Hq/Hkv=%d (supported: 1, 2, 4, 8)", G);
-  if (!std::isfinite(scale)) return fail(PA_ERR_SHAPE, "pa_decode: scale is not finite");
-  const int P = pa_decode_partition_size(S, Hq, Hkv, B, max_context_len, partition_size);
-  const int Pmax = max_context_len > 0 ? ceil_div(max_context_len, P) : 1;
-  if (Pmax > pa::kMaxPartitions)
-    return fail(PA_ERR_SHAPE, "pa_decode: %d partitions exceed %d", Pmax, pa::kMaxPartitions);
-  // partition kernel: one workgroup per (partition, sequence, KV head) of
-  // max(waves for the group size, heads / heads per wave) waves; reduce
-  // kernel: one wave per (sequence, query head)
-  const int hpw = G < pa::kDecodeHeadsPerWave ? G : pa::kDecodeHeadsPerWave;
-  const int waves = pa::decode_waves(G) > G / hpw ? pa::decode_waves(G) : G / hpw;
-  const int64_t wgs = (int64_t)Pmax * S * Hkv;
-  if (!dispatch_fits(wgs, waves * 64) || !dispatch_fits((int64_t)S * Hq, 64))
-    return fail(PA_ERR_SHAPE, "pa_decode: launch too large (S=%d Hq=%d, %lld workgroups)", S, Hq,
-                (long long)wgs);
-  if (S == 0) return ok();
-  if (!out || !query || !k_pool || !v_pool || !block_tables || !context_lens)
-    return fail(PA_ERR_NULL, "pa_decode: null pointer argument");
-  if (!aligned(out, 16) || !aligned(query, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16))
-    return fail(PA_ERR_ALIGN, "pa_decode: out/query/pools must be 16-byte aligned");
-  if (!aligned(block_tables, 4) || !aligned(context_lens, 4))
-    return fail(PA_ERR_ALIGN, "pa_decode: block_tables/context_lens misaligned");
-
-  const size_t need = pa_decode_workspace_bytes(S, Hq, Hkv, D, B, max_context_len, P);
+  pa::DecodeCall call;
+  const pa_status st = pa::decode_prepare("pa_decode", out, query, k_pool, v_pool, block_tables,
+                                          context_lens, S, Hq, Hkv, D, B, NB, MB, max_context_len,
+                                          scale, partition_size, &call);
+  if (st != PA_OK || call.a.S == 0) return st;
+  const size_t need = call.partials_bytes;
   if (need > 0) {
     if (!workspace || workspace_bytes < need)
       return fail(PA_ERR_WORKSPACE, "pa_decode: workspace %zu bytes < %zu needed", workspace_bytes,
                   need);
     if (!aligned(workspace, 16)) return fail(PA_ERR_ALIGN, "pa_decode: workspace misaligned");
   }
-
-  pa::DecodeArgs a;
-  a.out = static_cast<_Float16*>(out);
-  a.q = static_cast<const _Float16*>(query);
-  a.k_pool = static_cast<const _Float16*>(k_pool);
-  a.v_pool = static_cast<const _Float16*>(v_pool);
-  a.tables = block_tables;
-  a.lens = context_lens;
-  float* ws = static_cast<float*>(workspace);
-  a.part_acc = need > 0 ? ws : nullptr;
-  a.part_ml = need > 0 ? ws + (size_t)S * Hq * Pmax * D : nullptr;
-  a.S = S;
-  a.Hq = Hq;
-  a.Hkv = Hkv;
-  a.NB = NB;
-  a.MB = MB;
-  a.B = B;
-  a.P = P;
-  a.Pmax = Pmax;
-  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
-  return hip_status(pa::launch_decode(a, B, G, stream), "pa_decode launch");
+  return pa::decode_enqueue("pa_decode", call, workspace, stream);
 }
 
 pa_status pa_prefill(void* out, const void* query, const void* k_pool, const void* v_pool,

@@ -313,3 +313,20 @@ def test_binding_refuses_pools_that_do_not_fit_the_query():
         pa.pa_prefill(q, pool, pool, tables[0], lens, qs, 1, 0.1)
     with pytest.raises(ValueError, match="query_start S"):
         pa.pa_prefill(q, pool, pool, tables, lens, qs[:3], 1, 0.1)
+
+
+def test_static_decode_refuses_partials_beyond_its_scratch(lib):
+    # the size check comes before the library touches the device
+    lib.pa_decode_static_scratch_bytes.restype = ctypes.c_size_t
+    cap = lib.pa_decode_static_scratch_bytes()
+    assert cap == 32 << 20
+    v = ctypes.c_void_p
+    S, H, MB, maxL, P = 128, 32, 2000, 32000, 16     # 2000 partitions of partials per head
+    need = lib.pa_decode_workspace_bytes(S, H, H, 128, 16, maxL, P)
+    assert need > cap
+    st = lib.pa_decode_static(v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(FAKE), S, H, H, 128,
+                              16, 4096, MB, maxL, F(0.1), P, None)
+    assert st == PA_ERR_WORKSPACE
+    assert b"static scratch" in lib.pa_last_error()
+    assert lib.pa_decode_static(None, v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(FAKE), 2, 4, 4, 128,
+                                16, 16, 3, 48, F(0.1), 0, None) == PA_ERR_NULL

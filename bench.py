@@ -285,16 +285,16 @@ def bench_block_manager(args):
     us = (time.perf_counter() - t0) / args.steps * 1e6
     # the oracle's manager on the same work (prefill excluded from its timing too)
     ref = oracle.BlockManager(NB, B)
-    tables = [[] for _ in range(S)]
-    for t, L in zip(tables, lengths):
+    seqs_ref = [ref.new_sequence() for _ in range(S)]
+    for q, L in zip(seqs_ref, lengths):
         for _ in range(int(L) - 1):
-            ref.append_token(t)
+            ref.append(q)
     n_ref = max(1, min(args.steps, 20))
     t0 = time.perf_counter()
     for _ in range(n_ref):
-        for t in tables:
-            ref.append_token(t)
-        np.array([t + [-1] * (MB - len(t)) for t in tables], np.int32)
+        for q in seqs_ref:
+            ref.append(q)
+        np.array([q.blocks + [-1] * (MB - len(q.blocks)) for q in seqs_ref], np.int32)
     ref_us = (time.perf_counter() - t0) / n_ref * 1e6
     res = {
         "metric": "host block manager: one decode step of bookkeeping (append + export), batch 128",

@@ -3,18 +3,21 @@
 //
 // [L] "Paged Attention: OS-Inspired Memory Management for KV Caches":
 //     "How PagedAttention works" (prefill takes just enough blocks, new tokens
-//     fill the last block, a full last block triggers one more, blocks go back
-//     to the free list when the request ends), "Memory sharing across
-//     requests" (reference counts, copy-on-write of a shared block before a
-//     write), "Practice: try it yourself" (the same manager in miniature).
+//     go into the last block, one more block is taken only when a token's slot
+//     lies past the last one, blocks go back to the free list when the request
+//     ends), "Memory sharing across requests" (a count of users per block;
+//     before a token is written into a block that others use, the writer gets
+//     a copy of it, its table is repointed and the original's count drops).
 //
-// Host memory only; no GPU call is made here. The device-side copy that a
-// copy-on-write decision requires is reported as a (src, dst) pair for
-// pa_copy_blocks.
+// A sequence is its block table plus its token count: token t sits in table
+// entry t / B at offset t % B, so the slot of the next token, and whether it
+// needs a new block, follow from the count alone. Host memory only; no GPU
+// call is made here. The device-side copy that a copy-on-write decision
+// requires is reported as a (src, dst) pair for pa_copy_blocks.
 #include <cstdint>
-#include <deque>
+#include <functional>
 #include <new>
-#include <set>
+#include <queue>
 #include <vector>
 
 #include "pa.h"
@@ -24,30 +27,39 @@ struct pa_block_manager {
   struct Seq {
     bool live = false;
     std::vector<int32_t> table;   // physical block of logical block i
-    int64_t tokens = 0;
+    int64_t tokens = 0;           // tokens written; the next one goes to position `tokens`
   };
 
   int num_blocks = 0;
   int block_size = 0;
   int max_blocks_per_seq = 0;
-  std::deque<int32_t> free_list;  // handed out from the front, returned to the back
-  std::vector<int32_t> refs;      // sequences using each block (0 = free)
-  std::vector<int32_t> fill;      // slots of each block already written
+  std::vector<int32_t> users;     // sequences using each block (0 = free)
+  // free blocks in a ring, oldest first: taken from the head, returned behind
+  // the last one (every block is free at most once, so num_blocks slots suffice)
+  std::vector<int32_t> ring;
+  int64_t head = 0;
+  int64_t n_free = 0;
   std::vector<Seq> seqs;
-  std::set<int> free_ids;         // released sequence ids, reused smallest first
+  // released sequence ids, smallest first
+  std::priority_queue<int, std::vector<int>, std::greater<int>> spare_ids;
 
-  int32_t take() {
-    const int32_t b = free_list.front();
-    free_list.pop_front();
-    refs[b] = 1;
-    fill[b] = 0;
+  int32_t take_block() {
+    const int32_t b = ring[head];
+    head = (head + 1) % num_blocks;
+    --n_free;
+    users[b] = 1;
     return b;
   }
 
+  void return_block(int32_t b) {
+    ring[(head + n_free) % num_blocks] = b;
+    ++n_free;
+  }
+
   int new_id() {
-    if (!free_ids.empty()) {
-      const int id = *free_ids.begin();
-      free_ids.erase(free_ids.begin());
+    if (!spare_ids.empty()) {
+      const int id = spare_ids.top();
+      spare_ids.pop();
       return id;
     }
     seqs.emplace_back();
@@ -92,9 +104,10 @@ pa_status pa_bm_create(int num_blocks, int block_size, int max_blocks_per_seq,
       bm->num_blocks = num_blocks;
       bm->block_size = block_size;
       bm->max_blocks_per_seq = max_blocks_per_seq > 0 ? max_blocks_per_seq : num_blocks;
-      bm->refs.assign(num_blocks, 0);
-      bm->fill.assign(num_blocks, 0);
-      for (int b = 0; b < num_blocks; ++b) bm->free_list.push_back(b);
+      bm->users.assign(num_blocks, 0);
+      bm->ring.resize(num_blocks);
+      for (int b = 0; b < num_blocks; ++b) bm->ring[b] = b;
+      bm->n_free = num_blocks;
     } catch (...) {
       delete bm;
       throw;
@@ -128,7 +141,7 @@ pa_status pa_bm_fork(pa_block_manager* bm, int parent, int* child) {
     c.table = bm->seqs[parent].table;
     c.tokens = bm->seqs[parent].tokens;
     const int id = bm->new_id();
-    for (int32_t b : c.table) bm->refs[b] += 1;
+    for (int32_t b : c.table) bm->users[b] += 1;
     bm->seqs[id] = std::move(c);
     *child = id;
     return ok();
@@ -151,35 +164,33 @@ pa_status pa_bm_append_tokens(pa_block_manager* bm, const int* seq_ids, int n, i
       const int id = seq_ids[i];
       if (!bm->valid(id)) return fail(PA_ERR_STATE, "pa_bm_append_tokens: no live sequence %d", id);
       pa_block_manager::Seq& q = bm->seqs[id];
-      const int32_t last = q.table.empty() ? -1 : q.table.back();
-      if (last < 0 || bm->fill[last] == B) {
-        // no block yet, or the last one is full: take one more
+      const int64_t j = q.tokens / B;          // table entry of the new token
+      const int32_t off = (int32_t)(q.tokens % B);
+      if (j == (int64_t)q.table.size()) {
+        // the position lies past the last block: allocate on demand
         if ((int)q.table.size() >= bm->max_blocks_per_seq)
           return fail(PA_ERR_STATE, "pa_bm_append_tokens: sequence %d has %d blocks (maximum)", id,
                       (int)q.table.size());
-        if (bm->free_list.empty())
+        if (bm->n_free == 0)
           return fail(PA_ERR_EXHAUSTED, "pa_bm_append_tokens: no free block (token %d)", i);
-        q.table.reserve(q.table.size() + 1);   // may throw: before the block leaves the list
-        q.table.push_back(bm->take());
-      } else if (bm->refs[last] > 1) {
-        // the last block is shared: copy it before writing
-        if (bm->free_list.empty())
+        q.table.reserve(q.table.size() + 1);   // may throw: before the block leaves the ring
+        q.table.push_back(bm->take_block());
+      } else if (bm->users[q.table[j]] > 1) {
+        // the block is shared: the writer gets its own copy first
+        if (bm->n_free == 0)
           return fail(PA_ERR_EXHAUSTED, "pa_bm_append_tokens: no free block for a copy (token %d)", i);
         if (*n_copies >= max_copies)
           return fail(PA_ERR_SHAPE, "pa_bm_append_tokens: more than %d copies", max_copies);
-        const int32_t fresh = bm->take();
-        bm->fill[fresh] = bm->fill[last];
-        bm->refs[last] -= 1;
-        copy_pairs[2 * *n_copies] = last;
-        copy_pairs[2 * *n_copies + 1] = fresh;
+        const int32_t shared = q.table[j];
+        const int32_t own = bm->take_block();
+        bm->users[shared] -= 1;
+        copy_pairs[2 * *n_copies] = shared;
+        copy_pairs[2 * *n_copies + 1] = own;
         *n_copies += 1;
-        q.table.back() = fresh;
+        q.table[j] = own;
       }
-      const int32_t blk = q.table.back();
-      const int32_t off = bm->fill[blk];
-      bm->fill[blk] = off + 1;
+      slots[i] = (int64_t)q.table[j] * B + off;
       q.tokens += 1;
-      slots[i] = (int64_t)blk * B + off;
       *n_applied = i + 1;
     }
     return ok();
@@ -190,13 +201,12 @@ pa_status pa_bm_release(pa_block_manager* bm, int seq_id, int* n_freed) {
   if (!bm) return fail(PA_ERR_NULL, "pa_bm_release: null manager");
   if (!bm->valid(seq_id)) return fail(PA_ERR_STATE, "pa_bm_release: no live sequence %d", seq_id);
   return guarded("pa_bm_release", [&]() {
-    bm->free_ids.insert(seq_id);   // first: a failed insert leaves the sequence as it was
+    bm->spare_ids.push(seq_id);   // first: a failed push leaves the sequence as it was
     pa_block_manager::Seq& q = bm->seqs[seq_id];
     int freed = 0;
     for (int32_t b : q.table) {
-      if (--bm->refs[b] == 0) {
-        bm->fill[b] = 0;
-        bm->free_list.push_back(b);
+      if (--bm->users[b] == 0) {
+        bm->return_block(b);
         ++freed;
       }
     }
@@ -241,11 +251,11 @@ pa_status pa_bm_export(const pa_block_manager* bm, const int* seq_ids, int n, in
   return ok();
 }
 
-int pa_bm_num_free(const pa_block_manager* bm) { return bm ? (int)bm->free_list.size() : -1; }
+int pa_bm_num_free(const pa_block_manager* bm) { return bm ? (int)bm->n_free : -1; }
 
 int pa_bm_refcount(const pa_block_manager* bm, int block) {
   if (!bm || block < 0 || block >= bm->num_blocks) return -1;
-  return bm->refs[block];
+  return bm->users[block];
 }
 
 }  // extern "C"

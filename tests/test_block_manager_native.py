@@ -110,12 +110,12 @@ def _run_random(pa, seed, n_ops=400, NB=40, B=4):
     rng = np.random.default_rng(seed)
     nat = pa.BlockManager(NB, B)
     ref = oracle.BlockManager(NB, B)
-    live = {}            # native id -> oracle table (list)
+    live = {}            # native id -> oracle sequence
     for _ in range(n_ops):
         op = rng.random()
         if op < 0.15 or not live:
             sid = nat.add_sequence()
-            live[sid] = []
+            live[sid] = ref.new_sequence()
         elif op < 0.25:
             parent = int(rng.choice(list(live)))
             sid = nat.fork(parent)
@@ -123,14 +123,14 @@ def _run_random(pa, seed, n_ops=400, NB=40, B=4):
         elif op < 0.35 and len(live) > 1:
             sid = int(rng.choice(list(live)))
             freed = nat.release(sid)
-            assert freed == len(ref.release(live.pop(sid)))
+            assert freed == len(ref.free(live.pop(sid)))
         else:
             ids = [int(x) for x in rng.choice(list(live), size=int(rng.integers(1, 6)))]
             copies_before = len(ref.copies)
             want_slots = []
             try:
                 for sid in ids:
-                    want_slots.append(ref.append_token(live[sid]))
+                    want_slots.append(ref.append(live[sid]))
                 exhausted = False
             except oracle.PoolExhausted:
                 exhausted = True
@@ -145,12 +145,12 @@ def _run_random(pa, seed, n_ops=400, NB=40, B=4):
                 slots, copies = nat.append_tokens(ids)
                 assert slots.tolist() == want_slots
                 assert [tuple(p) for p in copies.tolist()] == want_copies
-        for sid, table in live.items():
-            row, _ = nat.table(sid)
-            assert row.tolist() == table
-        assert nat.num_free() == len(ref.free)
+        for sid, seq in live.items():
+            row, n_tokens = nat.table(sid)
+            assert row.tolist() == seq.blocks and n_tokens == seq.length
+        assert nat.num_free() == len(ref.free_list)
         for b in range(NB):
-            assert nat.refcount(b) == ref.refs.get(b, 0)
+            assert nat.refcount(b) == ref.refcount(b)
 
 
 @pytest.mark.parametrize("seed", range(6))

@@ -144,7 +144,7 @@ class Managed:
         vals = W.f16_normal(self.rng, (len(nat_ids), self.H, self.D))
         slots, copies = self.nat.append_tokens(nat_ids)
         c0 = len(self.ref.copies)
-        ref_slots = [self.ref.append_token(t) for t in ref_tables]
+        ref_slots = [self.ref.append(t) for t in ref_tables]
         assert slots.tolist() == ref_slots
         assert [tuple(p) for p in copies.tolist()] == self.ref.copies[c0:]
         if len(copies):
@@ -163,7 +163,8 @@ class Managed:
         out = host(self.pa.pa_decode(dev(q), self.kp, self.vp, dev(tables), dev(lens),
                                      int(lens.max()), 0.088))
         want = oracle.decode(q, self.rk, self.rv,
-                             np.array([t + [-1] * (MB - len(t)) for t in ref_tables], np.int32),
+                             np.array([t.blocks + [-1] * (MB - len(t.blocks)) for t in ref_tables],
+                                      np.int32),
                              lens, 0.088)
         assert_attention_close(out, want, what)
         return tables, lens
@@ -176,14 +177,14 @@ def test_native_block_manager_drives_the_device_path(pa):
     with its own manager, write, copy and decode."""
     m = Managed(pa, np.random.default_rng(77), 96, 4, 16, 128)
     prompt = m.nat.add_sequence()
-    rprompt = []
+    rprompt = m.ref.new_sequence()
     say("native manager: 37-token prompt, 5 samples, 21 steps")
     for _ in range(37):
         m.step([prompt], [rprompt])
     samples = [m.nat.fork(prompt) for _ in range(5)]
     rsamples = [m.ref.fork(rprompt) for _ in range(5)]
     m.nat.release(prompt)
-    m.ref.release(rprompt)
+    m.ref.free(rprompt)
     for _ in range(21):
         m.step(samples, rsamples)
     _, lens = m.check_decode(samples, rsamples, 6, "managed samples")
@@ -202,20 +203,20 @@ def test_beam_search_flow_drives_the_device_path(pa):
     NB = 128
     m = Managed(pa, np.random.default_rng(78), NB, 4, 16, 128)
     prompt = m.nat.add_sequence()
-    rprompt = []
+    rprompt = m.ref.new_sequence()
     say("beam search: 29-token prompt, 4 beams, 12 steps, prune and refork every 4")
     for _ in range(29):
         m.step([prompt], [rprompt])
     beams = [m.nat.fork(prompt) for _ in range(4)]
     rbeams = [m.ref.fork(rprompt) for _ in range(4)]
     m.nat.release(prompt)
-    m.ref.release(rprompt)
+    m.ref.free(rprompt)
     for t in range(12):
         m.step(beams, rbeams)
         if t % 4 == 3:
             for i in (1, 3):
                 m.nat.release(beams[i])
-                m.ref.release(rbeams[i])
+                m.ref.free(rbeams[i])
             beams, rbeams = [beams[0], beams[2]], [rbeams[0], rbeams[2]]
             beams += [m.nat.fork(b) for b in beams]
             rbeams += [m.ref.fork(r) for r in rbeams]

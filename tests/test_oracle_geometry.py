@@ -24,8 +24,10 @@ def test_seed7_simulation_matches_printed_output():
     assert round(100 * oracle.paged_waste(lengths, B), 1) == g["paged_waste_pct_1dp"]
     n0 = oracle.blocks_for(lengths[0], B)
     assert n0 == g["request0_blocks"]
-    free = list(rng.permutation(400))
-    table = [int(free.pop()) for _ in range(n0)]
+    # the printed table is the request's n0 blocks taken one at a time from
+    # the end of a shuffled list of 400 ids, after the lengths were drawn
+    shuffled = rng.permutation(400)
+    table = [int(b) for b in shuffled[::-1][:n0]]
     assert table[:6] == g["request0_table_head"]
     t = g["token"]
     assert oracle.logical_block(t, B) == g["token_logical_block"]

@@ -63,6 +63,10 @@ def parse():
                              "swap", "prefill", "prefix_prefill"])
     ap.add_argument("--layers", type=int, default=32, help="chat workload: layers per step")
     ap.add_argument("--block-size", type=int, default=16, help="chat workload: tokens per block")
+    ap.add_argument("--q-heads", type=int, default=32, help="chat workload: query heads")
+    ap.add_argument("--kv-heads", type=int, default=32,
+                    help="chat workload: KV heads (8 with 32 or 64 query heads: grouped-query "
+                         "variants)")
     ap.add_argument("--contiguous", action="store_true",
                     help="chat workload: one block per sequence sized for the longest one "
                          "(the pre-paging layout), for comparison")
@@ -75,7 +79,9 @@ def parse():
                          "mapping, K/V store, decode) in a HIP graph and time graph replays; the "
                          "per-call roofline events stay eager")
     ap.add_argument("--prompts", type=int, default=16, help="prefill workload: prompts per step")
-    ap.add_argument("--cpu-sample-layers", type=int, default=2)
+    ap.add_argument("--cpu-sample-layers", type=int, default=4,
+                    help="chat workload: layers the oracle decodes for cpu_baseline, evenly spaced "
+                         "(32 = every layer of the step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-reference-mb", type=int, default=0,
                     help="after timing, run one plain device-to-device copy of this many MiB "
@@ -179,10 +185,13 @@ def build_chat(args, dev):
     lengths = W.chat_lengths()
     layers = []
     for layer in range(args.layers):
-        c = W.chat_layer(layer, lengths=lengths, B=args.block_size, contiguous=args.contiguous)
+        c = W.chat_layer(layer, lengths=lengths, B=args.block_size, contiguous=args.contiguous,
+                         Hq=args.q_heads, Hkv=args.kv_heads)
         kp, vp = W.device_pools(c.NB, c.Hkv, c.B, c.D, seed=W.chat_pool_seed(layer))
         layers.append(_upload(c, kp, vp, dev))
     desc = "chat decode, batch 128, 32 layers (prompt U[100,2000] + generated U[50,500])"
+    if (args.q_heads, args.kv_heads) != (32, 32):
+        desc += f" -- GROUPED heads: {args.q_heads} query / {args.kv_heads} KV"
     if args.layers != 32:
         desc += f" -- REDUCED to {args.layers} layers"
     if args.contiguous:
@@ -710,7 +719,8 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": (measured_traffic() if args.workload == "chat" and args.layers == 32
-                        and args.block_size == 16 and not args.contiguous else None),
+                        and args.block_size == 16 and not args.contiguous
+                        and (args.q_heads, args.kv_heads) == (32, 32) else None),
             "kernel": "pa_decode call (partition + reduce kernels), average per layer",
             "avg_launch_us": round(decode_avg_ms * 1e3, 2),
             "median_launch_us": round(float(np.median(decode_ms)) * 1e3, 2),
@@ -752,14 +762,15 @@ def stream_ceiling(pa, steps_inputs):
     """Practical read ceiling on this GPU in this run: pa_stream_read over the
     workload's own pools, rotated so that no pass is served by the caches."""
     import torch
-    bufs = []
+    bufs, total = [], 0
     for ly in steps_inputs[0]:
         for t in (ly["kp"], ly["vp"]):
-            if t.numel() * t.element_size() >= (512 << 20):
+            if t.numel() * t.element_size() >= (256 << 20):
                 bufs.append(t)
-        if len(bufs) >= 4:
+                total += t.numel() * t.element_size()
+        if total >= (1536 << 20):
             break
-    if len(bufs) < 2:
+    if total < (1024 << 20):
         return None
     sink = torch.zeros(4, dtype=torch.int32, device="cuda")
     best = None
@@ -785,7 +796,10 @@ def stream_ceiling(pa, steps_inputs):
 
 def cpu_baseline(layers, n_sample, kv_bytes_step, n_layers):
     """Oracle decode (gather through the table, fp64 attention) on the host for
-    the first `n_sample` layers, on the same inputs the GPU saw."""
+    `n_sample` evenly spaced layers (every layer when n_sample >= the step's
+    layers), on the same inputs the GPU saw. The step's oracle time is the
+    mean layer time times the number of layers; its relative standard error
+    over the sampled layers is reported with it."""
     import torch
     import oracle
     try:
@@ -794,9 +808,11 @@ def cpu_baseline(layers, n_sample, kv_bytes_step, n_layers):
     except Exception:
         blas_threads = None
     n_sample = max(1, min(n_sample, len(layers)))
-    secs = 0.0
+    picks = sorted({int(round(x)) for x in np.linspace(0, len(layers) - 1, n_sample)})
+    per_layer = []
     tokens = 0
-    for ly in layers[:n_sample]:
+    for i in picks:
+        ly = layers[i]
         c = ly["case"]
         used = np.unique(c.block_tables[c.block_tables >= 0])
         idx = torch.from_numpy(used.astype(np.int64)).cuda()
@@ -807,22 +823,37 @@ def cpu_baseline(layers, n_sample, kv_bytes_step, n_layers):
         tables = np.where(c.block_tables >= 0, remap[np.maximum(c.block_tables, 0)], -1).astype(np.int32)
         t = time.perf_counter()
         oracle.decode(c.query, kb, vb, tables, c.context_lens, c.scale)
-        secs += time.perf_counter() - t
+        per_layer.append(time.perf_counter() - t)
         tokens += int(c.context_lens.sum())
         del kb, vb
-    per_layer = secs / n_sample
+        log(f"cpu baseline: layer {i} {per_layer[-1]:.2f} s")
+    secs = float(np.sum(per_layer))
+    mean = secs / len(per_layer)
+    if len(per_layer) == len(layers):
+        rel_err = 0.0
+    elif len(per_layer) > 1:
+        rel_err = float(np.std(per_layer, ddof=1) / np.sqrt(len(per_layer)) / mean)
+    else:
+        rel_err = None
+    step_s = mean * n_layers
     kv_layer = kv_bytes_step / n_layers
     S = layers[0]["case"].S
     return {
-        "value": round(kv_layer / per_layer / 1e9, 4),
+        "value": round(kv_layer / mean / 1e9, 4),
         "unit": "GB/s",
         "cores": len(os.sched_getaffinity(0)),
         "blas_threads": blas_threads,
         "kind": "oracle",
-        "decode_tokens_per_s": round(S / (per_layer * n_layers), 4),
-        "sample": f"oracle decode of {n_sample} of {n_layers} layer(s) (all {S} sequences, "
-                  f"{tokens} cached tokens x {layers[0]['case'].Hq} query heads), {secs:.1f} s; "
-                  f"tokens/s extrapolated to the {n_layers}-layer step",
+        "decode_tokens_per_s": round(S / step_s, 4),
+        "step_s": round(step_s, 2),
+        "step_s_rel_std_err": None if rel_err is None else round(rel_err, 4),
+        "layers_timed": picks,
+        "per_layer_s": [round(x, 3) for x in per_layer],
+        "sample": f"oracle decode of {len(picks)} of {n_layers} layer(s), evenly spaced (all {S} "
+                  f"sequences, {tokens} cached tokens x {layers[0]['case'].Hq} query heads), "
+                  f"{secs:.1f} s; the {n_layers}-layer step time is the mean layer time x "
+                  f"{n_layers}" + ("" if len(picks) == n_layers else
+                                   f", relative standard error {rel_err}"),
     }
 
 

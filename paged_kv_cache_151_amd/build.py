@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import glob
 import os
+import shlex
 import shutil
 import subprocess
 import sys
@@ -43,8 +44,12 @@ def sources():
 
 
 def build(verbose: bool = False) -> str:
+    """Compiles every source into libpa.so. PA_HIPCC_EXTRA (environment) adds
+    hipcc arguments, e.g. "-DPA_MFMA_WAVES=2" to build a variant of the
+    kernels' compile-time tuning parameters."""
     tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [hipcc(), *HIP_FLAGS, "-I", os.path.join(ROOT, "include"),
+    extra = shlex.split(os.environ.get("PA_HIPCC_EXTRA", ""))
+    cmd = [hipcc(), *HIP_FLAGS, *extra, "-I", os.path.join(ROOT, "include"),
            "-I", os.path.join(PKG, "csrc"), *sources(), "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)

@@ -64,6 +64,15 @@ struct Stage {
   static constexpr int value = S;
 };
 
+// Waves per workgroup and units fetched ahead of the one being computed
+// (compile-time tuning parameters).
+#ifndef PA_MFMA_WAVES
+#define PA_MFMA_WAVES 4
+#endif
+#ifndef PA_MFMA_DEPTH
+#define PA_MFMA_DEPTH 1
+#endif
+
 // 16-byte buffer loads of each lane into LDS (lane i's bytes at dst + 16 i;
 // lanes past the resource's range write zeros), plain and non-temporal.
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, lds_u8* dst, unsigned voff) {
@@ -75,9 +84,10 @@ __device__ __forceinline__ void dma16_nt(__amdgpu_buffer_rsrc_t r, lds_u8* dst, 
                                            0, 0, 2);
 }
 
-template <int BT, int G, int NW, bool NT>
+template <int BT, int G, int NW, int DEPTH, bool NT>
 __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeArgs a) {
   static_assert(G == 4 || G == 8, "groups of 4 or 8 query heads");
+  static_assert(DEPTH == 1 || DEPTH == 2, "prefetch depth 1 or 2");
   constexpr int D = kHeadDim;
   constexpr int U = kDecodeUnit;
   static_assert(BT == 0 || BT == 8 || BT % U == 0, "block size 8 or a multiple of 16");
@@ -85,10 +95,13 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeArgs a
   const int B = BT > 0 ? BT : a.B;
   const int UPB = kSplit ? 1 : B / U;   // units per block (B >= 16)
   // per-wave V tile buffers, one array per stage (the compiler tracks loads
-  // into LDS per array and waits only where a read meets its stage)
+  // into LDS per array and waits only where a read meets its stage); after
+  // the walk each wave's tile of stage 0 holds its G x D accumulators for the
+  // cross-wave merge (G * D * 4 bytes fit one 4 KiB tile)
+  static_assert(G * D * 4 <= kTileBytesG, "accumulators fit a wave's tile");
   __shared__ __attribute__((aligned(16))) unsigned char s_v0[NW * kTileBytesG];
   __shared__ __attribute__((aligned(16))) unsigned char s_v1[NW * kTileBytesG];
-  __shared__ float s_acc[NW][G][D];
+  __shared__ __attribute__((aligned(16))) unsigned char s_v2[DEPTH == 2 ? NW * kTileBytesG : 16];
   __shared__ float s_ml[NW][G][2];
 
   const int lane = threadIdx.x & 63;
@@ -236,7 +249,8 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeArgs a
       // returned before the buffer is refilled
       __builtin_amdgcn_sched_barrier(0);
       PA_G_WAIT_LDS();
-      lds_u8* vb = (decltype(stage)::value == 0 ? (lds_u8*)s_v0 : (lds_u8*)s_v1) + wbase;
+      constexpr int st = decltype(stage)::value;
+      lds_u8* vb = (st == 0 ? (lds_u8*)s_v0 : st == 1 ? (lds_u8*)s_v1 : (lds_u8*)s_v2) + wbase;
       // row groups 0-1 hold rows 0-7, groups 2-3 rows 8-15 (the second block at B = 8)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -248,7 +262,8 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeArgs a
       }
     };
     auto step = [&](const h8 (&ka)[4], int u, auto stage) {
-      const lds_u8* vb = (decltype(stage)::value == 0 ? (lds_u8*)s_v0 : (lds_u8*)s_v1) + wbase;
+      constexpr int st = decltype(stage)::value;
+      const lds_u8* vb = (st == 0 ? (lds_u8*)s_v0 : st == 1 ? (lds_u8*)s_v1 : (lds_u8*)s_v2) + wbase;
       f4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < 4; ++c) sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[c], qf[c], sc, 0, 0, 0);
@@ -288,19 +303,40 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeArgs a
     };
     int u = ub + wave;
     if (u >= ue) continue;
-    h8 k0[4], k1[4];
-    fetch(k0, u, Stage<0>{});
-    while (true) {
-      int un = u + NW;
-      fetch(k1, un, Stage<1>{});
-      step(k0, u, Stage<0>{});
-      if (un >= ue) break;
-      u = un;
-      un = u + NW;
-      fetch(k0, un, Stage<0>{});
-      step(k1, u, Stage<1>{});
-      if (un >= ue) break;
-      u = un;
+    if constexpr (DEPTH == 1) {
+      h8 k0[4], k1[4];
+      fetch(k0, u, Stage<0>{});
+      while (true) {
+        int un = u + NW;
+        fetch(k1, un, Stage<1>{});
+        step(k0, u, Stage<0>{});
+        if (un >= ue) break;
+        u = un;
+        un = u + NW;
+        fetch(k0, un, Stage<0>{});
+        step(k1, u, Stage<1>{});
+        if (un >= ue) break;
+        u = un;
+      }
+    } else {
+      // unit j of the wave uses register set and stage j % 3
+      h8 k0[4], k1[4], k2[4];
+      fetch(k0, u, Stage<0>{});
+      fetch(k1, u + NW, Stage<1>{});
+      while (true) {
+        fetch(k2, u + 2 * NW, Stage<2>{});
+        step(k0, u, Stage<0>{});
+        u += NW;
+        if (u >= ue) break;
+        fetch(k0, u + 2 * NW, Stage<0>{});
+        step(k1, u, Stage<1>{});
+        u += NW;
+        if (u >= ue) break;
+        fetch(k1, u + 2 * NW, Stage<1>{});
+        step(k2, u, Stage<2>{});
+        u += NW;
+        if (u >= ue) break;
+      }
     }
     // the last fetch was a no-op into a stage: let it land before the next
     // chunk's first load writes that stage
@@ -308,9 +344,13 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeArgs a
   }
   PA_G_WAIT_VM0();   // no load into LDS outlives the wave
 
-  // the four lanes of a head hold its sum in parts and the same maximum
+  // the four lanes of a head hold its sum in parts and the same maximum; the
+  // wave's accumulators go to its own tile of stage 0, which no other wave
+  // touches (its loads into LDS have landed, its reads have returned)
   float lt = lsum + __shfl_xor(lsum, 16);
   lt += __shfl_xor(lt, 32);
+  PA_G_WAIT_LDS();
+  float* acc_w = reinterpret_cast<float*>(s_v0 + wbase);
   if (m < G) {
     if (kq == 0) {
       s_ml[wave][m][0] = mrow;
@@ -319,7 +359,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeArgs a
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) s_acc[wave][m][16 * n + 4 * kq + r] = o[n][r];
+      for (int r = 0; r < 4; ++r) acc_w[m * D + 16 * n + 4 * kq + r] = o[n][r];
     }
   }
   __syncthreads();
@@ -336,7 +376,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeArgs a
     for (int w = 0; w < NW; ++w) {
       const float f = __builtin_amdgcn_exp2f(s_ml[w][h][0] - mx);
       den += f * s_ml[w][h][1];
-      num += f * s_acc[w][h][d];
+      num += f * reinterpret_cast<const float*>(s_v0 + w * kTileBytesG)[h * D + d];
     }
     const int hq = hq0 + h;
     if (nparts == 1) {
@@ -355,9 +395,10 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeArgs a
 
 template <int BT, int G>
 hipError_t launch_bt(const DecodeArgs& a, hipStream_t stream) {
-  constexpr int NW = 4;
+  constexpr int NW = PA_MFMA_WAVES;
   const int64_t grid = (int64_t)a.Pmax * a.S * a.Hkv;
-  decode_mfma_kernel<BT, G, NW, kDecodeNontemporal><<<(unsigned)grid, NW * 64, 0, stream>>>(a);
+  decode_mfma_kernel<BT, G, NW, PA_MFMA_DEPTH, kDecodeNontemporal>
+      <<<(unsigned)grid, NW * 64, 0, stream>>>(a);
   return hipGetLastError();
 }
 

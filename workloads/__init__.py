@@ -192,13 +192,15 @@ def chat_lengths(seed: int = CHAT_SEED, S: int = 128) -> np.ndarray:
 
 def chat_layer(layer: int, seed: int = CHAT_SEED, S: int = 128, with_pools: bool = False,
                lengths: Optional[np.ndarray] = None, B: int = 16,
-               contiguous: bool = False) -> DecodeCase:
+               contiguous: bool = False, Hq: int = 32, Hkv: int = 32) -> DecodeCase:
     """One layer of the batch-128 chat workload (32 heads, B = 16, 1.25x pool).
 
     All layers share the lengths; each layer has its own shuffle, query and new
     K/V (rng seeded with seed * 1000 + layer). `B` changes the block size;
     `contiguous=True` gives every sequence one block as long as the longest
-    sequence (the pre-paging layout), in a pool of exactly S blocks. Pools are large (about 1.7 GB
+    sequence (the pre-paging layout), in a pool of exactly S blocks. `Hq` / `Hkv` change the
+    head counts (grouped-query variants: 32 query heads over 8 KV heads, or 64 over 8). Pools are
+    large (about 1.7 GB
     each), so by default they are not drawn here: `device_pools` draws them on
     the GPU. `with_pools=True` draws them on the host (slow; small S only).
     """
@@ -212,8 +214,9 @@ def chat_layer(layer: int, seed: int = CHAT_SEED, S: int = 128, with_pools: bool
         # longest sequence of the batch (a multiple of 16 tokens)
         B = -(-int(lengths.max()) // 16) * 16
         NB = len(lengths)
-    case = _finish_case(f"chat_b{S}_layer{layer}", seed, rng, lengths,
-                        32, 32, B, HEAD_DIM, NB, (5, 4), None, with_pools)
+    name = f"chat_b{S}_layer{layer}" + ("" if (Hq, Hkv) == (32, 32) else f"_h{Hq}x{Hkv}")
+    case = _finish_case(name, seed, rng, lengths, Hq, Hkv, B, HEAD_DIM, NB, (5, 4), None,
+                        with_pools)
     case.extra["layer"] = layer
     return case
 

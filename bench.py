@@ -96,28 +96,27 @@ def parse():
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pa_decode_chat_b128_traffic.json")
-DECODE_SOURCES = [os.path.join(ROOT, "paged_kv_cache_151_amd", "csrc", f)
-                  for f in ("decode.hip", "decode_mfma.hip", "pa_internal.h")]
 
 
-def decode_source_hash() -> str:
+def _sources_hash(rel_paths) -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in DECODE_SOURCES:
-        with open(f, "rb") as fh:
+    for rel in rel_paths:
+        with open(os.path.join(ROOT, rel), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
 def measured_traffic():
     """HBM bytes per decode launch from the committed counter summary, or None
-    when the decode kernel's source changed after the counters were taken."""
+    when a source it lists (the decode kernels, their header, the build
+    flags) changed after the counters were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
-    except (OSError, ValueError):
-        return None
-    if t.get("decode_source_sha256") != decode_source_hash():
+        if t.get("decode_source_sha256") != _sources_hash(t["sources"]):
+            return None
+    except (OSError, ValueError, KeyError):
         return None
     return t.get("traffic_bytes_per_launch")
 
@@ -128,17 +127,12 @@ PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pa_prefill_chat_s16_traff
 def prefill_measured_traffic():
     """HBM bytes per prefill launch from the committed counter summary, or None
     when the prefill kernel or its build flags changed after the counters were taken."""
-    import hashlib
     try:
         with open(PREFILL_TRAFFIC_FILE) as f:
             t = json.load(f)
-        h = hashlib.sha256()
-        for rel in t["sources"]:
-            with open(os.path.join(ROOT, rel), "rb") as fh:
-                h.update(fh.read())
+        if t.get("prefill_source_sha256") != _sources_hash(t["sources"]):
+            return None
     except (OSError, ValueError, KeyError):
-        return None
-    if t.get("prefill_source_sha256") != h.hexdigest():
         return None
     return t.get("traffic_bytes_per_launch")
 

@@ -19,8 +19,9 @@
 // workgroup loads each chunk once, two chunks ahead of the one being computed,
 // with buffer loads that write straight into LDS (no staging registers, no
 // separate store step), into one of three LDS stages; the waves read their
-// matrix operands from there. Defaults (QT = 1, NW = 4, KC = 32) are set in
-// prefill_internal.h.
+// matrix operands from there. Defaults (QT = 1 for groups of one or two
+// query heads and 2 for four or eight, NW = 4, KC = 32, three LDS stages) are
+// set in prefill_internal.h.
 //
 // Instruction budget. A wave issues at most one instruction per turn on its
 // SIMD, so every scalar or vector instruction around the 16 matrix products of
@@ -95,6 +96,11 @@ struct Flag {
   static constexpr bool value = V;
 };
 
+template <int S>
+struct Stage {
+  static constexpr int value = S;
+};
+
 // 16-byte buffer load of each lane into LDS: lane i's bytes land at dst + 16 i
 // (lanes past the resource's range write zeros). Plain cache policy: the row
 // blocks of one sequence and KV head read the same chunks side by side on one
@@ -113,9 +119,10 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, lds_u8* dst
 // expcnt left at their maximum).
 #define PA_WAIT_LDS() __builtin_amdgcn_s_waitcnt(0xC07F)
 
-// Three waves per SIMD (at most 168 VGPRs; one row tile fits in about 150).
-template <int BT, int G, int QT, int NW, int KC>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(QT == 1 ? 3 : 1)))
+// Three waves per SIMD with one row tile (at most 168 VGPRs; it fits in about
+// 150); two row tiles fit in about 235 VGPRs, two waves per SIMD.
+template <int BT, int G, int QT, int NW, int KC, int NST>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(QT == 1 ? 3 : 2)))
 void prefill_kernel(const PrefillArgs a) {
   constexpr int D = kHeadDim;
   constexpr int HW = G < NW ? G : NW;      // query heads in a workgroup
@@ -133,6 +140,7 @@ void prefill_kernel(const PrefillArgs a) {
   static_assert(NW == 4, "the load layout assumes four waves");
   static_assert(KC == 32 || KC == 64, "keys per step");
   static_assert(NP * NTH == NPC, "whole load instructions per chunk");
+  static_assert(NST == 3 || NST == 4, "three or four LDS stages");
   // One array per stage, always indexed at compile time: the compiler tracks
   // loads into LDS per array and waits only where a read meets its stage.
   __shared__ __attribute__((aligned(16))) unsigned char s_k0[kStageBytes];
@@ -141,11 +149,13 @@ void prefill_kernel(const PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char s_v1[kStageBytes];
   __shared__ __attribute__((aligned(16))) unsigned char s_k2[kStageBytes];
   __shared__ __attribute__((aligned(16))) unsigned char s_v2[kStageBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char s_k3[NST == 4 ? kStageBytes : 16];
+  __shared__ __attribute__((aligned(16))) unsigned char s_v3[NST == 4 ? kStageBytes : 16];
   auto kst = [&](int st) -> lds_u8* {
-    return st == 0 ? (lds_u8*)s_k0 : st == 1 ? (lds_u8*)s_k1 : (lds_u8*)s_k2;
+    return st == 0 ? (lds_u8*)s_k0 : st == 1 ? (lds_u8*)s_k1 : st == 2 ? (lds_u8*)s_k2 : (lds_u8*)s_k3;
   };
   auto vst = [&](int st) -> lds_u8* {
-    return st == 0 ? (lds_u8*)s_v0 : st == 1 ? (lds_u8*)s_v1 : (lds_u8*)s_v2;
+    return st == 0 ? (lds_u8*)s_v0 : st == 1 ? (lds_u8*)s_v1 : st == 2 ? (lds_u8*)s_v2 : (lds_u8*)s_v3;
   };
   const int B = BT > 0 ? BT : a.B;
   // B = 8: a 16-token unit spans two blocks (two half tiles of 2 KiB), so it
@@ -197,11 +207,11 @@ void prefill_kernel(const PrefillArgs a) {
   const int nchunk_wg = (kend_wg + KC - 1) / KC;
   const int nblk = (kend_wg + B - 1) / B;
   // Chunks that every row of the workgroup sees in full (keys before the
-  // position of its first row), rounded down to whole turns of the three
-  // stages: these run through a loop with a single code path.
+  // position of its first row), rounded down to whole turns of the stages:
+  // these run through a loop with a single code path.
   int nall = base_pos + qb * QB + 1 > 0 ? (base_pos + qb * QB + 1) / KC : 0;
   nall = nall > nchunk_wg ? nchunk_wg : nall;
-  const int nfast = nall - nall % 3;
+  const int nfast = nall - nall % NST;
 
   // this wave's rows and the chunks it computes
   const int hq = g * G + hg * HW + wave % HW;
@@ -248,11 +258,12 @@ void prefill_kernel(const PrefillArgs a) {
   }
 
   // Physical blocks come from the table by a vector load per chunk (lane u
-  // reads unit u's entry, range-checked to the workgroup's nblk entries),
-  // issued just before the chunk loads of the same iteration: the wait at the
-  // top of the next iteration that lets those loads stay in flight also
-  // covers it, and no LDS wait ever waits for a table read (scalar loads share
-  // the LDS counter). Entries outside the pool are clamped to block 0.
+  // reads unit u's entry, range-checked to the workgroup's nblk entries; no
+  // LDS wait ever waits for a table read, as it would for scalar loads, which
+  // share the LDS counter). Each chunk's entries are loaded a whole turn of
+  // the pipeline before its chunk loads, into one of NST registers, so that
+  // the wait for a chunk's data always covers them. Entries outside the pool
+  // are clamped to block 0.
   const __amdgpu_buffer_rsrc_t trs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int32_t*>(a.tables + (int64_t)s * a.MB), 0, nblk * 4, kRsrcWord3);
   auto table_load = [&](int chunk) -> int {
@@ -433,19 +444,19 @@ void prefill_kernel(const PrefillArgs a) {
     }
   };
 
-  // Pipeline over three LDS stages: chunk k goes to stage k % 3. Iteration
+  // Pipeline over NST LDS stages: chunk k goes to stage k % NST. Iteration
   // c: wait until this wave's LDS reads have returned their data and its
-  // loads of chunk c and table read for chunk c + 2 are done (the loads of
-  // chunk c + 1 may still be in flight), barrier (every wave's part of chunk
-  // c is in LDS, and no wave still reads the stage of chunk c - 1), read chunk
-  // c + 2's entries, start the table read for chunk c + 3 and the loads of
-  // chunk c + 2 into the stage chunk c - 1 used, compute chunk c.
+  // loads of chunk c are done (the loads of chunks c + 1 .. c + NST - 2 may
+  // still be in flight), barrier (every wave's part of chunk c is in LDS, and
+  // no wave still reads the stage of chunk c - 1), read chunk c + NST - 1's
+  // entries, start the table read for chunk c + 2 NST - 1 and the loads of
+  // chunk c + NST - 1 into the stage chunk c - 1 used, compute chunk c.
   // The LDS wait is explicit: the barrier instruction does not wait for
   // outstanding reads, and the compiler is free to schedule the value products
   // of chunk c - 1, with the waits for their operand reads, below the barrier;
   // the scheduling fence keeps those reads above the wait. Without it a wave
   // could still be reading a stage when another wave's loads refill it.
-  // Both loops are unrolled three times so that every stage index is a
+  // Both loops are unrolled NST times so that every stage index is a
   // compile-time constant. The first runs the chunks every row sees in full
   // (all waves, no mask); the second the rest, where a wave masks the keys
   // beyond its rows (one masked code path: a second, unmasked copy there
@@ -455,55 +466,65 @@ void prefill_kernel(const PrefillArgs a) {
   // zeros.
   if (nchunk_wg > 0) {
     int ph[NE * NU];
-    int tv = table_load(0);
-    auto entries = [&]() {
+    int tvr[NST];   // table entries of chunk x live in tvr[x % NST]
+    auto entries = [&](int tv) {
 #pragma unroll
       for (int u = 0; u < NE * NU; ++u) ph[u] = __builtin_amdgcn_readlane(tv, u);
     };
-    entries();
-    load_chunk(0, 0, ph);
-    tv = table_load(1);
-    entries();
-    load_chunk(1, 1, ph);
-    tv = table_load(2);
-    // every row sees chunk c in full, every wave computes it
-    auto fast = [&](int c, int st) {
+    // The explicit wait at the top of each iteration counts loads in issue
+    // order, so the scheduling fences keep that order: table reads of chunks
+    // 0 .. NST - 1, then per chunk x < NST - 1 the table read of chunk
+    // x + NST and the loads of chunk x.
+#pragma unroll
+    for (int x = 0; x < NST; ++x) tvr[x] = table_load(x);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int x = 0; x + 1 < NST; ++x) {
+      entries(tvr[x]);
+      tvr[x] = table_load(x + NST);
+      __builtin_amdgcn_sched_barrier(0);
+      load_chunk(x, x, ph);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Iteration c (stage st = c % NST). Issue order per iteration: the table
+    // read of chunk c + 2 NST - 1, then the loads of chunk c + NST - 1. At the
+    // top, the loads issued after chunk c's are NST - 2 such pairs.
+    auto turn = [&](int c, auto st_flag, auto masked_flag) {
+      constexpr int st = decltype(st_flag)::value;
+      constexpr int nx = (st + NST - 1) % NST;
       __builtin_amdgcn_sched_barrier(0);
       PA_WAIT_LDS();
-      PA_WAIT_VM(NP);
+      PA_WAIT_VM((NST - 2) * (NP + 1));
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      entries();
-      tv = table_load(c + 3);
+      entries(tvr[nx]);
+      tvr[nx] = table_load(c + 2 * NST - 1);
       __builtin_amdgcn_sched_barrier(0);
-      load_chunk(c + 2, (st + 2) % 3, ph);
-      compute(st, c, Flag<false>{});
-    };
-    auto step = [&](int c, int st) {
-      __builtin_amdgcn_sched_barrier(0);
-      PA_WAIT_LDS();
-      PA_WAIT_VM(NP);
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      entries();
-      tv = table_load(c + 3);
-      __builtin_amdgcn_sched_barrier(0);
-      load_chunk(c + 2, (st + 2) % 3, ph);
-      if (c < nchunk) compute(st, c, Flag<true>{});
+      load_chunk(c + NST - 1, nx, ph);
+      if constexpr (decltype(masked_flag)::value) {
+        if (c < nchunk) compute(st, c, Flag<true>{});
+      } else {
+        compute(st, c, Flag<false>{});   // every row sees chunk c in full
+      }
     };
     int c = 0;
-    for (; c < nfast; c += 3) {
-      fast(c, 0);
-      fast(c + 1, 1);
-      fast(c + 2, 2);
+    for (; c < nfast; c += NST) {
+      turn(c, Stage<0>{}, Flag<false>{});
+      turn(c + 1, Stage<1>{}, Flag<false>{});
+      turn(c + 2, Stage<2>{}, Flag<false>{});
+      if constexpr (NST == 4) turn(c + 3, Stage<3>{}, Flag<false>{});
     }
     while (c < nchunk_wg) {
-      step(c, 0);
+      turn(c, Stage<0>{}, Flag<true>{});
       if (++c >= nchunk_wg) break;
-      step(c, 1);
+      turn(c, Stage<1>{}, Flag<true>{});
       if (++c >= nchunk_wg) break;
-      step(c, 2);
+      turn(c, Stage<2>{}, Flag<true>{});
       if (++c >= nchunk_wg) break;
+      if constexpr (NST == 4) {
+        turn(c, Stage<3>{}, Flag<true>{});
+        if (++c >= nchunk_wg) break;
+      }
     }
     PA_WAIT_VM(0);   // no load into LDS outlives the workgroup
   }
@@ -531,7 +552,7 @@ void prefill_kernel(const PrefillArgs a) {
 
 template <int BT, int G>
 hipError_t launch_g(const PrefillArgs& a, int64_t grid, hipStream_t stream) {
-  prefill_kernel<BT, G, kPrefillRowTiles, kPrefillWaves, kPrefillChunk>
+  prefill_kernel<BT, G, prefill_row_tiles(G), kPrefillWaves, kPrefillChunk, kPrefillStages>
       <<<(unsigned)grid, kPrefillWaves * 64, 0, stream>>>(a);
   return hipGetLastError();
 }
@@ -551,7 +572,7 @@ hipError_t launch_bt(const PrefillArgs& a, int G, int64_t grid, hipStream_t stre
 
 int prefill_rows_per_workgroup(int G) {
   const int hw = G < kPrefillWaves ? G : kPrefillWaves;
-  return (kPrefillWaves / hw) * 16 * kPrefillRowTiles;
+  return (kPrefillWaves / hw) * 16 * prefill_row_tiles(G);
 }
 
 int64_t prefill_work_items(int G, int S, int Hkv, int max_query_len) {

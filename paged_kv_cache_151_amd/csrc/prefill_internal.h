@@ -7,12 +7,21 @@ namespace pa {
 
 // Query row tiles of 16 per prefill wave. More rows per wave read each
 // staged key/value chunk from LDS for more rows, but hold more registers: one
-// tile fits in about 150 VGPRs (three waves per SIMD); two tiles need about
-// 300 (one wave per SIMD), and held to 256 they spill and measured 30 % slower.
+// tile fits in about 150 VGPRs (three waves per SIMD), two in about 235 (two
+// waves per SIMD). Measured on MI355X: for groups of 4 query heads (the
+// shared-prefix suffixes) two tiles are 5 % faster (289 against 304 us); for
+// one head per group (the 16-prompt chat batch) they tie (292 against 293).
 #ifndef PA_PREFILL_ROW_TILES
 #define PA_PREFILL_ROW_TILES 1
 #endif
+#ifndef PA_PREFILL_ROW_TILES_GROUPED
+#define PA_PREFILL_ROW_TILES_GROUPED 2
+#endif
 constexpr int kPrefillRowTiles = PA_PREFILL_ROW_TILES;
+// Row tiles per wave for a group of G query heads (4 and 8 take the grouped value).
+constexpr int prefill_row_tiles(int G) {
+  return G >= 4 ? PA_PREFILL_ROW_TILES_GROUPED : kPrefillRowTiles;
+}
 // Waves per prefill workgroup: they share each staged key/value chunk. The
 // load layout (each wave loads one pool, K or V, of half the units of every
 // chunk) is built for four. Eight (one workgroup per CU at two waves per
@@ -23,6 +32,12 @@ constexpr int kPrefillWaves = 4;
 #define PA_PREFILL_CHUNK 32
 #endif
 constexpr int kPrefillChunk = PA_PREFILL_CHUNK;
+// LDS stages of the key/value pipeline (3 or 4): chunks are loaded
+// kPrefillStages - 1 ahead of the one being computed.
+#ifndef PA_PREFILL_STAGES
+#define PA_PREFILL_STAGES 3
+#endif
+constexpr int kPrefillStages = PA_PREFILL_STAGES;
 
 // Arguments of the prefill kernel.
 struct PrefillArgs {

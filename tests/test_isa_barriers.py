@@ -12,6 +12,7 @@ from __future__ import annotations
 
 import importlib.util
 import os
+import shlex
 import subprocess
 
 import pytest
@@ -37,7 +38,9 @@ def _assembly(src: str, out_dir) -> str:
         hipcc = b.hipcc()
     except RuntimeError:
         pytest.skip("hipcc not found")
+    # the library's flags, plus any variant definitions the build also takes
     flags = [f for f in b.HIP_FLAGS if f not in ("-fPIC", "-shared")]
+    flags += shlex.split(os.environ.get("PA_HIPCC_EXTRA", ""))
     out = os.path.join(str(out_dir), src + ".s")
     cmd = [hipcc, *flags, "--cuda-device-only", "-S", "-I", os.path.join(ROOT, "include"),
            "-I", CSRC, os.path.join(CSRC, src), "-o", out]

@@ -155,3 +155,73 @@ def test_prefill_peaked_scores(pa, family, G):
         ref = oracle.prefill(c.query, c.k_pool, c.v_pool, c.block_tables, c.context_lens,
                              c.query_start, c.scale)
         assert_attention_close(got, ref, c.name)
+
+
+# ---------------------------------------------------------------------------
+# The remaining closed forms of decode, on the GPU for every group size (both
+# kernels): the pages fix the result as attention over the contiguous tokens
+# ([L] "How PagedAttention works", step 4; "Key takeaways": paging is exact),
+# and for these inputs that attention has a value that needs no oracle.
+# ---------------------------------------------------------------------------
+
+def _closed_form_case(name, seed, G, lens, B=16):
+    return W.make_case(name, seed, lens, Hq=2 * G, Hkv=2, B=B)
+
+
+def _values_in_order(c, s):
+    """Value rows of sequence s in logical order, the new token included: [Hkv, L, D]."""
+    L = int(c.context_lens[s])
+    V = oracle.gather(c.v_pool, c.block_tables[s], L, c.B).astype(np.float64)
+    V[:, L - 1] = c.value_new[s]
+    return V
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_decode_single_token_gives_its_value_row_bit_exact(pa, G):
+    """L = 1: the one weight is 1, so the output is V_0 exactly (fp16 in, fp16 out)."""
+    c = _closed_form_case(f"one_token_G{G}", 9800 + G, G, [1, 1, 1, 1])
+    say(c.name)
+    for P in (0, 16):
+        got = decode_gpu(pa, c, P)
+        want = np.repeat(c.value_new, G, axis=1)          # query head h reads KV head h // G
+        assert np.array_equal(got.view(np.uint16), want.view(np.uint16)), f"{c.name} P={P}"
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_decode_zero_query_or_equal_keys_give_the_mean_of_values(pa, G):
+    """Every score equal (a zero query; or one key repeated at every position):
+    the weights are uniform and the output is the mean of the value rows."""
+    lens = [3, 17, 100, 1030, 2049]
+    for how in ("zero query", "equal keys"):
+        c = _closed_form_case(f"uniform_{how.replace(' ', '_')}_G{G}", 9810 + G, G, lens)
+        if how == "zero query":
+            c.query[:] = 0
+        else:
+            rng = np.random.default_rng(9820 + G)
+            for s in range(c.S):
+                L = int(c.context_lens[s])
+                key = W.f16_normal(rng, (c.Hkv, c.D))
+                c.key_new[s] = key
+                for t in range(L - 1):
+                    for g in range(c.Hkv):
+                        PK._set_key(c.k_pool, c.block_tables[s], t, c.B, g, key[g])
+        want = np.stack([np.repeat(_values_in_order(c, s).mean(axis=1), G, axis=0)
+                         for s in range(c.S)])
+        say(c.name, how)
+        for P in (0, 64, 1024):
+            assert_attention_close(decode_gpu(pa, c, P), want, f"{c.name} P={P}")
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_decode_constant_values_give_that_constant(pa, G):
+    """Every value row equal to one vector: whatever the weights, the output is
+    that vector (to the fp16 rounding of the weights on the matrix cores)."""
+    c = _closed_form_case(f"constant_values_G{G}", 9830 + G, G, [2, 40, 513, 1500])
+    PK.decode_dominant_keys(c, np.random.default_rng(9840 + G))    # peaked weights too
+    const = W.f16_normal(np.random.default_rng(9850 + G), (c.Hkv, c.D))
+    c.v_pool[:] = const[None, :, None, :]
+    c.value_new[:] = const[None]
+    want = np.broadcast_to(np.repeat(const, G, axis=0)[None].astype(np.float64), (c.S, c.Hq, c.D))
+    say(c.name)
+    for P in (0, 64, 1024):
+        assert_attention_close(decode_gpu(pa, c, P), want, f"{c.name} P={P}")

@@ -743,12 +743,26 @@ def other_bytes(c, P):
     blocks = -(-L // c.B)
     row = c.Hkv * c.D * 2 * 2                     # K and V bytes of one token, all KV heads
     nparts = -(-L // P)
-    multi = nparts > 1
+    G = c.Hq // c.Hkv
+    parts = int(-(-int(L.max()) // P))
+    if G in (4, 8) and parts > 1 and c.S <= 1024:
+        # even split: runs of q units over the (KV head, sequence, unit)
+        # order, one per resident workgroup (4 per compute unit here)
+        n = -(-L // 16)
+        N = int(n.sum())
+        grid = min(1024, -(-c.S * c.Hkv * parts // 8) * 8)
+        q = max(-(-N * c.Hkv // grid), P // 16)
+        first = (np.arange(c.Hkv)[:, None] * N + (np.cumsum(n) - n)[None, :])
+        pieces = (first + n[None, :] - 1) // q - first // q + 1
+        pieces = pieces[n[None, :].repeat(c.Hkv, 0) > 0]
+        partial_rows = int(pieces[pieces > 1].sum()) * G
+    else:
+        partial_rows = int(nparts[nparts > 1].sum()) * c.Hq
     return {
         "kv_unread_tail_of_last_blocks": int((blocks * c.B - L).sum() * row),
         "query_and_output": int(2 * c.S * c.Hq * c.D * 2),
         "tables_and_lengths": int(blocks.sum() * 4 + c.S * 4),
-        "workspace_partials_written_and_read": int(2 * (nparts[multi].sum()) * c.Hq * (c.D + 2) * 4),
+        "workspace_partials_written_and_read": int(2 * partial_rows * (c.D + 2) * 4),
     }
 
 

@@ -183,10 +183,14 @@ int pa_decode_partition_size(int S, int Hq, int Hkv, int B, int max_context_len,
 
 /*
  * pa_decode_workspace_bytes — device workspace pa_decode needs: partial
- * results of every context partition, S * Hq * ceil(max_context_len / P)
- * * (D + 2) * 4 bytes, or 0 when one partition covers every sequence.
- * Returns 0 for invalid arguments, and when the size does not fit in size_t,
- * as well; pa_decode then reports the error.
+ * results of every context partition, S * Hq * n * (D + 2) * 4 bytes with
+ * n = ceil(max_context_len / P) partitions, or 0 when one partition covers
+ * every sequence. When the call splits its work evenly (below: Hq / Hkv of 4
+ * or 8, n > 1, S <= 1024, and S * Hkv * n * (P / 16 + 1) + 8 + 9 * P / 16
+ * below 2^31) a sequence has up to n + 1 pieces and the workspace also holds
+ * a piece count per (sequence, KV head): S * Hq * (n + 1) * (D + 2) * 4
+ * + S * Hkv * 4 bytes. Returns 0 for invalid arguments, and when the size
+ * does not fit in size_t, as well; pa_decode then reports the error.
  */
 size_t pa_decode_workspace_bytes(int S, int Hq, int Hkv, int D, int B, int max_context_len,
                                  int partition_size);
@@ -208,9 +212,17 @@ size_t pa_decode_workspace_bytes(int S, int Hq, int Hkv, int D, int B, int max_c
  * of either sign, is supported.
  * Slots past L_s in the last block and blocks the table does not name are
  * never read into the result, whatever they hold (NaN and Inf included).
- * The summation order depends only on logical token positions, so relabelling
- * physical blocks or sharing them between sequences leaves every output bit
- * unchanged.
+ * The summation order depends only on the sequences' lengths and logical
+ * token positions, so relabelling physical blocks or sharing them between
+ * sequences leaves every output bit unchanged.
+ * Work split: with one or two query heads per KV head, and for groups of four
+ * and eight when every sequence fits one partition, each workgroup serves one
+ * partition of one (sequence, KV head). Groups of four and eight over several
+ * partitions (and at most 1024 sequences) instead cut the batch's 16-token
+ * units, taken in (KV head, sequence, position) order, into equal runs, one
+ * per workgroup the GPU holds at once, and merge each sequence's pieces in the
+ * reduce kernel: every workgroup then starts at the launch and none is left
+ * running alone at its end.
  *
  *   out               device fp16 [S][Hq][D], 16-byte aligned, written
  *   query             device fp16 [S][Hq][D], 16-byte aligned
@@ -221,7 +233,7 @@ size_t pa_decode_workspace_bytes(int S, int Hq, int Hkv, int D, int B, int max_c
  *   scale             softmax scale, finite (either sign), usually 1/sqrt(D)
  *   partition_size    tokens per context partition: 0 = library choice, else a
  *                     positive multiple of 16 (a partition may start inside a
- *                     block)
+ *                     block); under the even split, the shortest run in tokens
  *   workspace         device buffer of at least pa_decode_workspace_bytes(...)
  *                     bytes, 16-byte aligned; may be NULL when that is 0
  * Supported: D = 128; B = 8 or a multiple of 16 (one block per sequence of at

@@ -104,7 +104,9 @@ pa_status decode_prepare(const char* fn, void* out, const void* query, const voi
     return fail(PA_ERR_UNSUPPORTED, "%s: Hq/Hkv=%d (supported: 1, 2, 4, 8)", fn, G);
   if (!std::isfinite(scale)) return fail(PA_ERR_SHAPE, "%s: scale is not finite", fn);
   const int P = pa_decode_partition_size(S, Hq, Hkv, B, max_context_len, partition_size);
-  const int Pmax = max_context_len > 0 ? ceil_div(max_context_len, P) : 1;
+  const int parts = max_context_len > 0 ? ceil_div(max_context_len, P) : 1;
+  const bool even = decode_even_split(S, Hq, Hkv, P, parts);
+  const int Pmax = even ? parts + 1 : parts;   // an even split adds at most one piece
   if (Pmax > kMaxPartitions)
     return fail(PA_ERR_SHAPE, "%s: %d partitions exceed %d", fn, Pmax, kMaxPartitions);
   // partition kernel: one workgroup per (partition, sequence, KV head) of
@@ -112,7 +114,7 @@ pa_status decode_prepare(const char* fn, void* out, const void* query, const voi
   // kernel: one wave per (sequence, query head)
   const int hpw = G < kDecodeHeadsPerWave ? G : kDecodeHeadsPerWave;
   const int waves = decode_waves(G) > G / hpw ? decode_waves(G) : G / hpw;
-  const int64_t wgs = (int64_t)Pmax * S * Hkv;
+  const int64_t wgs = (int64_t)parts * S * Hkv;
   if (!dispatch_fits(wgs, waves * 64) || !dispatch_fits((int64_t)S * Hq, 64))
     return fail(PA_ERR_SHAPE, "%s: launch too large (S=%d Hq=%d, %lld workgroups)", fn, S, Hq,
                 (long long)wgs);
@@ -133,6 +135,7 @@ pa_status decode_prepare(const char* fn, void* out, const void* query, const voi
   a.lens = context_lens;
   a.part_acc = nullptr;
   a.part_ml = nullptr;
+  a.part_np = nullptr;
   a.S = S;
   a.Hq = Hq;
   a.Hkv = Hkv;
@@ -143,6 +146,7 @@ pa_status decode_prepare(const char* fn, void* out, const void* query, const voi
   a.Pmax = Pmax;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   call->G = G;
+  call->even = even;
   call->partials_bytes = pa_decode_workspace_bytes(S, Hq, Hkv, D, B, max_context_len, P);
   if (Pmax > 1 && call->partials_bytes == 0)
     return fail(PA_ERR_SHAPE, "%s: partials of %d partitions do not fit in size_t", fn, Pmax);
@@ -155,6 +159,7 @@ pa_status decode_enqueue(const char* fn, DecodeCall& call, void* partials, hipSt
     float* ws = static_cast<float*>(partials);
     a.part_acc = ws;
     a.part_ml = ws + (size_t)a.S * a.Hq * a.Pmax * kHeadDim;
+    if (call.even) a.part_np = reinterpret_cast<int32_t*>(a.part_ml + (size_t)a.S * a.Hq * a.Pmax * 2);
   }
   const hipError_t e = launch_decode(a, a.B, call.G, stream);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "%s launch: %s", fn, hipGetErrorString(e));
@@ -345,13 +350,18 @@ size_t pa_decode_workspace_bytes(int S, int Hq, int Hkv, int D, int B, int max_c
                                  int partition_size) {
   const int P = pa_decode_partition_size(S, Hq, Hkv, B, max_context_len, partition_size);
   if (P <= 0 || S <= 0 || Hq <= 0 || D <= 0 || max_context_len <= 0) return 0;
-  const int64_t Pmax = ceil_div(max_context_len, P);
-  if (Pmax <= 1) return 0;
-  size_t n = 0;   // S * Hq * Pmax * (D + 2) floats; 0 when that overflows
+  const int64_t parts = ceil_div(max_context_len, P);
+  if (parts <= 1) return 0;
+  // an even split (groups of 4 and 8 over several partitions) has one more
+  // piece per sequence and a piece count per (sequence, KV head)
+  const bool even = pa::decode_even_split(S, Hq, Hkv, P, parts);
+  const int64_t Pmax = even ? parts + 1 : parts;
+  size_t n = 0;   // S * Hq * Pmax * (D + 2) floats (+ S * Hkv int32); 0 when that overflows
   if (__builtin_mul_overflow((size_t)S, (size_t)Hq, &n) ||
       __builtin_mul_overflow(n, (size_t)Pmax, &n) ||
       __builtin_mul_overflow(n, ((size_t)D + 2) * sizeof(float), &n))
     return 0;
+  if (even && __builtin_add_overflow(n, (size_t)S * Hkv * sizeof(int32_t), &n)) return 0;
   return n;
 }
 

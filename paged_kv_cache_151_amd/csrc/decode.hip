@@ -454,8 +454,9 @@ void decode_partition_kernel(const DecodeArgs a) {
   }
 }
 
-// One wave per (s, hq): out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
-// Sequences that fit one partition were finished by the partition kernel.
+// One wave per (s, hq): out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p
+// over the sequence's pieces (its partitions, or the counts the even split
+// recorded). Sequences of one piece were finished by the partition kernel.
 __global__ __launch_bounds__(64) void decode_reduce_kernel(const DecodeArgs a, int B_MB) {
   constexpr int D = kHeadDim;
   const int hq = blockIdx.x % a.Hq;
@@ -463,7 +464,7 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(const DecodeArgs a, i
   int L = a.lens[s];
   L = L < 0 ? 0 : L;
   L = L > B_MB ? B_MB : L;
-  int np = (L + a.P - 1) / a.P;
+  int np = a.part_np ? a.part_np[s * a.Hkv + hq / (a.Hq / a.Hkv)] : (L + a.P - 1) / a.P;
   np = np > a.Pmax ? a.Pmax : np;
   if (np <= 1) return;
   const int64_t row0 = ((int64_t)s * a.Hq + hq) * a.Pmax;

@@ -10,6 +10,7 @@ namespace pa {
 struct DecodeCall {
   DecodeArgs a;           // kernel arguments, partials pointers unset
   int G;                  // query heads per KV head
+  bool even;              // the work is split evenly over the resident workgroups
   size_t partials_bytes;  // workspace the call needs (0: one partition covers every sequence)
 };
 

@@ -35,6 +35,8 @@
 // partials for the reduce kernel. V tiles go to a per-wave LDS double buffer
 // by buffer loads that write LDS directly; piece c of V row r sits at
 // c ^ 2 (r % 8), which keeps the transposing reads free of bank conflicts.
+#include <atomic>
+
 #include "pa_internal.h"
 
 namespace pa {
@@ -84,8 +86,21 @@ __device__ __forceinline__ void dma16_nt(__amdgpu_buffer_rsrc_t r, lds_u8* dst, 
                                            0, 0, 2);
 }
 
+// Tokens [tok0, tok0 + len) of sequence s and KV head g (len > 0): piece p of
+// the nparts pieces the sequence's walk is cut into. With one piece the
+// result is the output; otherwise the piece's (maximum, sum, accumulators)
+// go to partial row p for the reduce kernel.
 template <int BT, int G, int NW, int DEPTH, bool NT>
-__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeArgs a) {
+__device__ __forceinline__ void attend_piece(const DecodeArgs& a, int s, int g, int tok0, int len,
+                                             int nparts, int p) {
+  // the piece is the same for every lane: keep its description in scalar
+  // registers (integer division and loads after stores leave it in vector ones)
+  s = __builtin_amdgcn_readfirstlane(s);
+  g = __builtin_amdgcn_readfirstlane(g);
+  tok0 = __builtin_amdgcn_readfirstlane(tok0);
+  len = __builtin_amdgcn_readfirstlane(len);
+  nparts = __builtin_amdgcn_readfirstlane(nparts);
+  p = __builtin_amdgcn_readfirstlane(p);
   static_assert(G == 4 || G == 8, "groups of 4 or 8 query heads");
   static_assert(DEPTH == 1 || DEPTH == 2, "prefetch depth 1 or 2");
   constexpr int D = kHeadDim;
@@ -108,29 +123,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeArgs a
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m = lane & 15;
   const int kq = lane >> 4;
-
-  int id = blockIdx.x;
-  const int g = id % a.Hkv;
-  id /= a.Hkv;
-  const int s = id % a.S;
-  const int p = id / a.S;
-
-  int L = a.lens[s];
-  L = L < 0 ? 0 : L;
-  L = L > a.MB * B ? a.MB * B : L;
-  L = L > a.Pmax * a.P ? a.Pmax * a.P : L;
-  const int tok0 = p * a.P;
   const int hq0 = g * G;
-  if (tok0 >= L) {
-    if (p == 0) {  // empty sequence: zero output
-      for (int e = threadIdx.x; e < G * D; e += NW * 64) {
-        a.out[((int64_t)s * a.Hq + hq0 + e / D) * D + (e % D)] = (_Float16)0.f;
-      }
-    }
-    return;
-  }
-  const int nparts = (L + a.P - 1) / a.P;
-  const int len = (tok0 + a.P < L ? tok0 + a.P : L) - tok0;
   const int nunits = (len + U - 1) / U;
   const int U0 = tok0 / U;
   const int blk0 = kSplit ? 2 * U0 : U0 / UPB;
@@ -393,9 +386,179 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeArgs a
   }
 }
 
+// Clamped context length of sequence s: within the table and the launch.
+__device__ __forceinline__ int clamped_len(const DecodeArgs& a, int s, int B, int cap) {
+  int L = a.lens[s];
+  L = L < 0 ? 0 : L;
+  L = L > a.MB * B ? a.MB * B : L;
+  return L > cap ? cap : L;
+}
+
+// Zero output of every query head of KV head g of sequence s (empty sequence).
+template <int G, int NW>
+__device__ __forceinline__ void zero_heads(const DecodeArgs& a, int s, int g) {
+  for (int e = threadIdx.x; e < G * kHeadDim; e += NW * 64)
+    a.out[((int64_t)s * a.Hq + g * G + e / kHeadDim) * kHeadDim + (e % kHeadDim)] = (_Float16)0.f;
+}
+
+// One workgroup per (partition, sequence, KV head), partitions of a.P tokens.
+template <int BT, int G, int NW, int DEPTH, bool NT>
+__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeArgs a) {
+  const int B = BT > 0 ? BT : a.B;
+  int id = blockIdx.x;
+  const int g = id % a.Hkv;
+  id /= a.Hkv;
+  const int s = id % a.S;
+  const int p = id / a.S;
+  const int L = clamped_len(a, s, B, a.Pmax * a.P);
+  const int tok0 = p * a.P;
+  if (tok0 >= L) {
+    if (p == 0) zero_heads<G, NW>(a, s, g);
+    return;
+  }
+  const int nparts = (L + a.P - 1) / a.P;
+  const int len = (tok0 + a.P < L ? tok0 + a.P : L) - tok0;
+  attend_piece<BT, G, NW, DEPTH, NT>(a, s, g, tok0, len, nparts, p);
+}
+
+// Equal-work split of the whole batch. The 16-token units of every (KV head,
+// sequence) pair are taken in the order (KV head, sequence, position) and cut
+// into runs of q consecutive units, one run per workgroup; q is the total over
+// the grid, at least a.P / 16. A workgroup walks its run pair by pair, each
+// pair's part being one piece for the reduce kernel. The grid is the number of
+// workgroups the GPU holds at once, so every run starts at the launch and
+// they all end together: no workgroup starts late behind a long one, which
+// costs grouped heads about a tenth of a launch in the per-partition grid.
+// Workgroup b runs on XCD b % 8 and takes run (b % 8) * (grid / 8) + b / 8,
+// so each XCD walks one contiguous eighth of the order: one KV head per XCD
+// when there are 8, as in the per-partition grid's order.
+template <int BT, int G, int NW, int DEPTH, bool NT>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4))) void decode_mfma_even_kernel(const DecodeArgs a) {
+  constexpr int U = kDecodeUnit;
+  const int B = BT > 0 ? BT : a.B;
+  const int cap = (a.Pmax - 1) * a.P;   // the launch's bound on every length
+  const int lane = threadIdx.x & 63;
+  const int nwg = gridDim.x;            // a multiple of 8
+  const int w = (blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8;
+
+  // empty sequences (workgroup b serves sequences b, b + grid, ...): zero
+  // output and no pieces
+  for (int s = blockIdx.x; s < a.S; s += nwg) {
+    if (clamped_len(a, s, B, cap) == 0) {
+      for (int g = 0; g < a.Hkv; ++g) zero_heads<G, NW>(a, s, g);
+      for (int g = threadIdx.x; g < a.Hkv; g += NW * 64) a.part_np[s * a.Hkv + g] = 0;
+    }
+  }
+
+  // N = units of one KV head over the batch; the run length q
+  int acc = 0;
+  for (int c = lane; c < a.S; c += 64) acc += (clamped_len(a, c, B, cap) + U - 1) / U;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) acc += __shfl_xor(acc, d);
+  const int N = __builtin_amdgcn_readfirstlane(acc);
+  const int total = N * a.Hkv;
+  const int qmin = a.P / U;
+  const int qe = (total + nwg - 1) / nwg;
+  const int q = __builtin_amdgcn_readfirstlane(qe > qmin ? qe : qmin);
+  const int begin = w * q;
+  if (begin >= total) return;
+  const int end = begin + q < total ? begin + q : total;
+
+  // the pair of the run's first unit: KV head g, then the first sequence
+  // whose running unit count passes the offset r inside that head
+  int g = __builtin_amdgcn_readfirstlane(begin / N);
+  const int r = begin - g * N;
+  int s = 0, cs = 0, ns = 0, Ls = 0;
+  for (int c = 0, base = 0; c < a.S; c += 64) {
+    const int L = c + lane < a.S ? clamped_len(a, c + lane, B, cap) : 0;
+    const int n = (L + U - 1) / U;
+    int incl = n;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int t = __shfl_up(incl, d);
+      incl += lane >= d ? t : 0;
+    }
+    const unsigned long long hit = __builtin_amdgcn_ballot_w64(base + incl > r);
+    if (hit) {
+      const int f = __builtin_ctzll(hit);
+      s = c + f;
+      ns = __builtin_amdgcn_readlane(n, f);
+      Ls = __builtin_amdgcn_readlane(L, f);
+      cs = base + __builtin_amdgcn_readlane(incl, f) - ns;
+      break;
+    }
+    base += __builtin_amdgcn_readlane(incl, 63);
+  }
+  s = __builtin_amdgcn_readfirstlane(s);
+  ns = __builtin_amdgcn_readfirstlane(ns);
+  Ls = __builtin_amdgcn_readfirstlane(Ls);
+  cs = __builtin_amdgcn_readfirstlane(cs);
+  if (ns == 0) return;   // unreachable: r < N
+
+  int pos = begin;
+  for (bool first = true;; first = false) {
+    const int pair0 = g * N + cs;                  // order position of the pair's unit 0
+    const int j0 = pos - pair0;
+    const int j1 = end - pair0 < ns ? end - pair0 : ns;
+    const int piece = w - pair0 / q;               // runs are numbered by position / q
+    const int nparts = (pair0 + ns - 1) / q - pair0 / q + 1;
+    if (!first) __syncthreads();                   // the last piece's merge has read the tiles
+    const int tok0 = j0 * U;
+    const int tok1 = j1 * U < Ls ? j1 * U : Ls;
+    attend_piece<BT, G, NW, DEPTH, NT>(a, s, g, tok0, tok1 - tok0, nparts, piece);
+    if (j1 == ns && threadIdx.x == 0) a.part_np[s * a.Hkv + g] = nparts;
+    pos = pair0 + j1;
+    if (pos >= end) break;
+    // the next pair in the order with at least one unit
+    do {
+      cs += ns;
+      if (++s == a.S) {
+        s = 0;
+        cs = 0;
+        if (++g == a.Hkv) return;   // unreachable: pos < end <= total
+      }
+      // a load after the kernel's stores: the compiler cannot see it uniform
+      Ls = __builtin_amdgcn_readfirstlane(clamped_len(a, s, B, cap));
+      ns = (Ls + U - 1) / U;
+    } while (ns == 0);
+  }
+}
+
+// Workgroups of `kernel` (NW * 64 threads) the current device holds at once,
+// rounded down to a multiple of 8; measured once per device.
+template <class K>
+int resident_workgroups(K kernel, int threads) {
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = -1;
+  if (dev >= 0) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) !=
+          hipSuccess)
+    return 0;
+  int n = per_cu * cus / 8 * 8;
+  if (n < 8) n = 8;
+  if (dev >= 0) cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 template <int BT, int G>
 hipError_t launch_bt(const DecodeArgs& a, hipStream_t stream) {
   constexpr int NW = PA_MFMA_WAVES;
+  if (a.part_np) {
+    auto kernel = decode_mfma_even_kernel<BT, G, NW, PA_MFMA_DEPTH, kDecodeNontemporal>;
+    const int resident = resident_workgroups(kernel, NW * 64);
+    if (resident <= 0) return hipErrorInvalidValue;
+    // no more runs than the minimum run length leaves units for
+    const int64_t most = ((int64_t)a.S * a.Hkv * (a.Pmax - 1) + 7) / 8 * 8;
+    const int64_t grid = most < resident ? most : resident;
+    kernel<<<(unsigned)grid, NW * 64, 0, stream>>>(a);
+    return hipGetLastError();
+  }
   const int64_t grid = (int64_t)a.Pmax * a.S * a.Hkv;
   decode_mfma_kernel<BT, G, NW, PA_MFMA_DEPTH, kDecodeNontemporal>
       <<<(unsigned)grid, NW * 64, 0, stream>>>(a);

@@ -8,8 +8,8 @@
 // code its name is only a stand-in for the symbol, so the device address is
 // looked up once per device with hipGetSymbolAddress (with that device
 // current) and kept; kernels receive that address. Nothing in the array needs
-// to start at zero: the partition kernel writes every partial that the reduce
-// kernel reads in the same call.
+// to start at zero: the partition kernel writes every partial and piece count
+// that the reduce kernel reads in the same call.
 #include <mutex>
 
 #include "decode_call.h"

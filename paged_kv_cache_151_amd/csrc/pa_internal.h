@@ -54,6 +54,24 @@ constexpr int64_t kComputeUnits = 256;
 // batch-8 decode: 3-9 % faster, one shape 3 % slower).
 constexpr int64_t kSmallLaunchWorkgroups = 2 * kComputeUnits;
 constexpr int kMaxPartitions = 1 << 16;
+// Devices a process may use the library on (per-device caches).
+constexpr int kMaxDevices = 64;
+
+// Groups of 4 and 8 query heads (the matrix-core kernel) whose sequences span
+// more than one partition split the batch's work evenly over the workgroups
+// the GPU holds at once instead of one workgroup per partition. Pieces of a
+// sequence are then at least P tokens long, except where a run begins or
+// ends, so a sequence has at most ceil(L / P) + 1 of them. Each workgroup
+// reads all S lengths first, which bounds S; positions in the split are
+// 32-bit.
+constexpr int kEvenSplitMaxSeqs = 1024;
+inline bool decode_even_split(int S, int Hq, int Hkv, int P, int64_t partitions) {
+  const int G = Hkv > 0 ? Hq / Hkv : 0;
+  if ((G != 4 && G != 8) || partitions < 2 || S > kEvenSplitMaxSeqs) return false;
+  const int64_t units = (int64_t)S * Hkv * partitions * (P / kDecodeUnit);
+  const int64_t runs = (int64_t)S * Hkv * partitions + 8;
+  return units + runs + 9 * (int64_t)(P / kDecodeUnit) < ((int64_t)1 << 31);
+}
 
 // Arguments of the decode partition kernel (passed by value in the kernarg segment).
 struct DecodeArgs {
@@ -65,10 +83,13 @@ struct DecodeArgs {
   const int32_t* lens;               // [S]
   float* part_acc;                   // [S][Hq][Pmax][D]   (unused when Pmax == 1)
   float* part_ml;                    // [S][Hq][Pmax][2]   (running max, sum; log2 domain)
+  int32_t* part_np;                  // [S][Hkv] pieces per sequence and KV head when the work
+                                     // is split evenly (nullptr: one per partition)
   int S, Hq, Hkv, NB, MB;
   int B;                             // block size in tokens (multiple of 16)
   int P;                             // partition size in tokens (multiple of 16)
-  int Pmax;                          // partitions the launch covers
+  int Pmax;                          // partial rows per (sequence, query head); lengths are
+                                     // clamped to Pmax * P, or (Pmax - 1) * P when split evenly
   float scale_log2;                  // softmax scale times log2(e)
 };
 

@@ -8,6 +8,7 @@ import re
 import pytest
 
 from conftest import ROOT
+from decode_rules import even_split
 
 HEADER = os.path.join(ROOT, "include", "pa.h")
 LIB = os.path.join(ROOT, "paged_kv_cache_151_amd", "libpa.so")
@@ -120,8 +121,33 @@ def test_workspace_size_is_exact_or_zero(lib):
             assert got == 0
             continue
         parts = -(-L // P)
-        want = S * Hq * parts * (D + 2) * 4 if parts > 1 else 0
+        even = even_split(S, Hq, Hkv, P, parts)
+        want = S * Hq * (parts + even) * (D + 2) * 4 + even * S * Hkv * 4 if parts > 1 else 0
         assert got == (want if want < (1 << 64) else 0), (S, Hq, D, L, P, got, want)
+
+
+def test_workspace_of_the_even_split(lib):
+    # one more partial per (sequence, query head) and a piece count per
+    # (sequence, KV head) when the work is split evenly
+    ws = lib.pa_decode_workspace_bytes
+    assert ws(128, 32, 8, 128, 16, 2500, 0) == 128 * 32 * 4 * 130 * 4 + 128 * 8 * 4
+    assert ws(128, 64, 8, 128, 16, 2500, 0) == 128 * 64 * 4 * 130 * 4 + 128 * 8 * 4
+    assert ws(128, 16, 8, 128, 16, 2500, 0) == 128 * 16 * 3 * 130 * 4     # groups of 2
+    assert ws(1025, 32, 8, 128, 16, 2500, 0) == 1025 * 32 * 3 * 130 * 4   # over 1024 sequences
+    assert ws(64, 32, 8, 128, 16, 993, 0) == 0                            # one partition
+    # split positions past 32 bits: one piece per partition
+    assert ws(1024, 32, 8, 128, 16, 1 << 22, 16) == 1024 * 32 * (1 << 18) * 130 * 4
+    rng = __import__("numpy").random.default_rng(12)
+    for _ in range(300):
+        S = int(rng.integers(1, 1200))
+        Hkv = int(rng.choice([1, 2, 8]))
+        Hq = Hkv * int(rng.choice([1, 2, 4, 8]))
+        P = 16 * int(rng.integers(1, 80))
+        L = int(rng.integers(1, 200000))
+        parts = -(-L // P)
+        even = even_split(S, Hq, Hkv, P, parts)
+        want = S * Hq * (parts + even) * 130 * 4 + even * S * Hkv * 4 if parts > 1 else 0
+        assert ws(S, Hq, Hkv, 128, 16, L, P) == want, (S, Hq, Hkv, L, P)
 
 
 def test_default_partition_keeps_a_workgroup_per_compute_unit(lib):

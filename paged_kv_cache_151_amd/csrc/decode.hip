@@ -468,16 +468,22 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(const DecodeArgs a, i
   np = np > a.Pmax ? a.Pmax : np;
   if (np <= 1) return;
   const int64_t row0 = ((int64_t)s * a.Hq + hq) * a.Pmax;
-  float mx = kNegBig;
-  for (int p = 0; p < np; ++p) mx = __builtin_fmaxf(mx, a.part_ml[(row0 + p) * 2]);
-  float den = 0.f, n0 = 0.f, n1 = 0.f;
+  // one pass, rescaling to the running maximum: the loads of all pieces are
+  // independent of the arithmetic and go out together
+  float mx = kNegBig, den = 0.f, n0 = 0.f, n1 = 0.f;
   const int d = 2 * threadIdx.x;
+#pragma unroll 4
   for (int p = 0; p < np; ++p) {
-    const float f = __builtin_amdgcn_exp2f(a.part_ml[(row0 + p) * 2] - mx);
-    den += f * a.part_ml[(row0 + p) * 2 + 1];
+    const float mp = a.part_ml[(row0 + p) * 2];
+    const float lp = a.part_ml[(row0 + p) * 2 + 1];
     const float2 v = *reinterpret_cast<const float2*>(a.part_acc + (row0 + p) * D + d);
-    n0 += f * v.x;
-    n1 += f * v.y;
+    const float mn = __builtin_fmaxf(mx, mp);
+    const float fo = __builtin_amdgcn_exp2f(mx - mn);
+    const float fp = __builtin_amdgcn_exp2f(mp - mn);
+    den = den * fo + fp * lp;
+    n0 = n0 * fo + fp * v.x;
+    n1 = n1 * fo + fp * v.y;
+    mx = mn;
   }
   _Float16* o = a.out + ((int64_t)s * a.Hq + hq) * D + d;
   o[0] = (_Float16)(den > 0.f ? n0 / den : 0.f);

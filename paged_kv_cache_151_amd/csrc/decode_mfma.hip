@@ -450,9 +450,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
     }
   }
 
-  // N = units of one KV head over the batch; the run length q
+  // every length once, into registers (lane l holds sequences 64c + l), so
+  // the sum below and the search for the run's first pair need one round
+  // trip to memory between them
+  constexpr int kChunks = kEvenSplitMaxSeqs / 64;
+  int lc[kChunks];
   int acc = 0;
-  for (int c = lane; c < a.S; c += 64) acc += (clamped_len(a, c, B, cap) + U - 1) / U;
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    lc[c] = 64 * c + lane < a.S ? clamped_len(a, 64 * c + lane, B, cap) : 0;
+    acc += (lc[c] + U - 1) / U;
+  }
+  // N = units of one KV head over the batch; the run length q
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) acc += __shfl_xor(acc, d);
   const int N = __builtin_amdgcn_readfirstlane(acc);
@@ -469,25 +478,30 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
   int g = __builtin_amdgcn_readfirstlane(begin / N);
   const int r = begin - g * N;
   int s = 0, cs = 0, ns = 0, Ls = 0;
-  for (int c = 0, base = 0; c < a.S; c += 64) {
-    const int L = c + lane < a.S ? clamped_len(a, c + lane, B, cap) : 0;
-    const int n = (L + U - 1) / U;
-    int incl = n;
+  bool found = false;
+  int base = 0;
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int t = __shfl_up(incl, d);
-      incl += lane >= d ? t : 0;
+  for (int c = 0; c < kChunks; ++c) {
+    if (!found && 64 * c < a.S) {
+      const int n = (lc[c] + U - 1) / U;
+      int incl = n;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int t = __shfl_up(incl, d);
+        incl += lane >= d ? t : 0;
+      }
+      const unsigned long long hit = __builtin_amdgcn_ballot_w64(base + incl > r);
+      if (hit) {
+        const int f = __builtin_ctzll(hit);
+        s = 64 * c + f;
+        ns = __builtin_amdgcn_readlane(n, f);
+        Ls = __builtin_amdgcn_readlane(lc[c], f);
+        cs = base + __builtin_amdgcn_readlane(incl, f) - ns;
+        found = true;
+      } else {
+        base += __builtin_amdgcn_readlane(incl, 63);
+      }
     }
-    const unsigned long long hit = __builtin_amdgcn_ballot_w64(base + incl > r);
-    if (hit) {
-      const int f = __builtin_ctzll(hit);
-      s = c + f;
-      ns = __builtin_amdgcn_readlane(n, f);
-      Ls = __builtin_amdgcn_readlane(L, f);
-      cs = base + __builtin_amdgcn_readlane(incl, f) - ns;
-      break;
-    }
-    base += __builtin_amdgcn_readlane(incl, 63);
   }
   s = __builtin_amdgcn_readfirstlane(s);
   ns = __builtin_amdgcn_readfirstlane(ns);

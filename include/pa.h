@@ -81,6 +81,36 @@ const char* pa_last_error(void);
 int pa_version(void);
 
 /*
+ * pa_debug_bounds_violations — the bounds-checked debug build. libpa_debug.so
+ * is built from the same sources with every global-memory access of every
+ * kernel (K/V tiles and rows inside their pool, query rows, table entries,
+ * lengths, output and partial elements, slots, copy pairs) first compared with
+ * the extent of its buffer as the call's sizes define it. An access that
+ * would leave its buffer is not made (a load reads zeros, a store is dropped)
+ * and is counted at its check site; nothing traps. This call waits for the
+ * device (hipDeviceSynchronize), copies the per-site counts accumulated since
+ * the previous call into counts[0 .. n) (at most n of them; counts may be
+ * NULL), resets them, and returns the number of sites. In the release library
+ * (libpa.so), which has no checks and the same kernels otherwise, it returns
+ * -1 and touches nothing; -2 reports a HIP error.
+ * The checks cover the library's own index arithmetic, including for caller
+ * input that the kernels clamp (lengths past the table, table entries outside
+ * the pool, slots outside it): with such input every count must stay 0.
+ */
+int pa_debug_bounds_violations(unsigned int* counts, int n);
+
+/* Name of check site `site` ("length", "table", "query", "pool", "out",
+ * "partial", "slot", "pair"), or NULL outside [0, sites). Either library. */
+const char* pa_debug_bounds_site(int site);
+
+/* Self-test of the debug build's counting path: enqueues, on the null stream,
+ * one kernel per source file with kernels that counts one refusal at every
+ * site of that file's counters and touches no other memory. Returns the
+ * number of such kernels (so the next pa_debug_bounds_violations reports that
+ * count at every site), -1 in the release library, -2 on a launch error. */
+int pa_debug_bounds_selftest(void);
+
+/*
  * pa_slot_mapping — where new tokens go ([L], "How PagedAttention works",
  * steps 2-3: a new token takes the next slot of the sequence's last block;
  * listing paged_vs_contiguous.py: token t is at offset t % B of the physical

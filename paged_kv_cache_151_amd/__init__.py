@@ -17,65 +17,97 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libpa.so")
+# the same library with every kernel's global-memory accesses bounds-checked
+# (python paged_kv_cache_151_amd/build.py --debug); see use_library
+DEBUG_LIB_PATH = os.path.join(_PKG, "libpa_debug.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python paged_kv_cache_151_amd/build.py`")
 
-_lib = ctypes.CDLL(LIB_PATH)
-
 _p = ctypes.c_void_p
 _i = ctypes.c_int
-_lib.pa_status_str.restype = ctypes.c_char_p
-_lib.pa_status_str.argtypes = [_i]
-_lib.pa_last_error.restype = ctypes.c_char_p
-_lib.pa_last_error.argtypes = []
-_lib.pa_version.restype = _i
-_lib.pa_slot_mapping.restype = _i
-_lib.pa_slot_mapping.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
-_lib.pa_write_kv.restype = _i
-_lib.pa_write_kv.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
-_lib.pa_copy_blocks.restype = _i
-_lib.pa_copy_blocks.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _p]
-_lib.pa_swap_blocks.restype = _i
-_lib.pa_swap_blocks.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p]
-_lib.pa_decode_partition_size.restype = _i
-_lib.pa_decode_partition_size.argtypes = [_i, _i, _i, _i, _i, _i]
-_lib.pa_decode_workspace_bytes.restype = ctypes.c_size_t
-_lib.pa_decode_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i]
-_lib.pa_decode.restype = _i
-_lib.pa_decode.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i,
-                           ctypes.c_float, _i, _p, ctypes.c_size_t, _p]
-_lib.pa_decode_static.restype = _i
-_lib.pa_decode_static.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i,
-                                  ctypes.c_float, _i, _p]
-_lib.pa_decode_static_scratch_bytes.restype = ctypes.c_size_t
-_lib.pa_decode_static_scratch_bytes.argtypes = []
 
-_lib.pa_prefill.restype = _i
-_lib.pa_prefill.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _i,
-                            ctypes.c_float, _p]
-_lib.pa_stream_read.restype = _i
-_lib.pa_stream_read.argtypes = [_p, ctypes.c_size_t, _p, _i, _p]
-_lib.pa_bm_create.restype = _i
-_lib.pa_bm_create.argtypes = [_i, _i, _i, ctypes.POINTER(_p)]
-_lib.pa_bm_destroy.restype = None
-_lib.pa_bm_destroy.argtypes = [_p]
-_lib.pa_bm_add_sequence.restype = _i
-_lib.pa_bm_add_sequence.argtypes = [_p, ctypes.POINTER(_i)]
-_lib.pa_bm_fork.restype = _i
-_lib.pa_bm_fork.argtypes = [_p, _i, ctypes.POINTER(_i)]
-_lib.pa_bm_append_tokens.restype = _i
-_lib.pa_bm_append_tokens.argtypes = [_p, _p, _i, _p, _p, _i, ctypes.POINTER(_i), ctypes.POINTER(_i)]
-_lib.pa_bm_release.restype = _i
-_lib.pa_bm_release.argtypes = [_p, _i, ctypes.POINTER(_i)]
-_lib.pa_bm_get_table.restype = _i
-_lib.pa_bm_get_table.argtypes = [_p, _i, _p, _i, ctypes.POINTER(_i), ctypes.POINTER(ctypes.c_int64)]
-_lib.pa_bm_export.restype = _i
-_lib.pa_bm_export.argtypes = [_p, _p, _i, _p, _i, _p]
-_lib.pa_bm_num_free.restype = _i
-_lib.pa_bm_num_free.argtypes = [_p]
-_lib.pa_bm_refcount.restype = _i
-_lib.pa_bm_refcount.argtypes = [_p, _i]
+
+def _declare(_lib):
+    """Sets the argument and result types of every entry point of `_lib`."""
+    _lib.pa_debug_bounds_violations.restype = _i
+    _lib.pa_debug_bounds_violations.argtypes = [_p, _i]
+    _lib.pa_debug_bounds_site.restype = ctypes.c_char_p
+    _lib.pa_debug_bounds_site.argtypes = [_i]
+    _lib.pa_debug_bounds_selftest.restype = _i
+    _lib.pa_debug_bounds_selftest.argtypes = []
+    _lib.pa_status_str.restype = ctypes.c_char_p
+    _lib.pa_status_str.argtypes = [_i]
+    _lib.pa_last_error.restype = ctypes.c_char_p
+    _lib.pa_last_error.argtypes = []
+    _lib.pa_version.restype = _i
+    _lib.pa_slot_mapping.restype = _i
+    _lib.pa_slot_mapping.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
+    _lib.pa_write_kv.restype = _i
+    _lib.pa_write_kv.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
+    _lib.pa_copy_blocks.restype = _i
+    _lib.pa_copy_blocks.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _p]
+    _lib.pa_swap_blocks.restype = _i
+    _lib.pa_swap_blocks.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p]
+    _lib.pa_decode_partition_size.restype = _i
+    _lib.pa_decode_partition_size.argtypes = [_i, _i, _i, _i, _i, _i]
+    _lib.pa_decode_workspace_bytes.restype = ctypes.c_size_t
+    _lib.pa_decode_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i]
+    _lib.pa_decode.restype = _i
+    _lib.pa_decode.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i,
+                               ctypes.c_float, _i, _p, ctypes.c_size_t, _p]
+    _lib.pa_decode_static.restype = _i
+    _lib.pa_decode_static.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i,
+                                      ctypes.c_float, _i, _p]
+    _lib.pa_decode_static_scratch_bytes.restype = ctypes.c_size_t
+    _lib.pa_decode_static_scratch_bytes.argtypes = []
+
+    _lib.pa_prefill.restype = _i
+    _lib.pa_prefill.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _i,
+                                ctypes.c_float, _p]
+    _lib.pa_stream_read.restype = _i
+    _lib.pa_stream_read.argtypes = [_p, ctypes.c_size_t, _p, _i, _p]
+    _lib.pa_bm_create.restype = _i
+    _lib.pa_bm_create.argtypes = [_i, _i, _i, ctypes.POINTER(_p)]
+    _lib.pa_bm_destroy.restype = None
+    _lib.pa_bm_destroy.argtypes = [_p]
+    _lib.pa_bm_add_sequence.restype = _i
+    _lib.pa_bm_add_sequence.argtypes = [_p, ctypes.POINTER(_i)]
+    _lib.pa_bm_fork.restype = _i
+    _lib.pa_bm_fork.argtypes = [_p, _i, ctypes.POINTER(_i)]
+    _lib.pa_bm_append_tokens.restype = _i
+    _lib.pa_bm_append_tokens.argtypes = [_p, _p, _i, _p, _p, _i, ctypes.POINTER(_i), ctypes.POINTER(_i)]
+    _lib.pa_bm_release.restype = _i
+    _lib.pa_bm_release.argtypes = [_p, _i, ctypes.POINTER(_i)]
+    _lib.pa_bm_get_table.restype = _i
+    _lib.pa_bm_get_table.argtypes = [_p, _i, _p, _i, ctypes.POINTER(_i), ctypes.POINTER(ctypes.c_int64)]
+    _lib.pa_bm_export.restype = _i
+    _lib.pa_bm_export.argtypes = [_p, _p, _i, _p, _i, _p]
+    _lib.pa_bm_num_free.restype = _i
+    _lib.pa_bm_num_free.argtypes = [_p]
+    _lib.pa_bm_refcount.restype = _i
+    _lib.pa_bm_refcount.argtypes = [_p, _i]
+    return _lib
+
+
+_lib = _declare(ctypes.CDLL(LIB_PATH))
+
+
+def use_library(path: str = LIB_PATH) -> str:
+    """Routes every following call to the library at `path` (for example
+    DEBUG_LIB_PATH, the bounds-checked build); returns the path in use before.
+    Tensors, streams and results are unaffected: both libraries take the same
+    arguments."""
+    global _lib, _lib_path
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with paged_kv_cache_151_amd/build.py")
+    before = _lib_path
+    _lib = _declare(ctypes.CDLL(path))
+    _lib_path = path
+    return before
+
+
+_lib_path = LIB_PATH
 
 PA_OK = 0
 
@@ -155,6 +187,25 @@ def lib() -> ctypes.CDLL:
 
 def pa_version() -> int:
     return _lib.pa_version()
+
+
+def pa_debug_bounds_selftest() -> int:
+    """Debug library: counts one refusal at every site in each source file's
+    counters; returns how many files (-1 in the release library)."""
+    return _lib.pa_debug_bounds_selftest()
+
+
+def pa_debug_bounds_violations():
+    """Accesses the bounds-checked library refused since the last call, per
+    check site ({site name: count}), then reset; None from the release library,
+    which has no checks."""
+    counts = (ctypes.c_uint * 16)()
+    n = _lib.pa_debug_bounds_violations(counts, 16)
+    if n == -1:
+        return None
+    if n < 0:
+        raise RuntimeError("pa_debug_bounds_violations: HIP error")
+    return {_lib.pa_debug_bounds_site(i).decode(): int(counts[i]) for i in range(n)}
 
 
 def pa_slot_mapping(block_tables, block_size: int, num_blocks: int, context_lens=None,

@@ -1,6 +1,7 @@
 """Build libpa.so (the HIP kernels and the C ABI) in-tree for gfx950.
 
-    python paged_kv_cache_151_amd/build.py   (run by path: importing the package needs the library)
+    python paged_kv_cache_151_amd/build.py [--debug]   (run by path: importing the package
+                                                        needs the library)
 
 Compiles every time it is called; the result lands next to this file so that
 it travels with the source tree.
@@ -17,6 +18,8 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libpa.so")
+# the same sources with every kernel's global-memory accesses bounds-checked
+DEBUG_LIB = os.path.join(PKG, "libpa_debug.so")
 ARCH = "gfx950"
 
 HIP_FLAGS = [
@@ -43,12 +46,17 @@ def sources():
     return sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.cpp")))
 
 
-def build(verbose: bool = False) -> str:
-    """Compiles every source into libpa.so. PA_HIPCC_EXTRA (environment) adds
-    hipcc arguments, e.g. "-DPA_MFMA_WAVES=2" to build a variant of the
-    kernels' compile-time tuning parameters."""
-    tmp = LIB + f".tmp{os.getpid()}"
+def build(verbose: bool = False, debug: bool = False) -> str:
+    """Compiles every source into libpa.so, or with debug=True into
+    libpa_debug.so with the kernels' bounds checks on (PA_DEBUG_BOUNDS=1).
+    PA_HIPCC_EXTRA (environment) adds hipcc arguments, e.g.
+    "-DPA_MFMA_WAVES=2" to build a variant of the kernels' compile-time tuning
+    parameters."""
+    out = DEBUG_LIB if debug else LIB
+    tmp = out + f".tmp{os.getpid()}"
     extra = shlex.split(os.environ.get("PA_HIPCC_EXTRA", ""))
+    if debug:
+        extra.append("-DPA_DEBUG_BOUNDS=1")
     cmd = [hipcc(), *HIP_FLAGS, *extra, "-I", os.path.join(ROOT, "include"),
            "-I", os.path.join(PKG, "csrc"), *sources(), "-o", tmp]
     if verbose:
@@ -61,9 +69,9 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{msgs}")
     if verbose and msgs.strip():
         print(msgs)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, debug="--debug" in sys.argv))

@@ -10,6 +10,7 @@
 #include "decode_call.h"
 #include "pa_internal.h"
 #include "prefill_internal.h"
+#include "pa_debug.h"
 
 namespace pa {
 hipError_t launch_stream_read(const void* buf, size_t bytes, void* sink, int workgroups,
@@ -188,6 +189,41 @@ const char* pa_status_str(int status) {
 const char* pa_last_error(void) { return pa::last_error(); }
 
 int pa_version(void) { return 200; }
+
+const char* pa_debug_bounds_site(int site) {
+  static const char* const names[pa::kBsSites] = {
+      "length", "table", "query", "pool", "out", "partial", "slot", "pair"};
+  return site >= 0 && site < pa::kBsSites ? names[site] : nullptr;
+}
+
+int pa_debug_bounds_selftest(void) {
+#if PA_DEBUG_BOUNDS
+  if (pa::bounds_take_cache_ops_selftest() != hipSuccess ||
+      pa::bounds_take_decode_selftest() != hipSuccess ||
+      pa::bounds_take_decode_mfma_selftest() != hipSuccess ||
+      pa::bounds_take_prefill_selftest() != hipSuccess)
+    return -2;
+  return 4;
+#else
+  return -1;
+#endif
+}
+
+int pa_debug_bounds_violations(unsigned int* counts, int n) {
+#if PA_DEBUG_BOUNDS
+  if (hipDeviceSynchronize() != hipSuccess) return -2;
+  unsigned int acc[pa::kBsSites] = {};
+  if (pa::bounds_take_cache_ops(acc) != hipSuccess || pa::bounds_take_decode(acc) != hipSuccess ||
+      pa::bounds_take_decode_mfma(acc) != hipSuccess || pa::bounds_take_prefill(acc) != hipSuccess)
+    return -2;
+  for (int i = 0; counts && i < n && i < pa::kBsSites; ++i) counts[i] = acc[i];
+  return pa::kBsSites;
+#else
+  (void)counts;
+  (void)n;
+  return -1;
+#endif
+}
 
 pa_status pa_slot_mapping(int64_t* slot_mapping, const int32_t* block_tables,
                           const int32_t* seq_ids, const int32_t* positions,

@@ -3,6 +3,7 @@
 // [L] "Paged Attention: OS-Inspired Memory Management for KV Caches",
 //     sections "How PagedAttention works" and "Memory sharing across requests".
 // All three are bit-level: no arithmetic touches the cached values.
+#include "pa_debug.h"
 #include "pa_internal.h"
 
 namespace pa {
@@ -19,11 +20,12 @@ __global__ __launch_bounds__(256) void slot_mapping_kernel(
   const int s = seq_ids ? seq_ids[i] : i;
   int64_t slot = -1;
   if (s >= 0 && s < S) {
-    const int t = positions ? positions[i] : lens[s] - 1;
+    const int t = positions ? positions[i] : (PA_IN_BOUNDS(kBsLength, s < S) ? lens[s] - 1 : -1);
     if (t >= 0) {
       const int j = t / B;
       if (j < MB) {
-        const int phys = tables[(int64_t)s * MB + j];
+        const int64_t te = (int64_t)s * MB + j;
+        const int phys = PA_IN_BOUNDS(kBsTable, te >= 0 && te < (int64_t)S * MB) ? tables[te] : -1;
         if (phys >= 0 && phys < NB) slot = (int64_t)phys * B + (t - j * B);
       }
     }
@@ -48,6 +50,7 @@ __global__ __launch_bounds__(256) void write_kv_kernel(
   const int64_t blk = slot / B;
   const int off = (int)(slot - blk * B);
   const int64_t dst = ((blk * Hkv + h) * B + off) * chunks + c;
+  if (!PA_IN_BOUNDS(kBsPool, dst >= 0 && dst < n_slots * Hkv * chunks)) return;
   k_pool[dst] = key[e];
   v_pool[dst] = value[e];
 }
@@ -74,6 +77,7 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(
   const uint4* vs = v_src + (int64_t)src * chunks;
   uint4* kd = k_dst + (int64_t)dst * chunks;
   uint4* vd = v_dst + (int64_t)dst * chunks;
+  if (!PA_IN_BOUNDS(kBsPair, lo >= 0 && hi <= chunks)) return;
   for (int64_t x = lo + threadIdx.x; x < hi; x += blockDim.x) {
     const uint4 a = ks[x];
     const uint4 b = vs[x];
@@ -83,6 +87,8 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(
 }
 
 }  // namespace
+
+PA_BOUNDS_COLLECTOR(bounds_take_cache_ops)
 
 hipError_t launch_slot_mapping(int64_t* slots, const int32_t* tables, const int32_t* seq_ids,
                                const int32_t* positions, const int32_t* lens, int T, int S,

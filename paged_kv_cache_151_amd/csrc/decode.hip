@@ -32,6 +32,7 @@
 // that block takes a masked path that selects (never multiplies) so NaN or
 // Inf in unused slots cannot reach the result. Arithmetic order depends only
 // on logical positions, so physical ids never change an output bit.
+#include "pa_debug.h"
 #include "pa_internal.h"
 
 namespace pa {
@@ -246,16 +247,18 @@ void decode_partition_kernel(const DecodeArgs a) {
   const int s = id % a.S;
   const int p = id / a.S;
 
-  int L = a.lens[s];
+  int L = PA_IN_BOUNDS(kBsLength, s < a.S) ? a.lens[s] : 0;
   L = L < 0 ? 0 : L;
   L = L > a.MB * B ? a.MB * B : L;
   L = L > a.Pmax * a.P ? a.Pmax * a.P : L;
   const int tok0 = p * a.P;
   const int hq0 = g * G;
+  const int64_t n_out = (int64_t)a.S * a.Hq * D;   // elements of out and of the query
   if (tok0 >= L) {
     if (p == 0) {  // empty sequence: zero output
       for (int e = threadIdx.x; e < G * D; e += NW * 64) {
-        a.out[((int64_t)s * a.Hq + hq0 + e / D) * D + (e % D)] = (_Float16)0.f;
+        const int64_t o = ((int64_t)s * a.Hq + hq0 + e / D) * D + (e % D);
+        if (PA_IN_BOUNDS(kBsOut, o >= 0 && o < n_out)) a.out[o] = (_Float16)0.f;
       }
     }
     return;
@@ -276,7 +279,10 @@ void decode_partition_kernel(const DecodeArgs a) {
   u32x4 q[HPW];
 #pragma unroll
   for (int h = 0; h < HPW; ++h) {
-    q[h] = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)s * a.Hq + hw0 + h) * D + 8 * c);
+    const int64_t qo = ((int64_t)s * a.Hq + hw0 + h) * D + 8 * c;
+    q[h] = PA_IN_BOUNDS(kBsQuery, qo >= 0 && qo + 8 <= n_out)
+               ? *reinterpret_cast<const u32x4*>(a.q + qo)
+               : u32x4{0, 0, 0, 0};
   }
   float m[HPW], l[HPW], acc[HPW][8];
 #pragma unroll
@@ -289,6 +295,8 @@ void decode_partition_kernel(const DecodeArgs a) {
 
   const int32_t* trow = a.tables + (int64_t)s * a.MB + blk0;
   const unsigned lane_off = (r * D + 8 * c) * 2u;   // bytes
+  const int64_t pool_elems = (int64_t)a.NB * a.Hkv * B * D;
+  (void)pool_elems;
 
   // Blocks are walked in chunks of 64: one lane holds one table entry of the
   // chunk and v_readlane hands the wave its entry, so no table access sits
@@ -303,7 +311,10 @@ void decode_partition_kernel(const DecodeArgs a) {
   // leaves the pool; the result for such input is unspecified).
   for (int cb = 0; cb < nblk; cb += 64) {
     const int ce = cb + 64 < nblk ? cb + 64 : nblk;
-    const int tbl = cb + lane < ce ? trow[cb + lane] : -1;
+    const int tbl = cb + lane < ce && PA_IN_BOUNDS(kBsTable, (int64_t)s * a.MB + blk0 + cb + lane <
+                                                              (int64_t)a.S * a.MB)
+                        ? trow[cb + lane]
+                        : -1;
     // the partition's units (counted from its start) whose block is in [cb, ce)
     const int ub0 = kSplit ? cb / 2 : (blk0 + cb) * UPB - U0;
     const int ue0 = kSplit ? (ce + 1) / 2 : (blk0 + ce) * UPB - U0;
@@ -335,14 +346,19 @@ void decode_partition_kernel(const DecodeArgs a) {
         const int64_t b1 = locate_half(uu, 1);
         const int v0 = valid < 8 ? valid : 8;
         const int v1 = valid - 8 < 0 ? 0 : (valid - 8 > 8 ? 8 : valid - 8);
-        const int n0 = live ? v0 * (kHeadDim * 2) : 0;
-        const int n1 = live ? v1 * (kHeadDim * 2) : 0;
+        int n0 = live ? v0 * (kHeadDim * 2) : 0;
+        int n1 = live ? v1 * (kHeadDim * 2) : 0;
+        // each half tile (8 rows) inside the pool
+        if (!PA_IN_BOUNDS(kBsPool, b0 >= 0 && b0 + 8 * kHeadDim <= pool_elems)) n0 = 0;
+        if (!PA_IN_BOUNDS(kBsPool, b1 >= 0 && b1 + 8 * kHeadDim <= pool_elems)) n1 = 0;
         load_tile_split<NT>(t, a.k_pool + b0, a.v_pool + b0, n0, a.k_pool + b1, a.v_pool + b1, n1,
                             lane_off);
       } else {
         const int64_t base = locate(uu);
         const int valid = len - uu * kUnit;
-        const int nbytes = !live ? 0 : (valid >= kUnit ? kUnitBytes : valid * (kHeadDim * 2));
+        int nbytes = !live ? 0 : (valid >= kUnit ? kUnitBytes : valid * (kHeadDim * 2));
+        // the unit's whole tile (16 rows) inside the pool
+        if (!PA_IN_BOUNDS(kBsPool, base >= 0 && base + kUnit * kHeadDim <= pool_elems)) nbytes = 0;
         load_tile<NT>(t, a.k_pool + base, a.v_pool + base, nbytes, lane_off);
       }
     };
@@ -442,13 +458,16 @@ void decode_partition_kernel(const DecodeArgs a) {
     const int hq = hq0 + h;
     if (nparts == 1) {
       const float o = lsum > 0.f ? num / lsum : 0.f;
-      a.out[((int64_t)s * a.Hq + hq) * D + d] = (_Float16)o;
+      const int64_t oi = ((int64_t)s * a.Hq + hq) * D + d;
+      if (PA_IN_BOUNDS(kBsOut, oi >= 0 && oi < n_out)) a.out[oi] = (_Float16)o;
     } else {
       const int64_t row = ((int64_t)s * a.Hq + hq) * a.Pmax + p;
-      a.part_acc[row * D + d] = num;
-      if (d == 0) {
-        a.part_ml[row * 2] = mx;
-        a.part_ml[row * 2 + 1] = lsum;
+      if (PA_IN_BOUNDS(kBsPartial, row >= 0 && row < (int64_t)a.S * a.Hq * a.Pmax)) {
+        a.part_acc[row * D + d] = num;
+        if (d == 0) {
+          a.part_ml[row * 2] = mx;
+          a.part_ml[row * 2 + 1] = lsum;
+        }
       }
     }
   }
@@ -461,13 +480,16 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(const DecodeArgs a, i
   constexpr int D = kHeadDim;
   const int hq = blockIdx.x % a.Hq;
   const int s = blockIdx.x / a.Hq;
-  int L = a.lens[s];
+  int L = PA_IN_BOUNDS(kBsLength, s < a.S) ? a.lens[s] : 0;
   L = L < 0 ? 0 : L;
   L = L > B_MB ? B_MB : L;
-  int np = a.part_np ? a.part_np[s * a.Hkv + hq / (a.Hq / a.Hkv)] : (L + a.P - 1) / a.P;
+  const int pc = s * a.Hkv + hq / (a.Hq / a.Hkv);
+  int np = a.part_np ? (PA_IN_BOUNDS(kBsPartial, pc < a.S * a.Hkv) ? a.part_np[pc] : 0)
+                     : (L + a.P - 1) / a.P;
   np = np > a.Pmax ? a.Pmax : np;
   if (np <= 1) return;
   const int64_t row0 = ((int64_t)s * a.Hq + hq) * a.Pmax;
+  if (!PA_IN_BOUNDS(kBsPartial, row0 >= 0 && row0 + np <= (int64_t)a.S * a.Hq * a.Pmax)) return;
   // one pass, rescaling to the running maximum: the loads of all pieces are
   // independent of the arithmetic and go out together
   float mx = kNegBig, den = 0.f, n0 = 0.f, n1 = 0.f;
@@ -485,7 +507,9 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(const DecodeArgs a, i
     n1 = n1 * fo + fp * v.y;
     mx = mn;
   }
-  _Float16* o = a.out + ((int64_t)s * a.Hq + hq) * D + d;
+  const int64_t oi = ((int64_t)s * a.Hq + hq) * D + d;
+  if (!PA_IN_BOUNDS(kBsOut, oi >= 0 && oi + 2 <= (int64_t)a.S * a.Hq * D)) return;
+  _Float16* o = a.out + oi;
   o[0] = (_Float16)(den > 0.f ? n0 / den : 0.f);
   o[1] = (_Float16)(den > 0.f ? n1 / den : 0.f);
 }
@@ -521,6 +545,8 @@ hipError_t launch_partition_g(const DecodeArgs& a, int G, hipStream_t stream) {
 }
 
 }  // namespace
+
+PA_BOUNDS_COLLECTOR(bounds_take_decode)
 
 hipError_t launch_decode(const DecodeArgs& a, int B, int G, hipStream_t stream) {
   hipError_t e;

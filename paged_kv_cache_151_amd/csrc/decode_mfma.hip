@@ -37,6 +37,7 @@
 // c ^ 2 (r % 8), which keeps the transposing reads free of bank conflicts.
 #include <atomic>
 
+#include "pa_debug.h"
 #include "pa_internal.h"
 
 namespace pa {
@@ -124,6 +125,10 @@ __device__ __forceinline__ void attend_piece(const DecodeArgs& a, int s, int g, 
   const int m = lane & 15;
   const int kq = lane >> 4;
   const int hq0 = g * G;
+  const int64_t n_out = (int64_t)a.S * a.Hq * D;               // elements of out and of the query
+  const int64_t pool_elems = (int64_t)a.NB * a.Hkv * B * D;    // elements of each pool
+  (void)n_out;
+  (void)pool_elems;
   const int nunits = (len + U - 1) / U;
   const int U0 = tok0 / U;
   const int blk0 = kSplit ? 2 * U0 : U0 / UPB;
@@ -141,9 +146,10 @@ __device__ __forceinline__ void attend_piece(const DecodeArgs& a, int s, int g, 
   h8 qf[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    const u32x4 raw = m < G ? *reinterpret_cast<const u32x4*>(
-                                  a.q + ((int64_t)s * a.Hq + hq0 + m) * D + 32 * c + 8 * kq)
-                            : u32x4{0, 0, 0, 0};
+    const int64_t qo = ((int64_t)s * a.Hq + hq0 + m) * D + 32 * c + 8 * kq;
+    const u32x4 raw = m < G && PA_IN_BOUNDS(kBsQuery, qo >= 0 && qo + 8 <= n_out)
+                          ? *reinterpret_cast<const u32x4*>(a.q + qo)
+                          : u32x4{0, 0, 0, 0};
     qf[c] = __builtin_bit_cast(h8, raw ^ qflip);
   }
   f4 o[8];
@@ -179,7 +185,10 @@ __device__ __forceinline__ void attend_piece(const DecodeArgs& a, int s, int g, 
   const int32_t* trow = a.tables + (int64_t)s * a.MB + blk0;
   for (int cb = 0; cb < nblk; cb += 64) {
     const int ce = cb + 64 < nblk ? cb + 64 : nblk;
-    const int tbl = cb + lane < ce ? trow[cb + lane] : -1;
+    const int tbl = cb + lane < ce && PA_IN_BOUNDS(kBsTable, (int64_t)s * a.MB + blk0 + cb + lane <
+                                                              (int64_t)a.S * a.MB)
+                        ? trow[cb + lane]
+                        : -1;
     const int ub0 = kSplit ? cb / 2 : (blk0 + cb) * UPB - U0;
     const int ue0 = kSplit ? (ce + 1) / 2 : (blk0 + ce) * UPB - U0;
     const int ub = ub0 > 0 ? ub0 : 0;
@@ -212,13 +221,16 @@ __device__ __forceinline__ void attend_piece(const DecodeArgs& a, int s, int g, 
         const int64_t b1 = locate_half(uu, 1);
         const int v0 = valid < 8 ? valid : 8;
         const int v1 = valid - 8 < 0 ? 0 : (valid - 8 > 8 ? 8 : valid - 8);
-        const int n0 = live ? v0 * kRowBytesG : 0;
-        const int n1 = live ? v1 * kRowBytesG : 0;
+        // each half tile (8 rows) inside the pool
+        const bool in0 = PA_IN_BOUNDS(kBsPool, b0 >= 0 && b0 + 8 * D <= pool_elems);
+        const bool in1 = PA_IN_BOUNDS(kBsPool, b1 >= 0 && b1 + 8 * D <= pool_elems);
+        const int n0 = live && in0 ? v0 * kRowBytesG : 0;
+        const int n1 = live && in1 ? v1 * kRowBytesG : 0;
         rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16*>(a.v_pool + b0), 0, n0, kRsrcWord3G);
         rv1 = __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16*>(a.v_pool + b1), 0, n1, kRsrcWord3G);
         // K rows past the valid tokens are read from their (clamped, in-pool)
         // block but never used: their scores are masked by selection
-        if (live) {
+        if (live && (m < 8 ? in0 : in1)) {
           const u32x4* kr = reinterpret_cast<const u32x4*>(a.k_pool + (m < 8 ? b0 : b1) + k_elt8);
 #pragma unroll
           for (int c = 0; c < 4; ++c)
@@ -229,7 +241,9 @@ __device__ __forceinline__ void attend_piece(const DecodeArgs& a, int s, int g, 
         }
       } else {
         const int64_t base = locate(uu);
-        const int nbytes = !live ? 0 : (valid >= U ? kTileBytesG : valid * kRowBytesG);
+        int nbytes = !live ? 0 : (valid >= U ? kTileBytesG : valid * kRowBytesG);
+        // the unit's whole tile (16 rows) inside the pool
+        if (!PA_IN_BOUNDS(kBsPool, base >= 0 && base + U * D <= pool_elems)) nbytes = 0;
         rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16*>(a.k_pool + base), 0, nbytes, kRsrcWord3G);
         rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16*>(a.v_pool + base), 0, nbytes, kRsrcWord3G);
         rv1 = rv;
@@ -374,13 +388,16 @@ __device__ __forceinline__ void attend_piece(const DecodeArgs& a, int s, int g, 
     const int hq = hq0 + h;
     if (nparts == 1) {
       const float ov = den > 0.f ? num / den : 0.f;
-      a.out[((int64_t)s * a.Hq + hq) * D + d] = (_Float16)ov;
+      const int64_t oi = ((int64_t)s * a.Hq + hq) * D + d;
+      if (PA_IN_BOUNDS(kBsOut, oi >= 0 && oi < n_out)) a.out[oi] = (_Float16)ov;
     } else {
       const int64_t row = ((int64_t)s * a.Hq + hq) * a.Pmax + p;
-      a.part_acc[row * D + d] = num;
-      if (d == 0) {
-        a.part_ml[row * 2] = mx;
-        a.part_ml[row * 2 + 1] = den;
+      if (PA_IN_BOUNDS(kBsPartial, p >= 0 && p < a.Pmax && row < (int64_t)a.S * a.Hq * a.Pmax)) {
+        a.part_acc[row * D + d] = num;
+        if (d == 0) {
+          a.part_ml[row * 2] = mx;
+          a.part_ml[row * 2 + 1] = den;
+        }
       }
     }
   }
@@ -388,7 +405,7 @@ __device__ __forceinline__ void attend_piece(const DecodeArgs& a, int s, int g, 
 
 // Clamped context length of sequence s: within the table and the launch.
 __device__ __forceinline__ int clamped_len(const DecodeArgs& a, int s, int B, int cap) {
-  int L = a.lens[s];
+  int L = PA_IN_BOUNDS(kBsLength, s >= 0 && s < a.S) ? a.lens[s] : 0;
   L = L < 0 ? 0 : L;
   L = L > a.MB * B ? a.MB * B : L;
   return L > cap ? cap : L;
@@ -397,8 +414,10 @@ __device__ __forceinline__ int clamped_len(const DecodeArgs& a, int s, int B, in
 // Zero output of every query head of KV head g of sequence s (empty sequence).
 template <int G, int NW>
 __device__ __forceinline__ void zero_heads(const DecodeArgs& a, int s, int g) {
-  for (int e = threadIdx.x; e < G * kHeadDim; e += NW * 64)
-    a.out[((int64_t)s * a.Hq + g * G + e / kHeadDim) * kHeadDim + (e % kHeadDim)] = (_Float16)0.f;
+  for (int e = threadIdx.x; e < G * kHeadDim; e += NW * 64) {
+    const int64_t oi = ((int64_t)s * a.Hq + g * G + e / kHeadDim) * kHeadDim + (e % kHeadDim);
+    if (PA_IN_BOUNDS(kBsOut, oi >= 0 && oi < (int64_t)a.S * a.Hq * kHeadDim)) a.out[oi] = (_Float16)0.f;
+  }
 }
 
 // One workgroup per (partition, sequence, KV head), partitions of a.P tokens.
@@ -446,7 +465,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
   for (int s = blockIdx.x; s < a.S; s += nwg) {
     if (clamped_len(a, s, B, cap) == 0) {
       for (int g = 0; g < a.Hkv; ++g) zero_heads<G, NW>(a, s, g);
-      for (int g = threadIdx.x; g < a.Hkv; g += NW * 64) a.part_np[s * a.Hkv + g] = 0;
+      for (int g = threadIdx.x; g < a.Hkv; g += NW * 64)
+        if (PA_IN_BOUNDS(kBsPartial, s * a.Hkv + g < a.S * a.Hkv)) a.part_np[s * a.Hkv + g] = 0;
     }
   }
 
@@ -520,7 +540,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
     const int tok0 = j0 * U;
     const int tok1 = j1 * U < Ls ? j1 * U : Ls;
     attend_piece<BT, G, NW, DEPTH, NT>(a, s, g, tok0, tok1 - tok0, nparts, piece);
-    if (j1 == ns && threadIdx.x == 0) a.part_np[s * a.Hkv + g] = nparts;
+    if (j1 == ns && threadIdx.x == 0 &&
+        PA_IN_BOUNDS(kBsPartial, s * a.Hkv + g < a.S * a.Hkv && nparts <= a.Pmax))
+      a.part_np[s * a.Hkv + g] = nparts;
     pos = pair0 + j1;
     if (pos >= end) break;
     // the next pair in the order with at least one unit
@@ -590,6 +612,8 @@ hipError_t launch_g(const DecodeArgs& a, int B, hipStream_t stream) {
 }
 
 }  // namespace
+
+PA_BOUNDS_COLLECTOR(bounds_take_decode_mfma)
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int B, int G, hipStream_t stream) {
   switch (G) {

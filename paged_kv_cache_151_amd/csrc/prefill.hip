@@ -59,6 +59,7 @@
 // Masking: keys and values past the sequence's L tokens are fetched as zeros
 // by the buffer range check (so NaN or Inf in unused slots never enters a
 // product); causal exclusions select the score to "no token" and p to 0.
+#include "pa_debug.h"
 #include "prefill_internal.h"
 
 namespace pa {
@@ -187,17 +188,22 @@ void prefill_kernel(const PrefillArgs a) {
   const int s = (int)(id % a.S);
   const int g = (int)(id / a.S);
 
-  const int qs0 = a.qstart[s];
-  const int qs1 = a.qstart[s + 1];
+  const bool s_ok = PA_IN_BOUNDS(kBsLength, s >= 0 && s < a.S);
+  const int qs0 = s_ok ? a.qstart[s] : 0;
+  const int qs1 = s_ok ? a.qstart[s + 1] : 0;
   if (qs0 < 0 || qs1 > a.T || qs1 <= qs0) return;
   const int n = qs1 - qs0;
   const int nqb = (n + QB - 1) / QB;
   if (rank >= nqb) return;                 // whole workgroup, before any barrier
   const int qb = nqb - 1 - rank;
-  int L = a.lens[s];
+  int L = s_ok ? a.lens[s] : 0;
   L = L < 0 ? 0 : L;
   L = L > a.MB * B ? a.MB * B : L;
-  const int base_pos = L - n;              // row j sits at position base_pos + j
+  const int base_pos = L - n;
+  const int64_t n_rows = (int64_t)a.T * a.Hq * D;            // elements of the query and out
+  const int64_t pool_bytes = (int64_t)a.NB * a.Hkv * B * kRowBytes;
+  (void)n_rows;
+  (void)pool_bytes;              // row j sits at position base_pos + j
 
   // keys the workgroup walks: [0, kend_wg), as far as its last row sees
   const int jl_wg = (qb * QB + QB < n ? qb * QB + QB : n) - 1;
@@ -239,10 +245,13 @@ void prefill_kernel(const PrefillArgs a) {
     const int j = j0 + 16 * t + m;
     const bool ok = j < n;
     pos[t] = base_pos + j;
-    const _Float16* qrow = a.q + ((int64_t)(qs0 + (ok ? j : 0)) * a.Hq + hq) * D + 8 * kq;
+    const int64_t qo = ((int64_t)(qs0 + (ok ? j : 0)) * a.Hq + hq) * D + 8 * kq;
+    const _Float16* qrow = a.q + qo;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const u32x4 raw = ok ? *reinterpret_cast<const u32x4*>(qrow + 32 * c) : u32x4{0, 0, 0, 0};
+      const u32x4 raw = ok && PA_IN_BOUNDS(kBsQuery, qo >= 0 && qo + 32 * c + 8 <= n_rows)
+                            ? *reinterpret_cast<const u32x4*>(qrow + 32 * c)
+                            : u32x4{0, 0, 0, 0};
       qf[t][c] = __builtin_bit_cast(h8, raw ^ qflip);
     }
   }
@@ -264,8 +273,9 @@ void prefill_kernel(const PrefillArgs a) {
   // the pipeline before its chunk loads, into one of NST registers, so that
   // the wait for a chunk's data always covers them. Entries outside the pool
   // are clamped to block 0.
+  const bool table_ok = PA_IN_BOUNDS(kBsTable, nblk <= a.MB);
   const __amdgpu_buffer_rsrc_t trs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<int32_t*>(a.tables + (int64_t)s * a.MB), 0, nblk * 4, kRsrcWord3);
+      const_cast<int32_t*>(a.tables + (int64_t)s * a.MB), 0, table_ok ? nblk * 4 : 0, kRsrcWord3);
   auto table_load = [&](int chunk) -> int {
     if constexpr (kSplit) {   // lane 2u + h reads the block of half h of unit u
       const int e = 2 * NU * chunk + (lane < 2 * NU ? lane : 0);
@@ -309,9 +319,13 @@ void prefill_kernel(const PrefillArgs a) {
         for (int h = 0; h < 2; ++h) {
           const int t0 = U * kUnitTok + 8 * h;
           const int valid = L - t0 < 8 ? L - t0 : 8;
-          const int nbytes = t0 < kend_wg ? valid * kRowBytes : 0;
+          int nbytes = t0 < kend_wg ? valid * kRowBytes : 0;
           const int phys = ph[2 * (w_u0 + j) + h];
           const uint32_t safe = (unsigned)phys < (unsigned)a.NB ? (uint32_t)phys : 0u;
+          // the half tile (8 rows) inside the pool
+          if (!PA_IN_BOUNDS(kBsPool, (int64_t)g * B * kRowBytes + (int64_t)safe * blk_bytes +
+                                             8 * kRowBytes <= pool_bytes))
+            nbytes = 0;
           const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
               const_cast<unsigned char*>(pg + (uint64_t)safe * blk_bytes), 0, nbytes, kRsrcWord3);
           rs[2 * h] = r;
@@ -321,10 +335,14 @@ void prefill_kernel(const PrefillArgs a) {
         }
       } else {
         const int valid = L - U * kUnitTok < kUnitTok ? L - U * kUnitTok : kUnitTok;
-        const int nbytes = U * kUnitTok < kend_wg ? valid * kRowBytes : 0;
+        int nbytes = U * kUnitTok < kend_wg ? valid * kRowBytes : 0;
         const int phys = ph[w_u0 + j];
         const uint32_t safe = (unsigned)phys < (unsigned)a.NB ? (uint32_t)phys : 0u;
         const uint64_t off = (uint64_t)safe * blk_bytes + (uint32_t)((U % UPB) * kUnitTok * kRowBytes);
+        // the unit's whole tile (16 rows) inside the pool
+        if (!PA_IN_BOUNDS(kBsPool, (int64_t)g * B * kRowBytes + (int64_t)off + kUnitTok * kRowBytes <=
+                                       pool_bytes))
+          nbytes = 0;
         const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<unsigned char*>(pg + off), 0, nbytes, kRsrcWord3);
 #pragma unroll
@@ -538,7 +556,9 @@ void prefill_kernel(const PrefillArgs a) {
     const int j = j0 + 16 * t + m;
     if (j >= n) continue;
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    _Float16* orow = a.out + ((int64_t)(qs0 + j) * a.Hq + hq) * D + 4 * kq;
+    const int64_t oo = ((int64_t)(qs0 + j) * a.Hq + hq) * D + 4 * kq;
+    if (!PA_IN_BOUNDS(kBsOut, oo >= 0 && oo + 16 * 7 + 4 <= n_rows)) continue;
+    _Float16* orow = a.out + oo;
 #pragma unroll
     for (int nn = 0; nn < 8; ++nn) {
       typedef _Float16 h4 __attribute__((ext_vector_type(4)));
@@ -569,6 +589,8 @@ hipError_t launch_bt(const PrefillArgs& a, int G, int64_t grid, hipStream_t stre
 }
 
 }  // namespace
+
+PA_BOUNDS_COLLECTOR(bounds_take_prefill)
 
 int prefill_rows_per_workgroup(int G) {
   const int hw = G < kPrefillWaves ? G : kPrefillWaves;

@@ -41,6 +41,29 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, n), n
 
 
+DEBUG_LIB = os.path.join(ROOT, "paged_kv_cache_151_amd", "libpa_debug.so")
+
+
+def test_debug_library_exports_the_same_entry_points():
+    # the bounds-checked build: same sources, same ABI
+    if not os.path.exists(DEBUG_LIB):
+        pytest.fail("libpa_debug.so not built (run __graft_entry__.build())")
+    dbg = ctypes.CDLL(DEBUG_LIB)
+    for n in declared_functions():
+        assert hasattr(dbg, n), n
+    dbg.pa_debug_bounds_site.restype = ctypes.c_char_p
+    names = [dbg.pa_debug_bounds_site(i) for i in range(8)]
+    assert names == [b"length", b"table", b"query", b"pool", b"out", b"partial", b"slot", b"pair"]
+    assert dbg.pa_debug_bounds_site(8) is None and dbg.pa_debug_bounds_site(-1) is None
+
+
+def test_release_library_has_no_bounds_counters(lib):
+    counts = (ctypes.c_uint * 8)(*([7] * 8))
+    assert lib.pa_debug_bounds_violations(counts, 8) == -1
+    assert list(counts) == [7] * 8     # untouched
+    assert lib.pa_debug_bounds_selftest() == -1
+
+
 def test_status_strings(lib):
     assert lib.pa_status_str(0) == b"PA_OK"
     assert lib.pa_status_str(5) == b"PA_ERR_WORKSPACE"

@@ -112,3 +112,22 @@ def test_relabelling_physical_blocks_is_bit_identical_under_the_split(pa, G):
     got = host(pa.pa_decode(dev(c.query), dev(kp), dev(vp), dev(tables), dev(c.context_lens),
                             c.max_context_len, c.scale, partition_size=256))
     assert np.array_equal(base.view(np.uint16), got.view(np.uint16))
+
+
+@pytest.mark.parametrize("Hq", [32, 64])
+def test_chat_lengths_grouped_heads_full_size_every_output(pa, Hq):
+    """Layer 0 of the batch-128 chat lengths with 8 KV heads (groups of 4 and
+    8) in the benchmark's launch configuration, which takes the even split:
+    every (sequence, head, dimension) of the output against the oracle."""
+    c = W.chat_layer(0, Hq=Hq, Hkv=8)
+    engaged, parts = split_engaged(pa, c, 0)
+    assert engaged and parts == 3, parts
+    say(c.name, f"NB={c.NB} maxL={c.max_context_len} even split")
+    kp, vp = W.device_pools(c.NB, c.Hkv, c.B, c.D, seed=W.chat_pool_seed(0))
+    out = pa.pa_decode(dev(c.query), kp, vp, dev(c.block_tables), dev(c.context_lens),
+                       c.max_context_len, c.scale)
+    got = host(out)
+    k_host, v_host = host(kp), host(vp)
+    del kp, vp
+    ref = oracle.decode(c.query, k_host, v_host, c.block_tables, c.context_lens, c.scale)
+    assert_attention_close(got, ref, c.name)

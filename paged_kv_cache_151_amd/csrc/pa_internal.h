@@ -65,9 +65,14 @@ constexpr int kMaxDevices = 64;
 // reads all S lengths first, which bounds S; positions in the split are
 // 32-bit.
 constexpr int kEvenSplitMaxSeqs = 1024;
+#ifndef PA_EVEN_SPLIT_MIN_PARTS
+#define PA_EVEN_SPLIT_MIN_PARTS 2
+#endif
 inline bool decode_even_split(int S, int Hq, int Hkv, int P, int64_t partitions) {
   const int G = Hkv > 0 ? Hq / Hkv : 0;
-  if ((G != 4 && G != 8) || partitions < 2 || S > kEvenSplitMaxSeqs) return false;
+  if ((G != 4 && G != 8) || partitions < PA_EVEN_SPLIT_MIN_PARTS || partitions < 2 ||
+      S > kEvenSplitMaxSeqs)
+    return false;
   const int64_t units = (int64_t)S * Hkv * partitions * (P / kDecodeUnit);
   const int64_t runs = (int64_t)S * Hkv * partitions + 8;
   return units + runs + 9 * (int64_t)(P / kDecodeUnit) < ((int64_t)1 << 31);

@@ -18,14 +18,22 @@ def pa():
     return pa_module()
 
 
-def test_decode_step_replays_bit_identical(pa):
+def _grouped_case():
+    # groups of 4 over several partitions: the even split, with its piece
+    # counts and partials in the workspace for the reduce kernel
+    return W.make_case("graph_grouped", 8100, [700, 1500, 33, 900, 0, 260, 1023, 64],
+                       Hq=32, Hkv=8, B=16)
+
+
+@pytest.mark.parametrize("which", ["7b", "grouped"])
+def test_decode_step_replays_bit_identical(pa, which):
     import torch
-    c = W.seven_b_single_layer()
+    c = W.seven_b_single_layer() if which == "7b" else _grouped_case()
     say(c.name, "decode step in a graph")
     kp, vp = dev(c.k_pool), dev(c.v_pool)
     tables, lens = dev(c.block_tables), dev(c.context_lens)
     q, k_new, v_new = dev(c.query), dev(c.key_new), dev(c.value_new)
-    P = 256                                   # several partitions: the reduce kernel and workspace are in the graph
+    P = 256   # several partitions: the partials, the reduce kernel and the workspace are in the graph
     ws = torch.empty(max(pa.pa_decode_workspace_bytes(c.S, c.Hq, c.Hkv, c.D, c.B,
                                                       c.max_context_len, P), 16),
                      dtype=torch.uint8, device="cuda")
@@ -54,6 +62,13 @@ def test_decode_step_replays_bit_identical(pa):
         slots.fill_(-1)
         kp.view(-1)[:4096].zero_()            # unrelated eager writes to the pool between replays
         kp.view(-1)[:4096] = dev(c.k_pool).view(-1)[:4096]
+        if r == 1:
+            # an eager call on the same workspace between replays
+            other = torch.empty_like(out)
+            pa.pa_decode(q, kp, vp, tables, lens, c.max_context_len, c.scale, partition_size=P,
+                         out=other, workspace=ws)
+            assert np.array_equal(u16(host(other)), u16(eager))
+            slots.fill_(-1)
         g.replay()
         got = host(out)
         assert np.array_equal(u16(got), u16(eager)), f"replay {r}"

@@ -450,9 +450,12 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeArgs a
 // costs grouped heads about a tenth of a launch in the per-partition grid.
 // Workgroup b runs on XCD b % 8 and takes run (b % 8) * (grid / 8) + b / 8,
 // so each XCD walks one contiguous eighth of the order: one KV head per XCD
-// when there are 8, as in the per-partition grid's order.
+// when there are 8, as in the per-partition grid's order. Four waves per SIMD
+// are asked for explicitly: left to itself the compiler keeps the walk's
+// state in 151 VGPRs and three waves per SIMD; at 127 it needs no spills.
 template <int BT, int G, int NW, int DEPTH, bool NT>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4))) void decode_mfma_even_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void decode_mfma_even_kernel(const DecodeArgs a) {
   constexpr int U = kDecodeUnit;
   const int B = BT > 0 ? BT : a.B;
   const int cap = (a.Pmax - 1) * a.P;   // the launch's bound on every length

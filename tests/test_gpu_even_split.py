@@ -131,3 +131,27 @@ def test_chat_lengths_grouped_heads_full_size_every_output(pa, Hq):
     del kp, vp
     ref = oracle.decode(c.query, k_host, v_host, c.block_tables, c.context_lens, c.scale)
     assert_attention_close(got, ref, c.name)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_even_split_shapes(pa, seed):
+    # batches up to the split's 1,024-sequence limit (16 chunks of lengths per
+    # wave), every block size the kernels specialise, partitions of 16 to 1,024
+    # tokens, lengths with zeros and unit edges
+    rng = np.random.default_rng(6700 + seed)
+    G = int(rng.choice([4, 8]))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    B = int(rng.choice([8, 16, 32, 48]))
+    S = int(rng.choice([3, 65, 300, 1024])) if seed % 3 else 1024
+    top = 160 if S >= 300 else 1800
+    lens = rng.integers(0, top, size=S).astype(np.int32)
+    lens[rng.random(S) < 0.1] = 0
+    edge = rng.random(S) < 0.1
+    lens[edge] = rng.choice([1, 15, 16, 17, 31, 33], size=int(edge.sum()))
+    lens[int(rng.integers(0, S))] = top           # the longest sets the partitions
+    P = int(rng.choice([16, 64])) if top < 1000 else int(rng.choice([0, 64, 1024]))
+    c = W.make_case(f"even_rand_{seed}", 6800 + seed, lens, Hq=G * Hkv, Hkv=Hkv, B=B)
+    engaged, _ = split_engaged(pa, c, P)
+    if not engaged:
+        pytest.skip("this draw gives one partition per sequence")
+    run_and_check(pa, c, P)

@@ -4,8 +4,9 @@ Default workload (`--workload chat`): 128 sequences, context = prompt
 U[100, 2000] + generated U[50, 500] tokens, 32 layers, each with its own K/V
 block pool (32 KV heads, head dim 128, fp16, blocks of 16 tokens, 1.25x pool,
 shuffled physical ids). One step is one decode step of the whole model's
-attention cache path: per layer, the new token's slot (pa_slot_mapping), its
-K/V store (pa_write_kv) and paged decode attention (pa_decode).
+attention cache path: per layer, the new token's slot and K/V store
+(pa_append_kv, the slot mapping and store in one launch) and paged decode
+attention (pa_decode).
 
 Other workloads (`--workload 7b|shared_prefix|long_context|tiny`) time one
 layer per step and rotate over `--replicas` copies of the inputs so that the
@@ -370,8 +371,8 @@ def prefill_flops(new_lens, context_lens, Hq, D):
 
 def bench_prefill(args):
     """Paged prefill of a batch of chat prompts (U[100, 2000] tokens, 32 heads
-    of 128 dims, B = 16): per step, every prompt token's slot (pa_slot_mapping),
-    its K/V store (pa_write_kv) and causal prefill attention through the block
+    of 128 dims, B = 16): per step, every prompt token's slot and K/V store
+    (pa_append_kv) and causal prefill attention through the block
     tables (pa_prefill)."""
     import torch
     import paged_kv_cache_151_amd as pa
@@ -396,8 +397,7 @@ def bench_prefill(args):
     log(f"setup {time.time() - t0:.1f}s: {c.name}, T={c.T}, NB={c.NB}, {flops / 1e9:.1f} GFLOP")
 
     def step(ev=None):
-        pa.pa_slot_mapping(tables, c.B, c.NB, seq_ids=seq, positions=pos, out=slots)
-        pa.pa_write_kv(k_new, v_new, kp, vp, slots)
+        pa.pa_append_kv(k_new, v_new, kp, vp, tables, seq_ids=seq, positions=pos, slot_mapping=slots)
         if ev is not None:
             ev[0].record(stream)
         pa.pa_prefill(q, kp, vp, tables, lens, qs, c.max_query_len, c.scale, out=out)
@@ -499,8 +499,7 @@ def bench_prefix_prefill(args):
 
     def step(ev=None):
         pa.pa_copy_blocks(kp, vp, pairs)
-        pa.pa_slot_mapping(tables, B, NB, seq_ids=seq_d, positions=pos_d, out=slots)
-        pa.pa_write_kv(ks, vs, kp, vp, slots)
+        pa.pa_append_kv(ks, vs, kp, vp, tables, seq_ids=seq_d, positions=pos_d, slot_mapping=slots)
         if ev is not None:
             ev[0].record(stream)
         pa.pa_prefill(q, kp, vp, tables, lens, qs, maxq, d["scale"], out=out)
@@ -614,8 +613,8 @@ def main():
     def step(k, events=None):
         for i, ly in enumerate(steps_inputs[k % len(steps_inputs)]):
             c = ly["case"]
-            pa.pa_slot_mapping(ly["tables"], c.B, c.NB, context_lens=ly["lens"], out=ly["slots"])
-            pa.pa_write_kv(ly["k_new"], ly["v_new"], ly["kp"], ly["vp"], ly["slots"])
+            pa.pa_append_kv(ly["k_new"], ly["v_new"], ly["kp"], ly["vp"], ly["tables"],
+                            context_lens=ly["lens"], slot_mapping=ly["slots"])
             if events is not None:
                 events[i][0].record(stream)
             pa.pa_decode(ly["q"], ly["kp"], ly["vp"], ly["tables"], ly["lens"], maxL, c.scale,

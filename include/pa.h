@@ -156,6 +156,25 @@ pa_status pa_write_kv(const void* key, const void* value, void* k_pool, void* v_
                       hipStream_t stream);
 
 /*
+ * pa_append_kv — pa_slot_mapping and pa_write_kv in one launch ([L], "How
+ * PagedAttention works", steps 2-3: each new token's key and value go into the
+ * next slot of its sequence's last block, found through the block table).
+ *
+ * Token i's slot is computed exactly as pa_slot_mapping computes it (from
+ * seq_ids, positions or context_lens, and block_tables), written to
+ * slot_mapping[i] when slot_mapping is not NULL, and key[i] and value[i] are
+ * then stored into it exactly as pa_write_kv stores them (tokens whose slot is
+ * -1 are skipped). The pools and slot_mapping end bit for bit as after
+ * pa_slot_mapping followed by pa_write_kv with the same arguments; one launch
+ * replaces two. Arguments as in those two calls; slot_mapping may be NULL.
+ * Two tokens with the same slot in one call is a caller error.
+ */
+pa_status pa_append_kv(int64_t* slot_mapping, const void* key, const void* value, void* k_pool,
+                       void* v_pool, const int32_t* block_tables, const int32_t* seq_ids,
+                       const int32_t* positions, const int32_t* context_lens, int T, int S,
+                       int MB, int Hkv, int D, int B, int NB, hipStream_t stream);
+
+/*
  * pa_copy_blocks — copy-on-write of whole blocks ([L], "Memory sharing across
  * requests": a sequence about to write into a block that others share first
  * gets a private copy of it).

@@ -45,6 +45,9 @@ def _declare(_lib):
     _lib.pa_slot_mapping.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
     _lib.pa_write_kv.restype = _i
     _lib.pa_write_kv.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
+    _lib.pa_append_kv.restype = _i
+    _lib.pa_append_kv.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i,
+                                  _p]
     _lib.pa_copy_blocks.restype = _i
     _lib.pa_copy_blocks.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _p]
     _lib.pa_swap_blocks.restype = _i
@@ -241,6 +244,34 @@ def pa_write_kv(key, value, k_pool, v_pool, slot_mapping, stream=None):
         _arg(key, "key", _F16), _arg(value, "value", _F16), _arg(k_pool, "k_pool", _F16),
         _arg(v_pool, "v_pool", _F16), _arg(slot_mapping, "slot_mapping", _I64),
         T, Hkv, D, B, NB, _stream(stream)))
+
+
+def pa_append_kv(key, value, k_pool, v_pool, block_tables, context_lens=None, seq_ids=None,
+                 positions=None, slot_mapping=None, stream=None):
+    """pa_slot_mapping and pa_write_kv in one launch: each new token's key/value
+    [T, Hkv, D] goes into its slot found through block_tables; the slots are
+    also written to slot_mapping when it is given (int64 [T])."""
+    _dims(key, 3, "key", "pa_append_kv")
+    _dims(block_tables, 2, "block_tables", "pa_append_kv")
+    T, Hkv, D = key.shape
+    S, MB = block_tables.shape
+    _dims(k_pool, 4, "k_pool", "pa_append_kv")
+    NB, _, B, _ = k_pool.shape
+    _same_shape(key, value, "key/value")
+    _same_shape(k_pool, v_pool, "k_pool/v_pool")
+    if tuple(k_pool.shape[1:2]) != (Hkv,) or k_pool.shape[3] != D:
+        raise ValueError(f"pa_append_kv: key {tuple(key.shape)} does not fit pool blocks {tuple(k_pool.shape)}")
+    _rows(seq_ids, "seq_ids", T, "pa_append_kv")
+    _rows(positions, "positions", T, "pa_append_kv")
+    _rows(context_lens, "context_lens", S, "pa_append_kv")
+    _rows(slot_mapping, "slot_mapping", T, "pa_append_kv")
+    _check("pa_append_kv", _lib.pa_append_kv(
+        _arg(slot_mapping, "slot_mapping", _I64), _arg(key, "key", _F16),
+        _arg(value, "value", _F16), _arg(k_pool, "k_pool", _F16), _arg(v_pool, "v_pool", _F16),
+        _arg(block_tables, "block_tables", _I32), _arg(seq_ids, "seq_ids", _I32),
+        _arg(positions, "positions", _I32), _arg(context_lens, "context_lens", _I32),
+        T, S, MB, Hkv, D, B, NB, _stream(stream)))
+    return slot_mapping
 
 
 def pa_copy_blocks(k_pool, v_pool, block_mapping, stream=None):

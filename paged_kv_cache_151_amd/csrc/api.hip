@@ -271,6 +271,38 @@ pa_status pa_write_kv(const void* key, const void* value, void* k_pool, void* v_
                     "pa_write_kv launch");
 }
 
+pa_status pa_append_kv(int64_t* slot_mapping, const void* key, const void* value, void* k_pool,
+                       void* v_pool, const int32_t* block_tables, const int32_t* seq_ids,
+                       const int32_t* positions, const int32_t* context_lens, int T, int S,
+                       int MB, int Hkv, int D, int B, int NB, hipStream_t stream) {
+  if (T < 0 || S < 0) return fail(PA_ERR_SHAPE, "pa_append_kv: T=%d S=%d must be >= 0", T, S);
+  if (Hkv <= 0 || D <= 0 || B <= 0 || NB <= 0 || MB <= 0)
+    return fail(PA_ERR_SHAPE, "pa_append_kv: Hkv=%d D=%d B=%d NB=%d MB=%d must be > 0", Hkv, D, B,
+                NB, MB);
+  if (D % 8) return fail(PA_ERR_UNSUPPORTED, "pa_append_kv: D=%d must be a multiple of 8", D);
+  if (!seq_ids && T > S)
+    return fail(PA_ERR_SHAPE, "pa_append_kv: T=%d > S=%d needs seq_ids", T, S);
+  if ((int64_t)NB * B > ((int64_t)1 << 62))
+    return fail(PA_ERR_SHAPE, "pa_append_kv: pool too large");
+  if (T > 0 && (int64_t)Hkv * (D / 8) > (kMaxWorkItems - 255) / T)
+    return fail(PA_ERR_SHAPE, "pa_append_kv: T=%d tokens of Hkv=%d x D=%d exceed one launch", T,
+                Hkv, D);
+  if (T == 0) return ok();
+  if (!key || !value || !k_pool || !v_pool || !block_tables)
+    return fail(PA_ERR_NULL, "pa_append_kv: null pointer argument");
+  if (!positions && !context_lens)
+    return fail(PA_ERR_NULL, "pa_append_kv: need positions or context_lens");
+  if (!aligned(key, 16) || !aligned(value, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16))
+    return fail(PA_ERR_ALIGN, "pa_append_kv: key/value/pools must be 16-byte aligned");
+  if (!aligned(slot_mapping, 8) || !aligned(block_tables, 4) || !aligned(seq_ids, 4) ||
+      !aligned(positions, 4) || !aligned(context_lens, 4))
+    return fail(PA_ERR_ALIGN, "pa_append_kv: misaligned index buffer");
+  return hip_status(pa::launch_append_kv(slot_mapping, key, value, k_pool, v_pool, block_tables,
+                                         seq_ids, positions, context_lens, T, S, MB, Hkv, D, B,
+                                         NB, stream),
+                    "pa_append_kv launch");
+}
+
 pa_status pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_mapping, int n,
                          int Hkv, int D, int B, int NB, hipStream_t stream) {
   if (n < 0) return fail(PA_ERR_SHAPE, "pa_copy_blocks: n=%d must be >= 0", n);

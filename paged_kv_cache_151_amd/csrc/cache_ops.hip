@@ -9,14 +9,15 @@
 namespace pa {
 namespace {
 
-// slot of token (s, t): table entry of logical block t / B, times B, plus t % B.
-// -1 when the token cannot be placed (bad sequence, position or table entry).
-__global__ __launch_bounds__(256) void slot_mapping_kernel(
-    int64_t* __restrict__ slots, const int32_t* __restrict__ tables,
-    const int32_t* __restrict__ seq_ids, const int32_t* __restrict__ positions,
-    const int32_t* __restrict__ lens, int T, int S, int MB, int B, int NB) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= T) return;
+// slot of token i of sequence s = seq_ids[i] (or i) at position t =
+// positions[i] (or lens[s] - 1): table entry of logical block t / B, times B,
+// plus t % B. -1 when the token cannot be placed (bad sequence, position or
+// table entry).
+__device__ __forceinline__ int64_t token_slot(int i, const int32_t* __restrict__ tables,
+                                              const int32_t* __restrict__ seq_ids,
+                                              const int32_t* __restrict__ positions,
+                                              const int32_t* __restrict__ lens, int S, int MB,
+                                              int B, int NB) {
   const int s = seq_ids ? seq_ids[i] : i;
   int64_t slot = -1;
   if (s >= 0 && s < S) {
@@ -30,7 +31,42 @@ __global__ __launch_bounds__(256) void slot_mapping_kernel(
       }
     }
   }
-  slots[i] = slot;
+  return slot;
+}
+
+__global__ __launch_bounds__(256) void slot_mapping_kernel(
+    int64_t* __restrict__ slots, const int32_t* __restrict__ tables,
+    const int32_t* __restrict__ seq_ids, const int32_t* __restrict__ positions,
+    const int32_t* __restrict__ lens, int T, int S, int MB, int B, int NB) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= T) return;
+  slots[i] = token_slot(i, tables, seq_ids, positions, lens, S, MB, B, NB);
+}
+
+// The slot mapping and the store in one pass: each thread of the store finds
+// its token's slot itself (the token's threads read the same few index words,
+// which the caches serve), and the first thread of each token records it.
+__global__ __launch_bounds__(256) void append_kv_kernel(
+    int64_t* __restrict__ slots_out, const uint4* __restrict__ key,
+    const uint4* __restrict__ value, uint4* __restrict__ k_pool, uint4* __restrict__ v_pool,
+    const int32_t* __restrict__ tables, const int32_t* __restrict__ seq_ids,
+    const int32_t* __restrict__ positions, const int32_t* __restrict__ lens, int64_t total,
+    int Hkv, int chunks, int S, int MB, int B, int NB) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= total) return;
+  const int c = (int)(e % chunks);
+  const int64_t ih = e / chunks;           // token * Hkv + head
+  const int h = (int)(ih % Hkv);
+  const int i = (int)(ih / Hkv);
+  const int64_t slot = token_slot(i, tables, seq_ids, positions, lens, S, MB, B, NB);
+  if (slots_out && h == 0 && c == 0) slots_out[i] = slot;
+  if (slot < 0) return;
+  const int64_t blk = slot / B;
+  const int off = (int)(slot - blk * B);
+  const int64_t dst = ((blk * Hkv + h) * B + off) * chunks + c;
+  if (!PA_IN_BOUNDS(kBsPool, dst >= 0 && dst < (int64_t)NB * B * Hkv * chunks)) return;
+  k_pool[dst] = key[e];
+  v_pool[dst] = value[e];
 }
 
 // One thread moves one 16-byte chunk (8 fp16) of one token's row for one head,
@@ -97,6 +133,21 @@ hipError_t launch_slot_mapping(int64_t* slots, const int32_t* tables, const int3
   const int grid = (T + threads - 1) / threads;
   slot_mapping_kernel<<<grid, threads, 0, stream>>>(slots, tables, seq_ids, positions, lens, T,
                                                     S, MB, B, NB);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_kv(int64_t* slots, const void* key, const void* value, void* k_pool,
+                            void* v_pool, const int32_t* tables, const int32_t* seq_ids,
+                            const int32_t* positions, const int32_t* lens, int T, int S, int MB,
+                            int Hkv, int D, int B, int NB, hipStream_t stream) {
+  const int chunks = D / 8;
+  const int64_t total = (int64_t)T * Hkv * chunks;
+  const int threads = 256;
+  const int64_t grid = (total + threads - 1) / threads;
+  append_kv_kernel<<<(unsigned)grid, threads, 0, stream>>>(
+      slots, static_cast<const uint4*>(key), static_cast<const uint4*>(value),
+      static_cast<uint4*>(k_pool), static_cast<uint4*>(v_pool), tables, seq_ids, positions, lens,
+      total, Hkv, chunks, S, MB, B, NB);
   return hipGetLastError();
 }
 

@@ -102,6 +102,12 @@ hipError_t launch_slot_mapping(int64_t* slots, const int32_t* tables, const int3
                                const int32_t* positions, const int32_t* lens, int T, int S,
                                int MB, int B, int NB, hipStream_t stream);
 
+// The slot mapping and the K/V store in one launch (slots may be nullptr).
+hipError_t launch_append_kv(int64_t* slots, const void* key, const void* value, void* k_pool,
+                            void* v_pool, const int32_t* tables, const int32_t* seq_ids,
+                            const int32_t* positions, const int32_t* lens, int T, int S, int MB,
+                            int Hkv, int D, int B, int NB, hipStream_t stream);
+
 hipError_t launch_write_kv(const void* key, const void* value, void* k_pool, void* v_pool,
                            const int64_t* slots, int T, int Hkv, int D, int B, int NB,
                            hipStream_t stream);

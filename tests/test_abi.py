@@ -190,6 +190,27 @@ def test_default_partition_keeps_a_workgroup_per_compute_unit(lib):
         assert P == 1024 or wgs(2 * P) < 256
 
 
+def test_append_kv_validation(lib):
+    v = ctypes.c_void_p
+    f = lib.pa_append_kv
+    f.argtypes = [v, v, v, v, v, v, v, v, v] + [ctypes.c_int] * 7 + [v]
+
+    def call(slots=None, key=FAKE, val=FAKE, kp=FAKE, vp=FAKE, tables=FAKE, seq=None, pos=None,
+             lens=FAKE, T=2, S=2, MB=3, Hkv=2, D=128, B=16, NB=8):
+        return f(slots, key, val, kp, vp, tables, seq, pos, lens, T, S, MB, Hkv, D, B, NB, None)
+
+    assert call(T=0) == PA_OK                        # nothing to do
+    assert call(T=-1) == PA_ERR_SHAPE
+    assert call(MB=0) == PA_ERR_SHAPE
+    assert call(D=12) == PA_ERR_UNSUPPORTED
+    assert call(T=3, S=2) == PA_ERR_SHAPE            # more tokens than sequences needs seq_ids
+    assert call(key=None) == PA_ERR_NULL
+    assert call(tables=None) == PA_ERR_NULL
+    assert call(lens=None) == PA_ERR_NULL            # neither positions nor lengths
+    assert call(kp=FAKE + 8) == PA_ERR_ALIGN
+    assert call(slots=FAKE + 4) == PA_ERR_ALIGN
+
+
 def test_write_copy_slot_validation(lib):
     v = ctypes.c_void_p
     assert lib.pa_write_kv(v(FAKE), v(FAKE), v(FAKE), v(FAKE), None, 4, 2, 128, 16, 8, None) == PA_ERR_NULL

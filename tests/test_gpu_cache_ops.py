@@ -270,3 +270,53 @@ def test_swap_refuses_pageable_host_memory(pa):
     say("swap with pageable memory is refused before any launch")
     with pytest.raises(pa.PaError, match="PA_ERR_UNSUPPORTED"):
         pa.pa_swap_blocks(pageable, pageable, pool, pool, pairs)
+
+
+def test_append_kv_decode_form_equals_slot_mapping_then_write(pa):
+    # one launch against the two calls it replaces and against the oracle:
+    # slots and whole pools bit for bit
+    c = W.seven_b_single_layer()
+    say("append_kv decode form, 7b_single_layer")
+    tables, lens = dev(c.block_tables), dev(c.context_lens)
+    k_new, v_new = dev(c.key_new), dev(c.value_new)
+    kp1, vp1 = dev(c.k_pool), dev(c.v_pool)
+    slots1 = pa.pa_slot_mapping(tables, c.B, c.NB, context_lens=lens)
+    pa.pa_write_kv(k_new, v_new, kp1, vp1, slots1)
+    kp2, vp2 = dev(c.k_pool), dev(c.v_pool)
+    import torch
+    slots2 = torch.full((c.S,), 77, dtype=torch.int64, device="cuda")
+    pa.pa_append_kv(k_new, v_new, kp2, vp2, tables, context_lens=lens, slot_mapping=slots2)
+    assert np.array_equal(host(slots1), host(slots2))
+    assert np.array_equal(u16(host(kp1)), u16(host(kp2))) and np.array_equal(u16(host(vp1)), u16(host(vp2)))
+    ref_slots = oracle.decode_slots(c.block_tables, c.context_lens, c.B, c.NB)
+    rk, rv = oracle.write_kv(c.k_pool, c.v_pool, c.key_new, c.value_new, ref_slots)
+    assert np.array_equal(host(slots2), ref_slots)
+    assert np.array_equal(u16(host(kp2)), u16(rk)) and np.array_equal(u16(host(vp2)), u16(rv))
+
+
+def test_append_kv_token_form_with_unplaceable_tokens(pa):
+    # seq_ids + positions (prefill and extension); tokens whose sequence,
+    # position or table entry is out of range get slot -1 and are skipped
+    tables = np.array([[3, 1, -1], [0, 2, 5], [7, -1, -1], [1, 9, 2]], dtype=np.int32)
+    NB, B, Hkv, D = 8, 4, 2, 16
+    seq = np.array([0, 1, 1, 3, 4, -1, 2, 1], dtype=np.int32)
+    pos = np.array([7, 11, 12, 5, 0, 0, 0, 3], dtype=np.int32)
+    rng = np.random.default_rng(91)
+    kp = W.f16_normal(rng, (NB, Hkv, B, D))
+    vp = W.f16_normal(rng, (NB, Hkv, B, D))
+    key = W.f16_normal(rng, (len(seq), Hkv, D))
+    val = W.f16_normal(rng, (len(seq), Hkv, D))
+    say("append_kv token form")
+    import torch
+    gk, gv = dev(kp), dev(vp)
+    slots = torch.empty(len(seq), dtype=torch.int64, device="cuda")
+    pa.pa_append_kv(dev(key), dev(val), gk, gv, dev(tables), seq_ids=dev(seq), positions=dev(pos),
+                    slot_mapping=slots)
+    ref_slots = oracle.token_slots(tables, seq, pos, B, NB)
+    assert np.array_equal(host(slots), ref_slots)
+    rk, rv = oracle.write_kv(kp, vp, key, val, ref_slots)
+    assert np.array_equal(u16(host(gk)), u16(rk)) and np.array_equal(u16(host(gv)), u16(rv))
+    # without a slot output the pools end the same
+    gk2, gv2 = dev(kp), dev(vp)
+    pa.pa_append_kv(dev(key), dev(val), gk2, gv2, dev(tables), seq_ids=dev(seq), positions=dev(pos))
+    assert np.array_equal(u16(host(gk2)), u16(rk)) and np.array_equal(u16(host(gv2)), u16(rv))

@@ -164,6 +164,10 @@ def test_cache_call_breaches_stay_inside_the_buffers(pa):
     pa.pa_copy_blocks(kp, vp, dev(pairs))
     tables = c.block_tables.copy()
     tables[0, 2] = c.NB + 9
+    tables[1, 1] = -4
     pa.pa_slot_mapping(dev(tables), c.B, c.NB, context_lens=dev(c.context_lens))
+    # the last token of each sequence lands in those entries: both skipped
+    pa.pa_append_kv(dev(c.key_new), dev(c.value_new), kp, vp, dev(tables),
+                    context_lens=dev(c.context_lens))
     assert np.array_equal(u16(host(kp)), u16(c.k_pool))   # nothing was written
     no_violations(pa, c.name)

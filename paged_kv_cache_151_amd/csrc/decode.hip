@@ -498,7 +498,13 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(const DecodeArgs a, i
   for (int p = 0; p < np; ++p) {
     const float mp = a.part_ml[(row0 + p) * 2];
     const float lp = a.part_ml[(row0 + p) * 2 + 1];
-    const float2 v = *reinterpret_cast<const float2*>(a.part_acc + (row0 + p) * D + d);
+    float2 v;
+    if (a.part_half) {   // the piece's normalised result: scale back by its sum
+      const _Float16* hv = reinterpret_cast<const _Float16*>(a.part_acc) + (row0 + p) * D + d;
+      v = float2{(float)hv[0] * lp, (float)hv[1] * lp};
+    } else {
+      v = *reinterpret_cast<const float2*>(a.part_acc + (row0 + p) * D + d);
+    }
     const float mn = __builtin_fmaxf(mx, mp);
     const float fo = __builtin_amdgcn_exp2f(mx - mn);
     const float fp = __builtin_amdgcn_exp2f(mp - mn);

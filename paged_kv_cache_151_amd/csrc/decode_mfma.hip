@@ -31,9 +31,13 @@
 // sequence, KV head) in the same order, the same length clamping and empty
 // sequence, block-table chunks of 64 entries handed out by v_readlane, units
 // dealt round-robin to the waves and fetched one unit ahead with empty-range
-// no-op loads past a wave's last unit, the same cross-wave merge and the same
-// partials for the reduce kernel. V tiles go to a per-wave LDS double buffer
-// by buffer loads that write LDS directly; piece c of V row r sits at
+// no-op loads past a wave's last unit, and the same cross-wave merge. A
+// piece's partial row holds its normalised result in fp16 (the reduce kernel
+// scales it back by the piece's sum): half the bytes of the vector kernel's
+// fp32 sums. Scattered writes amid the read stream cost far more than their
+// share of the bandwidth: with eight heads per piece, fp32 rows took about
+// 4 % of a call on the chat lengths. V tiles go to a per-wave LDS double
+// buffer by buffer loads that write LDS directly; piece c of V row r sits at
 // c ^ 2 (r % 8), which keeps the transposing reads free of bank conflicts.
 #include <atomic>
 
@@ -393,7 +397,7 @@ __device__ __forceinline__ void attend_piece(const DecodeArgs& a, int s, int g, 
     } else {
       const int64_t row = ((int64_t)s * a.Hq + hq) * a.Pmax + p;
       if (PA_IN_BOUNDS(kBsPartial, p >= 0 && p < a.Pmax && row < (int64_t)a.S * a.Hq * a.Pmax)) {
-        a.part_acc[row * D + d] = num;
+        reinterpret_cast<_Float16*>(a.part_acc)[row * D + d] = (_Float16)(den > 0.f ? num / den : 0.f);
         if (d == 0) {
           a.part_ml[row * 2] = mx;
           a.part_ml[row * 2 + 1] = den;

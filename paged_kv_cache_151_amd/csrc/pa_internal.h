@@ -68,9 +68,12 @@ constexpr int kEvenSplitMaxSeqs = 1024;
 #ifndef PA_EVEN_SPLIT_MIN_PARTS
 #define PA_EVEN_SPLIT_MIN_PARTS 2
 #endif
+// Groups of 4 and 8 query heads run on the matrix-core kernel.
+inline bool decode_on_matrix_cores(int G) { return G == 4 || G == 8; }
+
 inline bool decode_even_split(int S, int Hq, int Hkv, int P, int64_t partitions) {
   const int G = Hkv > 0 ? Hq / Hkv : 0;
-  if ((G != 4 && G != 8) || partitions < PA_EVEN_SPLIT_MIN_PARTS || partitions < 2 ||
+  if (!decode_on_matrix_cores(G) || partitions < PA_EVEN_SPLIT_MIN_PARTS || partitions < 2 ||
       S > kEvenSplitMaxSeqs)
     return false;
   const int64_t units = (int64_t)S * Hkv * partitions * (P / kDecodeUnit);
@@ -86,7 +89,8 @@ struct DecodeArgs {
   const _Float16* v_pool;            // [NB][Hkv][B][D]
   const int32_t* tables;             // [S][MB]
   const int32_t* lens;               // [S]
-  float* part_acc;                   // [S][Hq][Pmax][D]   (unused when Pmax == 1)
+  float* part_acc;                   // [S][Hq][Pmax][D]   (unused when Pmax == 1); with
+                                     // part_half the first half of it holds fp16 rows
   float* part_ml;                    // [S][Hq][Pmax][2]   (running max, sum; log2 domain)
   int32_t* part_np;                  // [S][Hkv] pieces per sequence and KV head when the work
                                      // is split evenly (nullptr: one per partition)
@@ -96,6 +100,10 @@ struct DecodeArgs {
   int Pmax;                          // partial rows per (sequence, query head); lengths are
                                      // clamped to Pmax * P, or (Pmax - 1) * P when split evenly
   float scale_log2;                  // softmax scale times log2(e)
+  int part_half;                     // 1: a piece's row is its normalised result (sum of
+                                     // weights times values over the sum of weights) in
+                                     // fp16, at _Float16 index row * D of part_acc;
+                                     // 0: the unnormalised fp32 sum at float index row * D
 };
 
 hipError_t launch_slot_mapping(int64_t* slots, const int32_t* tables, const int32_t* seq_ids,

@@ -19,9 +19,8 @@
 // workgroup loads each chunk once, two chunks ahead of the one being computed,
 // with buffer loads that write straight into LDS (no staging registers, no
 // separate store step), into one of three LDS stages; the waves read their
-// matrix operands from there. Defaults (QT = 1 for groups of one or two
-// query heads and 2 for four or eight, NW = 4, KC = 32, three LDS stages) are
-// set in prefill_internal.h.
+// matrix operands from there. Defaults (QT = 2, NW = 4, KC = 32, three LDS
+// stages) are set in prefill_internal.h.
 //
 // Instruction budget. A wave issues at most one instruction per turn on its
 // SIMD, so every scalar or vector instruction around the 16 matrix products of

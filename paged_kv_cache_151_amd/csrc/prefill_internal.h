@@ -10,9 +10,10 @@ namespace pa {
 // tile fits in about 150 VGPRs (three waves per SIMD), two in about 235 (two
 // waves per SIMD). Measured on MI355X: for groups of 4 query heads (the
 // shared-prefix suffixes) two tiles are 5 % faster (289 against 304 us); for
-// one head per group (the 16-prompt chat batch) they tie (292 against 293).
+// one head per group (the 16-prompt chat batch) they tied in one session (292
+// against 293) and were 2-3 % faster in two others (297-300 against 307-309).
 #ifndef PA_PREFILL_ROW_TILES
-#define PA_PREFILL_ROW_TILES 1
+#define PA_PREFILL_ROW_TILES 2
 #endif
 #ifndef PA_PREFILL_ROW_TILES_GROUPED
 #define PA_PREFILL_ROW_TILES_GROUPED 2

@@ -233,7 +233,7 @@ int pa_decode_partition_size(int S, int Hq, int Hkv, int B, int max_context_len,
 /*
  * pa_decode_workspace_bytes — device workspace pa_decode needs: partial
  * results of every context partition, S * Hq * n * (D + 2) * 4 bytes with
- * n = ceil(max_context_len / P) partitions (groups of four and eight use the
+ * n = ceil(max_context_len / P) partitions (the pieces' fp16 rows use the
  * first half of each row's D * 4 bytes), or 0 when one partition covers
  * every sequence. When the call splits its work evenly (below: Hq / Hkv of 4
  * or 8, n > 1, S <= 1024, and S * Hkv * n * (P / 16 + 1) + 8 + 9 * P / 16
@@ -258,11 +258,12 @@ size_t pa_decode_workspace_bytes(int S, int Hq, int Hkv, int D, int B, int max_c
  * one or two query heads per KV head the weighted sum of values is fp32 as
  * well; for groups of four and eight (the matrix-core path) each softmax
  * weight, at most 2^8 before normalisation, is rounded to fp16 for the
- * product with V (fp32 accumulation), and when a sequence's walk is cut into
- * several pieces each piece's normalised result is rounded to fp16 before the
- * pieces are merged in fp32 (one more fp16 rounding of a convex combination's
- * terms: at most 2^-11 of the largest |value| in the sequence). L_s = 0 gives
- * zeros. Any finite scale, of either sign, is supported.
+ * product with V (fp32 accumulation). On every path, when a sequence's walk
+ * is cut into several pieces each piece's normalised result is rounded to
+ * fp16 before the pieces are merged in fp32 (one more fp16 rounding of a
+ * convex combination's terms: at most 2^-11 of the largest |value| in the
+ * sequence). L_s = 0 gives zeros. Any finite scale, of either sign, is
+ * supported.
  * Slots past L_s in the last block and blocks the table does not name are
  * never read into the result, whatever they hold (NaN and Inf included).
  * The summation order depends only on the sequences' lengths and logical

@@ -146,7 +146,6 @@ pa_status decode_prepare(const char* fn, void* out, const void* query, const voi
   a.P = P;
   a.Pmax = Pmax;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
-  a.part_half = decode_on_matrix_cores(G) ? 1 : 0;
   call->G = G;
   call->even = even;
   call->partials_bytes = pa_decode_workspace_bytes(S, Hq, Hkv, D, B, max_context_len, P);

@@ -31,12 +31,11 @@
 // sequence, KV head) in the same order, the same length clamping and empty
 // sequence, block-table chunks of 64 entries handed out by v_readlane, units
 // dealt round-robin to the waves and fetched one unit ahead with empty-range
-// no-op loads past a wave's last unit, and the same cross-wave merge. A
-// piece's partial row holds its normalised result in fp16 (the reduce kernel
-// scales it back by the piece's sum): half the bytes of the vector kernel's
-// fp32 sums. Scattered writes amid the read stream cost far more than their
-// share of the bandwidth: with eight heads per piece, fp32 rows took about
-// 4 % of a call on the chat lengths. V tiles go to a per-wave LDS double
+// no-op loads past a wave's last unit, the same cross-wave merge, and the
+// same partial rows: a piece's normalised result in fp16 (the reduce kernel
+// scales it back by the piece's sum). Scattered writes amid the read stream
+// cost far more than their share of the bandwidth: with eight heads per
+// piece, fp32 rows took about 4 % of a call on the chat lengths. V tiles go to a per-wave LDS double
 // buffer by buffer loads that write LDS directly; piece c of V row r sits at
 // c ^ 2 (r % 8), which keeps the transposing reads free of bank conflicts.
 #include <atomic>

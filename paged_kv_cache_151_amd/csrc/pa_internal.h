@@ -89,8 +89,10 @@ struct DecodeArgs {
   const _Float16* v_pool;            // [NB][Hkv][B][D]
   const int32_t* tables;             // [S][MB]
   const int32_t* lens;               // [S]
-  float* part_acc;                   // [S][Hq][Pmax][D]   (unused when Pmax == 1); with
-                                     // part_half the first half of it holds fp16 rows
+  float* part_acc;                   // [S][Hq][Pmax][D] fp16 rows in the first half of
+                                     // this area (unused when Pmax == 1): a piece's
+                                     // normalised result (weighted sum of values over
+                                     // the sum of weights), row r at _Float16 index r * D
   float* part_ml;                    // [S][Hq][Pmax][2]   (running max, sum; log2 domain)
   int32_t* part_np;                  // [S][Hkv] pieces per sequence and KV head when the work
                                      // is split evenly (nullptr: one per partition)
@@ -100,10 +102,6 @@ struct DecodeArgs {
   int Pmax;                          // partial rows per (sequence, query head); lengths are
                                      // clamped to Pmax * P, or (Pmax - 1) * P when split evenly
   float scale_log2;                  // softmax scale times log2(e)
-  int part_half;                     // 1: a piece's row is its normalised result (sum of
-                                     // weights times values over the sum of weights) in
-                                     // fp16, at _Float16 index row * D of part_acc;
-                                     // 0: the unnormalised fp32 sum at float index row * D
 };
 
 hipError_t launch_slot_mapping(int64_t* slots, const int32_t* tables, const int32_t* seq_ids,

@@ -744,12 +744,15 @@ def other_bytes(c, P):
     nparts = -(-L // P)
     G = c.Hq // c.Hkv
     parts = int(-(-int(L.max()) // P))
-    if G in (4, 8) and parts > 1 and c.S <= 1024:
+    even = parts > 1 and c.S <= 1024 and (G >= 4 or c.S * c.Hkv * parts > 2048)
+    if even:
         # even split: runs of q units over the (KV head, sequence, unit)
-        # order, one per resident workgroup (4 per compute unit here)
+        # order, one per resident workgroup (4 per compute unit for groups of
+        # 4 and 8, 8 for the vector kernel)
         n = -(-L // 16)
         N = int(n.sum())
-        grid = min(1024, -(-c.S * c.Hkv * parts // 8) * 8)
+        resident = 1024 if G >= 4 else 2048
+        grid = min(resident, -(-c.S * c.Hkv * parts // 8) * 8)
         q = max(-(-N * c.Hkv // grid), P // 16)
         first = (np.arange(c.Hkv)[:, None] * N + (np.cumsum(n) - n)[None, :])
         pieces = (first + n[None, :] - 1) // q - first // q + 1
@@ -761,7 +764,8 @@ def other_bytes(c, P):
         "kv_unread_tail_of_last_blocks": int((blocks * c.B - L).sum() * row),
         "query_and_output": int(2 * c.S * c.Hq * c.D * 2),
         "tables_and_lengths": int(blocks.sum() * 4 + c.S * 4),
-        "workspace_partials_written_and_read": int(2 * partial_rows * (c.D + 2) * 4),
+        # a piece's row: its normalised result in fp16 and its maximum and sum in fp32
+        "workspace_partials_written_and_read": int(2 * partial_rows * (c.D * 2 + 8)),
     }
 
 

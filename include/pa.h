@@ -235,9 +235,10 @@ int pa_decode_partition_size(int S, int Hq, int Hkv, int B, int max_context_len,
  * results of every context partition, S * Hq * n * (D + 2) * 4 bytes with
  * n = ceil(max_context_len / P) partitions (the pieces' fp16 rows use the
  * first half of each row's D * 4 bytes), or 0 when one partition covers
- * every sequence. When the call splits its work evenly (below: Hq / Hkv of 4
- * or 8, n > 1, S <= 1024, and S * Hkv * n * (P / 16 + 1) + 8 + 9 * P / 16
- * below 2^31) a sequence has up to n + 1 pieces and the workspace also holds
+ * every sequence. When the call splits its work evenly (below: n > 1,
+ * S <= 1024, S * Hkv * n * (P / 16 + 1) + 8 + 9 * P / 16 below 2^31, and for
+ * one or two query heads per KV head S * Hkv * n > 2048) a sequence has up
+ * to n + 1 pieces and the workspace also holds
  * a piece count per (sequence, KV head): S * Hq * (n + 1) * (D + 2) * 4
  * + S * Hkv * 4 bytes. Returns 0 for invalid arguments, and when the size
  * does not fit in size_t, as well; pa_decode then reports the error.
@@ -269,14 +270,16 @@ size_t pa_decode_workspace_bytes(int S, int Hq, int Hkv, int D, int B, int max_c
  * The summation order depends only on the sequences' lengths and logical
  * token positions, so relabelling physical blocks or sharing them between
  * sequences leaves every output bit unchanged.
- * Work split: with one or two query heads per KV head, and for groups of four
- * and eight when every sequence fits one partition, each workgroup serves one
- * partition of one (sequence, KV head). Groups of four and eight over several
- * partitions (and at most 1024 sequences) instead cut the batch's 16-token
- * units, taken in (KV head, sequence, position) order, into equal runs, one
- * per workgroup the GPU holds at once, and merge each sequence's pieces in the
- * reduce kernel: every workgroup then starts at the launch and none is left
- * running alone at its end.
+ * Work split: when every sequence fits one partition, for more than 1024
+ * sequences, and for one or two query heads per KV head when the partitions
+ * number at most 2048 (one round of that kernel's resident workgroups, so all
+ * start at the launch anyway), each workgroup serves one partition of one
+ * (sequence, KV head). Otherwise the batch's 16-token units, taken in (KV
+ * head, sequence, position) order, are cut into equal runs, one per workgroup
+ * the GPU holds at once, and each sequence's pieces are merged in the reduce
+ * kernel: every workgroup then starts at the launch and none is left running
+ * alone at its end. Groups of one and two query heads per KV head run on the vector
+ * kernel, groups of four and eight on the matrix cores, either way.
  *
  *   out               device fp16 [S][Hq][D], 16-byte aligned, written
  *   query             device fp16 [S][Hq][D], 16-byte aligned

@@ -34,6 +34,7 @@
 // that block takes a masked path that selects (never multiplies) so NaN or
 // Inf in unused slots cannot reach the result. Arithmetic order depends only
 // on logical positions, so physical ids never change an output bit.
+#include "decode_even.h"
 #include "pa_debug.h"
 #include "pa_internal.h"
 
@@ -211,6 +212,10 @@ __device__ __forceinline__ void merge_state(float& m, float& l, float* acc, floa
   for (int d = 0; d < 8; ++d) acc[d] = acc[d] * a + acco[d] * b;
 }
 
+// Tokens [tok0, tok0 + len) of sequence s (clamped length L) and KV head g
+// (len > 0): piece p of the nparts pieces the sequence's walk is cut into.
+// With one piece the result is the output; otherwise the piece's maximum and
+// sum (fp32) and its normalised result (fp16) go to partial row p.
 // G query heads share KV head g. The workgroup's waves are split into NH =
 // G / HPW head groups (wave w serves heads HPW * (w % NH) ... of the group)
 // and NU = NW / NH unit subsets (wave w walks units w / NH, + NU, ...), so a
@@ -218,9 +223,15 @@ __device__ __forceinline__ void merge_state(float& m, float& l, float* acc, floa
 // K/V tile is loaded by NH waves of the same workgroup: the repeats are
 // served by the caches, HBM traffic is unchanged.
 template <int BT, int G, int HPW, int NW, int DEPTH, bool NT>
-__global__ __launch_bounds__(NW * 64)
-__attribute__((amdgpu_waves_per_eu(PA_DECODE_MIN_WAVES_PER_EU)))
-void decode_partition_kernel(const DecodeArgs a) {
+__device__ __forceinline__ void vec_piece(const DecodeArgs& a, int s, int g, int L, int tok0,
+                                          int len, int nparts, int p) {
+  s = __builtin_amdgcn_readfirstlane(s);
+  g = __builtin_amdgcn_readfirstlane(g);
+  L = __builtin_amdgcn_readfirstlane(L);
+  tok0 = __builtin_amdgcn_readfirstlane(tok0);
+  len = __builtin_amdgcn_readfirstlane(len);
+  nparts = __builtin_amdgcn_readfirstlane(nparts);
+  p = __builtin_amdgcn_readfirstlane(p);
   constexpr int D = kHeadDim;
   constexpr int NH = G / HPW;           // head groups
   constexpr int NU = NW / NH;           // unit subsets
@@ -239,41 +250,15 @@ void decode_partition_kernel(const DecodeArgs a) {
   const int c = lane & 15;
   const int hgrp = wave % NH;
   const int usub = wave / NH;
-
-  // blockIdx -> (p, s, g) with g fastest: consecutive workgroups go to
-  // consecutive XCDs, so every workgroup of one KV head lands on the same XCD
-  // when Hkv is a multiple of 8 (shared prefix blocks stay in one L2).
-  int id = blockIdx.x;
-  const int g = id % a.Hkv;
-  id /= a.Hkv;
-  const int s = id % a.S;
-  const int p = id / a.S;
-
-  int L = PA_IN_BOUNDS(kBsLength, s < a.S) ? a.lens[s] : 0;
-  L = L < 0 ? 0 : L;
-  L = L > a.MB * B ? a.MB * B : L;
-  L = L > a.Pmax * a.P ? a.Pmax * a.P : L;
-  const int tok0 = p * a.P;
   const int hq0 = g * G;
   const int64_t n_out = (int64_t)a.S * a.Hq * D;   // elements of out and of the query
   (void)n_out;
-  if (tok0 >= L) {
-    if (p == 0) {  // empty sequence: zero output
-      for (int e = threadIdx.x; e < G * D; e += NW * 64) {
-        const int64_t o = ((int64_t)s * a.Hq + hq0 + e / D) * D + (e % D);
-        if (PA_IN_BOUNDS(kBsOut, o >= 0 && o < n_out)) a.out[o] = (_Float16)0.f;
-      }
-    }
-    return;
-  }
-  const int nparts = (L + a.P - 1) / a.P;
-  const int len = (tok0 + a.P < L ? tok0 + a.P : L) - tok0;
   const int nunits = (len + kUnit - 1) / kUnit;
   const int n_full = len / kUnit;        // units with every slot valid
-  // P is a multiple of 16, not necessarily of B: the partition may start
+  // tok0 is a multiple of 16, not necessarily of B: the piece may start
   // inside a block. U0 is its first unit counted from the sequence start.
   const int U0 = tok0 / kUnit;
-  // blocks holding the partition's tokens (B = 8: two per unit, the last
+  // blocks holding the piece's tokens (B = 8: two per unit, the last
   // possibly absent when the final unit ends within its first half)
   const int blk0 = kSplit ? 2 * U0 : U0 / UPB;
   const int nblk = kSplit ? (len + 7) / 8 : (U0 + nunits - 1) / UPB - blk0 + 1;
@@ -476,6 +461,65 @@ void decode_partition_kernel(const DecodeArgs a) {
   }
 }
 
+// One workgroup per (partition, sequence, KV head), partitions of a.P tokens.
+// blockIdx -> (p, s, g) with g fastest: consecutive workgroups go to
+// consecutive XCDs, so every workgroup of one KV head lands on the same XCD
+// when Hkv is a multiple of 8 (shared prefix blocks stay in one L2).
+template <int BT, int G, int HPW, int NW, int DEPTH, bool NT>
+__global__ __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu(PA_DECODE_MIN_WAVES_PER_EU)))
+void decode_partition_kernel(const DecodeArgs a) {
+  constexpr int D = kHeadDim;
+  const int B = BT > 0 ? BT : a.B;
+  int id = blockIdx.x;
+  const int g = id % a.Hkv;
+  id /= a.Hkv;
+  const int s = id % a.S;
+  const int p = id / a.S;
+  int L = PA_IN_BOUNDS(kBsLength, s < a.S) ? a.lens[s] : 0;
+  L = L < 0 ? 0 : L;
+  L = L > a.MB * B ? a.MB * B : L;
+  L = L > a.Pmax * a.P ? a.Pmax * a.P : L;
+  const int tok0 = p * a.P;
+  const int hq0 = g * G;
+  const int64_t n_out = (int64_t)a.S * a.Hq * D;
+  (void)n_out;
+  if (tok0 >= L) {
+    if (p == 0) {  // empty sequence: zero output
+      for (int e = threadIdx.x; e < G * D; e += NW * 64) {
+        const int64_t o = ((int64_t)s * a.Hq + hq0 + e / D) * D + (e % D);
+        if (PA_IN_BOUNDS(kBsOut, o >= 0 && o < n_out)) a.out[o] = (_Float16)0.f;
+      }
+    }
+    return;
+  }
+  const int nparts = (L + a.P - 1) / a.P;
+  const int len = (tok0 + a.P < L ? tok0 + a.P : L) - tok0;
+  vec_piece<BT, G, HPW, NW, DEPTH, NT>(a, s, g, L, tok0, len, nparts, p);
+}
+
+// Equal-work split of the whole batch (decode_even.h), one or two query heads
+// per KV head.
+template <int BT, int G, int HPW, int NW, int DEPTH, bool NT>
+__global__ __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu(PA_DECODE_MIN_WAVES_PER_EU)))
+void decode_vec_even_kernel(const DecodeArgs a) {
+  constexpr int D = kHeadDim;
+  even_split_walk<NW * 64>(
+      a, BT > 0 ? BT : a.B,
+      [&](int s, int g, int L, int tok0, int len, int nparts, int p) {
+        vec_piece<BT, G, HPW, NW, DEPTH, NT>(a, s, g, L, tok0, len, nparts, p);
+      },
+      [&](int s) {
+        const int64_t n_out = (int64_t)a.S * a.Hq * D;
+        (void)n_out;
+        for (int e = threadIdx.x; e < a.Hkv * G * D; e += NW * 64) {
+          const int64_t o = (int64_t)s * a.Hq * D + e;
+          if (PA_IN_BOUNDS(kBsOut, o >= 0 && o < n_out)) a.out[o] = (_Float16)0.f;
+        }
+      });
+}
+
 // One wave per (s, hq): out = sum_p 2^(m_p - M) l_p o_p / sum_p 2^(m_p - M) l_p
 // (o_p the piece's normalised result, l_p its sum) over the sequence's pieces (its partitions, or the counts the even split
 // recorded). Sequences of one piece were finished by the partition kernel.
@@ -524,6 +568,13 @@ hipError_t launch_partition(const DecodeArgs& a, hipStream_t stream) {
   constexpr int HPW = G < kDecodeHeadsPerWave ? G : kDecodeHeadsPerWave;
   constexpr int NH = G / HPW;
   constexpr int NW = decode_waves(G) > NH ? decode_waves(G) : NH;
+  if (a.part_np) {
+    auto kernel = decode_vec_even_kernel<BT, G, HPW, NW, kDecodeDepth, kDecodeNontemporal>;
+    const int64_t grid = even_split_grid(a, kernel, NW * 64);
+    if (grid <= 0) return hipErrorInvalidValue;
+    kernel<<<(unsigned)grid, NW * 64, 0, stream>>>(a);
+    return hipGetLastError();
+  }
   const int64_t grid = (int64_t)a.Pmax * a.S * a.Hkv;
   if constexpr (G <= 2) {
     if (grid <= kSmallLaunchWorkgroups) {

@@ -38,8 +38,7 @@
 // piece, fp32 rows took about 4 % of a call on the chat lengths. V tiles go to a per-wave LDS double
 // buffer by buffer loads that write LDS directly; piece c of V row r sits at
 // c ^ 2 (r % 8), which keeps the transposing reads free of bank conflicts.
-#include <atomic>
-
+#include "decode_even.h"
 #include "pa_debug.h"
 #include "pa_internal.h"
 
@@ -443,149 +442,21 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const DecodeArgs a
   attend_piece<BT, G, NW, DEPTH, NT>(a, s, g, tok0, len, nparts, p);
 }
 
-// Equal-work split of the whole batch. The 16-token units of every (KV head,
-// sequence) pair are taken in the order (KV head, sequence, position) and cut
-// into runs of q consecutive units, one run per workgroup; q is the total over
-// the grid, at least a.P / 16. A workgroup walks its run pair by pair, each
-// pair's part being one piece for the reduce kernel. The grid is the number of
-// workgroups the GPU holds at once, so every run starts at the launch and
-// they all end together: no workgroup starts late behind a long one, which
-// costs grouped heads about a tenth of a launch in the per-partition grid.
-// Workgroup b runs on XCD b % 8 and takes run (b % 8) * (grid / 8) + b / 8,
-// so each XCD walks one contiguous eighth of the order: one KV head per XCD
-// when there are 8, as in the per-partition grid's order. Four waves per SIMD
-// are asked for explicitly: left to itself the compiler keeps the walk's
-// state in 151 VGPRs and three waves per SIMD; at 127 it needs no spills.
+// Equal-work split of the whole batch (the walk and its reasons are in
+// decode_even.h). Four waves per SIMD are asked for explicitly: left to itself
+// the compiler keeps the walk's state in 151 VGPRs and three waves per SIMD;
+// at 127 it needs no spills.
 template <int BT, int G, int NW, int DEPTH, bool NT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void decode_mfma_even_kernel(const DecodeArgs a) {
-  constexpr int U = kDecodeUnit;
-  const int B = BT > 0 ? BT : a.B;
-  const int cap = (a.Pmax - 1) * a.P;   // the launch's bound on every length
-  const int lane = threadIdx.x & 63;
-  const int nwg = gridDim.x;            // a multiple of 8
-  const int w = (blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8;
-
-  // empty sequences (workgroup b serves sequences b, b + grid, ...): zero
-  // output and no pieces
-  for (int s = blockIdx.x; s < a.S; s += nwg) {
-    if (clamped_len(a, s, B, cap) == 0) {
-      for (int g = 0; g < a.Hkv; ++g) zero_heads<G, NW>(a, s, g);
-      for (int g = threadIdx.x; g < a.Hkv; g += NW * 64)
-        if (PA_IN_BOUNDS(kBsPartial, s * a.Hkv + g < a.S * a.Hkv)) a.part_np[s * a.Hkv + g] = 0;
-    }
-  }
-
-  // every length once, into registers (lane l holds sequences 64c + l), so
-  // the sum below and the search for the run's first pair need one round
-  // trip to memory between them
-  constexpr int kChunks = kEvenSplitMaxSeqs / 64;
-  int lc[kChunks];
-  int acc = 0;
-#pragma unroll
-  for (int c = 0; c < kChunks; ++c) {
-    lc[c] = 64 * c + lane < a.S ? clamped_len(a, 64 * c + lane, B, cap) : 0;
-    acc += (lc[c] + U - 1) / U;
-  }
-  // N = units of one KV head over the batch; the run length q
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) acc += __shfl_xor(acc, d);
-  const int N = __builtin_amdgcn_readfirstlane(acc);
-  const int total = N * a.Hkv;
-  const int qmin = a.P / U;
-  const int qe = (total + nwg - 1) / nwg;
-  const int q = __builtin_amdgcn_readfirstlane(qe > qmin ? qe : qmin);
-  const int begin = w * q;
-  if (begin >= total) return;
-  const int end = begin + q < total ? begin + q : total;
-
-  // the pair of the run's first unit: KV head g, then the first sequence
-  // whose running unit count passes the offset r inside that head
-  int g = __builtin_amdgcn_readfirstlane(begin / N);
-  const int r = begin - g * N;
-  int s = 0, cs = 0, ns = 0, Ls = 0;
-  bool found = false;
-  int base = 0;
-#pragma unroll
-  for (int c = 0; c < kChunks; ++c) {
-    if (!found && 64 * c < a.S) {
-      const int n = (lc[c] + U - 1) / U;
-      int incl = n;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int t = __shfl_up(incl, d);
-        incl += lane >= d ? t : 0;
-      }
-      const unsigned long long hit = __builtin_amdgcn_ballot_w64(base + incl > r);
-      if (hit) {
-        const int f = __builtin_ctzll(hit);
-        s = 64 * c + f;
-        ns = __builtin_amdgcn_readlane(n, f);
-        Ls = __builtin_amdgcn_readlane(lc[c], f);
-        cs = base + __builtin_amdgcn_readlane(incl, f) - ns;
-        found = true;
-      } else {
-        base += __builtin_amdgcn_readlane(incl, 63);
-      }
-    }
-  }
-  s = __builtin_amdgcn_readfirstlane(s);
-  ns = __builtin_amdgcn_readfirstlane(ns);
-  Ls = __builtin_amdgcn_readfirstlane(Ls);
-  cs = __builtin_amdgcn_readfirstlane(cs);
-  if (ns == 0) return;   // unreachable: r < N
-
-  int pos = begin;
-  for (bool first = true;; first = false) {
-    const int pair0 = g * N + cs;                  // order position of the pair's unit 0
-    const int j0 = pos - pair0;
-    const int j1 = end - pair0 < ns ? end - pair0 : ns;
-    const int piece = w - pair0 / q;               // runs are numbered by position / q
-    const int nparts = (pair0 + ns - 1) / q - pair0 / q + 1;
-    if (!first) __syncthreads();                   // the last piece's merge has read the tiles
-    const int tok0 = j0 * U;
-    const int tok1 = j1 * U < Ls ? j1 * U : Ls;
-    attend_piece<BT, G, NW, DEPTH, NT>(a, s, g, tok0, tok1 - tok0, nparts, piece);
-    if (j1 == ns && threadIdx.x == 0 &&
-        PA_IN_BOUNDS(kBsPartial, s * a.Hkv + g < a.S * a.Hkv && nparts <= a.Pmax))
-      a.part_np[s * a.Hkv + g] = nparts;
-    pos = pair0 + j1;
-    if (pos >= end) break;
-    // the next pair in the order with at least one unit
-    do {
-      cs += ns;
-      if (++s == a.S) {
-        s = 0;
-        cs = 0;
-        if (++g == a.Hkv) return;   // unreachable: pos < end <= total
-      }
-      // a load after the kernel's stores: the compiler cannot see it uniform
-      Ls = __builtin_amdgcn_readfirstlane(clamped_len(a, s, B, cap));
-      ns = (Ls + U - 1) / U;
-    } while (ns == 0);
-  }
-}
-
-// Workgroups of `kernel` (NW * 64 threads) the current device holds at once,
-// rounded down to a multiple of 8; measured once per device.
-template <class K>
-int resident_workgroups(K kernel, int threads) {
-  static std::atomic<int> cached[kMaxDevices];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = -1;
-  if (dev >= 0) {
-    const int c = cached[dev].load(std::memory_order_relaxed);
-    if (c > 0) return c;
-  }
-  int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) !=
-          hipSuccess)
-    return 0;
-  int n = per_cu * cus / 8 * 8;
-  if (n < 8) n = 8;
-  if (dev >= 0) cached[dev].store(n, std::memory_order_relaxed);
-  return n;
+  even_split_walk<NW * 64>(
+      a, BT > 0 ? BT : a.B,
+      [&](int s, int g, int /*L*/, int tok0, int len, int nparts, int p) {
+        attend_piece<BT, G, NW, DEPTH, NT>(a, s, g, tok0, len, nparts, p);
+      },
+      [&](int s) {
+        for (int g = 0; g < a.Hkv; ++g) zero_heads<G, NW>(a, s, g);
+      });
 }
 
 template <int BT, int G>
@@ -593,11 +464,8 @@ hipError_t launch_bt(const DecodeArgs& a, hipStream_t stream) {
   constexpr int NW = PA_MFMA_WAVES;
   if (a.part_np) {
     auto kernel = decode_mfma_even_kernel<BT, G, NW, PA_MFMA_DEPTH, kDecodeNontemporal>;
-    const int resident = resident_workgroups(kernel, NW * 64);
-    if (resident <= 0) return hipErrorInvalidValue;
-    // no more runs than the minimum run length leaves units for
-    const int64_t most = ((int64_t)a.S * a.Hkv * (a.Pmax - 1) + 7) / 8 * 8;
-    const int64_t grid = most < resident ? most : resident;
+    const int64_t grid = even_split_grid(a, kernel, NW * 64);
+    if (grid <= 0) return hipErrorInvalidValue;
     kernel<<<(unsigned)grid, NW * 64, 0, stream>>>(a);
     return hipGetLastError();
   }

@@ -121,9 +121,14 @@ def test_workspace_and_partition_sizing(lib):
     assert ps(1, 1, 1, 32, 100, 48) == 48        # partitions may start inside a block
     P = ps(16, 32, 32, 32, 4096, 0)
     assert P % 32 == 0
-    assert ws(16, 32, 32, 128, 32, 4096, 512) == 16 * 32 * 8 * 130 * 4
+    # more partitions than one round of the vector kernel's resident
+    # workgroups (2,048) are split evenly: one more piece per sequence and a
+    # piece count per (sequence, KV head)
+    assert ws(16, 32, 32, 128, 32, 4096, 512) == 16 * 32 * 9 * 130 * 4 + 16 * 32 * 4
+    assert ws(16, 32, 32, 128, 32, 4096, 1024) == 16 * 32 * 4 * 130 * 4   # 2,048: one round
     assert ws(2, 4, 4, 128, 16, 48, 0) == 0              # one partition: no workspace
     assert ws(2, 4, 4, 128, 16, 48, 16) == 2 * 4 * 3 * 130 * 4
+    assert ws(1025, 4, 4, 128, 16, 48, 16) == 1025 * 4 * 3 * 130 * 4   # over 1024 sequences
 
 
 def test_workspace_size_is_exact_or_zero(lib):
@@ -155,7 +160,11 @@ def test_workspace_of_the_even_split(lib):
     ws = lib.pa_decode_workspace_bytes
     assert ws(128, 32, 8, 128, 16, 2500, 0) == 128 * 32 * 4 * 130 * 4 + 128 * 8 * 4
     assert ws(128, 64, 8, 128, 16, 2500, 0) == 128 * 64 * 4 * 130 * 4 + 128 * 8 * 4
-    assert ws(128, 16, 8, 128, 16, 2500, 0) == 128 * 16 * 3 * 130 * 4     # groups of 2
+    # groups of 2 and of 1: 3,072 and 12,288 partitions, more than 2,048
+    assert ws(128, 16, 8, 128, 16, 2500, 0) == 128 * 16 * 4 * 130 * 4 + 128 * 8 * 4
+    assert ws(128, 32, 32, 128, 16, 2500, 0) == 128 * 32 * 4 * 130 * 4 + 128 * 32 * 4
+    # groups of 1 with 1,536 partitions (one round of the vector kernel): no split
+    assert ws(128, 4, 4, 128, 16, 2500, 0) == 128 * 4 * 3 * 130 * 4
     assert ws(1025, 32, 8, 128, 16, 2500, 0) == 1025 * 32 * 3 * 130 * 4   # over 1024 sequences
     assert ws(64, 32, 8, 128, 16, 993, 0) == 0                            # one partition
     # split positions past 32 bits: one piece per partition

@@ -70,9 +70,13 @@ def test_decode_valid_input_is_never_refused(pa, G, B):
         no_violations(pa, f"{c.name} P={P}")
 
 
-def test_even_split_and_static_scratch_are_never_refused(pa):
+@pytest.mark.parametrize("Hq,Hkv", [(32, 8), (64, 64)])
+def test_even_split_and_static_scratch_are_never_refused(pa, Hq, Hkv):
+    # groups of 4 (matrix cores) and of 1 (vector kernel; 64 KV heads give it
+    # enough partitions to take the split)
     pa.pa_debug_bounds_violations()
-    c = W.make_case("dbg_even", 7100, [0, 900, 33, 1500, 1, 260, 0, 640], Hq=32, Hkv=8, B=16)
+    c = W.make_case(f"dbg_even_{Hq}_{Hkv}", 7100, [0, 900, 33, 1500, 1, 260, 0, 640], Hq=Hq, Hkv=Hkv,
+                    B=16)
     ref = oracle.decode(c.query, c.k_pool, c.v_pool, c.block_tables, c.context_lens, c.scale)
     say(c.name, "debug build, even split and static scratch")
     assert_attention_close(decode(pa, c, P=64), ref, c.name)

@@ -1,6 +1,7 @@
-"""Parity of grouped-head decode when the batch's work is split evenly over the
-resident workgroups (groups of 4 and 8 query heads whose sequences span more
-than one partition). Runs of equal length then start and end anywhere inside
+"""Parity of decode when the batch's work is split evenly over the resident
+workgroups (any group size, once sequences span more than one partition; the
+vector kernel for groups of 1 and 2 query heads, the matrix-core kernel for 4
+and 8). Runs of equal length then start and end anywhere inside
 a sequence and may cover several (sequence, KV head) pairs, so these cases aim
 at the run boundaries: empty sequences between others, sequences of one unit,
 one long sequence among many short ones (many pieces for one sequence), and
@@ -23,6 +24,14 @@ D = 128
 @pytest.fixture(scope="module")
 def pa():
     return pa_module()
+
+
+def kv_heads(G, few):
+    """KV heads for a case: `few` for groups of 4 and 8; for one or two query
+    heads per KV head 64, so that the small batches here still have more
+    partitions than one round of the vector kernel's resident workgroups, the
+    size from which that kernel takes the split."""
+    return few if G >= 4 else 64
 
 
 def split_engaged(pa, c, P):
@@ -50,16 +59,17 @@ def run_and_check(pa, c, P, workspace=None, expect_split=True):
 
 
 @pytest.mark.parametrize("B", [8, 16, 32])
-@pytest.mark.parametrize("G", [4, 8])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
 @pytest.mark.parametrize("P", [16, 64, 256])
 def test_mixed_lengths_with_empty_sequences(pa, G, B, P):
     lens = [0, 1, 15, 16, 17, P - 1, P, P + 1, 0, 3 * P + 5, 40, 0, 700, 1, 2 * P]
     lens = [max(0, L) for L in lens]
-    c = W.make_case(f"even_G{G}_B{B}_P{P}", 6000 + G + B + P, lens, Hq=4 * G, Hkv=4, B=B)
+    Hkv = kv_heads(G, 4)
+    c = W.make_case(f"even_G{G}_B{B}_P{P}", 6000 + G + B + P, lens, Hq=Hkv * G, Hkv=Hkv, B=B)
     run_and_check(pa, c, P)
 
 
-@pytest.mark.parametrize("G", [4, 8])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
 def test_one_long_sequence_among_many_short(pa, G):
     # the long sequence is cut into many pieces, short ones share runs
     lens = [20] * 60 + [5000] + [33] * 40
@@ -67,7 +77,7 @@ def test_one_long_sequence_among_many_short(pa, G):
     run_and_check(pa, c, 64)
 
 
-@pytest.mark.parametrize("G", [4, 8])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
 def test_eight_kv_heads_across_xcds(pa, G):
     # 8 KV heads: each XCD's eighth of the runs is about one head
     rng = np.random.default_rng(61 + G)
@@ -96,10 +106,11 @@ def test_back_to_back_calls_share_one_workspace(pa):
     assert np.array_equal(a1.view(np.uint16), a2.view(np.uint16))
 
 
-@pytest.mark.parametrize("G", [4, 8])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
 def test_relabelling_physical_blocks_is_bit_identical_under_the_split(pa, G):
+    Hkv = kv_heads(G, 4)
     c = W.make_case(f"even_relabel_G{G}", 6500 + G, [700, 90, 1023, 5, 2000, 0, 1200],
-                    Hq=4 * G, Hkv=4, B=16)
+                    Hq=Hkv * G, Hkv=Hkv, B=16)
     engaged, _ = split_engaged(pa, c, 256)
     assert engaged
     say(c.name, "relabel")
@@ -114,11 +125,12 @@ def test_relabelling_physical_blocks_is_bit_identical_under_the_split(pa, G):
     assert np.array_equal(base.view(np.uint16), got.view(np.uint16))
 
 
-@pytest.mark.parametrize("Hq", [32, 64])
+@pytest.mark.parametrize("Hq", [8, 16, 32, 64])
 def test_chat_lengths_grouped_heads_full_size_every_output(pa, Hq):
-    """Layer 0 of the batch-128 chat lengths with 8 KV heads (groups of 4 and
-    8) in the benchmark's launch configuration, which takes the even split:
-    every (sequence, head, dimension) of the output against the oracle."""
+    """Layer 0 of the batch-128 chat lengths with 8 KV heads (groups of 1, 2,
+    4 and 8) in the benchmark's launch configuration, which takes the even
+    split: every (sequence, head, dimension) of the output against the
+    oracle."""
     c = W.chat_layer(0, Hq=Hq, Hkv=8)
     engaged, parts = split_engaged(pa, c, 0)
     assert engaged and parts == 3, parts
@@ -139,7 +151,7 @@ def test_random_even_split_shapes(pa, seed):
     # wave), every block size the kernels specialise, partitions of 16 to 1,024
     # tokens, lengths with zeros and unit edges
     rng = np.random.default_rng(6700 + seed)
-    G = int(rng.choice([4, 8]))
+    G = int(rng.choice([1, 2, 4, 8]))
     Hkv = int(rng.choice([1, 2, 4, 8]))
     B = int(rng.choice([8, 16, 32, 48]))
     S = int(rng.choice([3, 65, 300, 1024])) if seed % 3 else 1024

@@ -747,11 +747,11 @@ def other_bytes(c, P):
     even = parts > 1 and c.S <= 1024 and (G >= 4 or c.S * c.Hkv * parts > 2048)
     if even:
         # even split: runs of q units over the (KV head, sequence, unit)
-        # order, one per resident workgroup (4 per compute unit for groups of
-        # 4 and 8, 8 for the vector kernel)
+        # order, one per workgroup of the grid (2 per compute unit, 6 for two
+        # heads per KV head)
         n = -(-L // 16)
         N = int(n.sum())
-        resident = 1024 if G >= 4 else 2048
+        resident = 1536 if G == 2 else 512
         grid = min(resident, -(-c.S * c.Hkv * parts // 8) * 8)
         q = max(-(-N * c.Hkv // grid), P // 16)
         first = (np.arange(c.Hkv)[:, None] * N + (np.cumsum(n) - n)[None, :])

@@ -276,10 +276,12 @@ size_t pa_decode_workspace_bytes(int S, int Hq, int Hkv, int D, int B, int max_c
  * start at the launch anyway), each workgroup serves one partition of one
  * (sequence, KV head). Otherwise the batch's 16-token units, taken in (KV
  * head, sequence, position) order, are cut into equal runs, one per workgroup
- * the GPU holds at once, and each sequence's pieces are merged in the reduce
- * kernel: every workgroup then starts at the launch and none is left running
- * alone at its end. Groups of one and two query heads per KV head run on the vector
- * kernel, groups of four and eight on the matrix cores, either way.
+ * of a grid that the GPU holds at once (two per compute unit, or for two query
+ * heads per KV head as many as fit), and each sequence's pieces are merged in
+ * the reduce kernel: every workgroup then starts at the launch and none is
+ * left running alone at its end. Groups of one and two query heads per KV
+ * head run on the vector kernel, groups of four and eight on the matrix cores,
+ * either way.
  *
  *   out               device fp16 [S][Hq][D], 16-byte aligned, written
  *   query             device fp16 [S][Hq][D], 16-byte aligned

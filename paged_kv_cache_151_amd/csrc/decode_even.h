@@ -10,11 +10,14 @@
 // (KV head, sequence, position) and cut into runs of q consecutive units, one
 // run per workgroup; q is the total over the grid, at least a.P / 16. A
 // workgroup walks its run pair by pair, each pair's part being one piece for
-// the reduce kernel. The grid is the number of workgroups the GPU holds at
-// once, so every run starts at the launch and they all end together: no
-// workgroup starts late behind a long one, which cost grouped heads about a
-// tenth of a launch, and one or two heads per KV head about 1.5 %, in the
-// per-partition grid on the chat lengths. Workgroup b runs on XCD b % 8 and
+// the reduce kernel. Every workgroup of the grid is resident at once (the
+// same number on every compute unit), so every run starts at the launch and
+// they all end together: no workgroup starts late behind a long one, which
+// cost grouped heads about a tenth of a launch, and one or two heads per KV
+// head about 1.5 %, in the per-partition grid on the chat lengths. Fewer,
+// longer runs cut fewer sequences into pieces: two workgroups per compute
+// unit measured best where the kernel leaves the choice (one query head per
+// KV head, and the matrix-core kernel). Workgroup b runs on XCD b % 8 and
 // takes run (b % 8) * (grid / 8) + b / 8, so each XCD walks one contiguous
 // eighth of the order.
 #pragma once
@@ -49,15 +52,22 @@ int resident_workgroups(K kernel, int threads) {
   return n;
 }
 
-// Grid of an evenly split launch: the resident workgroups, and no more runs
-// than the minimum run length leaves units for. 0 when the occupancy query
-// fails.
+// Grid of an evenly split launch: per_cu workgroups per compute unit, at most
+// the resident ones, a multiple of 8, and no more runs than the minimum run
+// length leaves units for. 0 when a device query fails.
 template <class K>
-int64_t even_split_grid(const DecodeArgs& a, K kernel, int threads) {
+int64_t even_split_grid(const DecodeArgs& a, K kernel, int threads, int per_cu) {
   const int resident = resident_workgroups(kernel, threads);
   if (resident <= 0) return 0;
+  int cus = 0, dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  int64_t want = (int64_t)per_cu * cus / 8 * 8;
+  if (want < 8) want = 8;
+  if (want > resident) want = resident;
   const int64_t most = ((int64_t)a.S * a.Hkv * (a.Pmax - 1) + 7) / 8 * 8;
-  return most < resident ? most : resident;
+  return most < want ? most : want;
 }
 
 // Clamped context length of sequence s: within the table and the launch.

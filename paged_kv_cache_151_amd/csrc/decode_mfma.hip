@@ -464,7 +464,9 @@ hipError_t launch_bt(const DecodeArgs& a, hipStream_t stream) {
   constexpr int NW = PA_MFMA_WAVES;
   if (a.part_np) {
     auto kernel = decode_mfma_even_kernel<BT, G, NW, PA_MFMA_DEPTH, kDecodeNontemporal>;
-    const int64_t grid = even_split_grid(a, kernel, NW * 64);
+    // two workgroups per CU: 0.7 % faster for groups of 8 on the chat lengths
+    // than the four resident ones, groups of 4 within noise
+    const int64_t grid = even_split_grid(a, kernel, NW * 64, 2);
     if (grid <= 0) return hipErrorInvalidValue;
     kernel<<<(unsigned)grid, NW * 64, 0, stream>>>(a);
     return hipGetLastError();

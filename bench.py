@@ -728,8 +728,8 @@ def main():
         res["stream_read"] = {"GBs": stream["GBs"], "workgroups": stream["workgroups"],
                               "decode_vs_stream": round(achieved / stream["GBs"], 4),
                               "what": "pa_stream_read: one linear pass over this run's K/V pools "
-                                      "(8 16-byte loads in flight per lane, nt + sc1), best of 3 "
-                                      "launch shapes"}
+                                      "(8 16-byte loads in flight per lane, nt + sc1), best of 6 "
+                                      "launch shapes (512 to 16,384 workgroups of 256 threads)"}
     print(json.dumps(res), flush=True)
 
 
@@ -785,7 +785,7 @@ def stream_ceiling(pa, steps_inputs):
         return None
     sink = torch.zeros(4, dtype=torch.int32, device="cuda")
     best = None
-    for wg in (4096, 8192, 16384):
+    for wg in (512, 1024, 2048, 4096, 8192, 16384):   # 2 to 64 workgroups of 4 waves per CU
         for b in bufs:
             pa.pa_stream_read(b, sink, wg)
         torch.cuda.synchronize()

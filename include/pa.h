@@ -223,9 +223,12 @@ pa_status pa_swap_blocks(void* dst_k_pool, void* dst_v_pool, const void* src_k_p
 /*
  * pa_decode_partition_size — the context partition (in tokens) pa_decode uses
  * for these sizes: partition_size itself when positive, otherwise the
- * library's choice (1024 tokens, halved while the launch would have fewer
- * workgroups than the GPU has compute units, down to 64). Returns -1 for invalid arguments (B <= 0, partition_size < 0
- * or not a multiple of 16).
+ * library's choice: 1024 tokens, halved while the launch would have fewer
+ * workgroups than the GPU has compute units (256), down to 64; then, when the
+ * call does not split its work evenly and S * Hkv * ceil(max_context_len / P)
+ * is at least 1024, doubled while P < max_context_len and the doubled size
+ * still gives at least 512 workgroups. Returns -1 for invalid arguments
+ * (B <= 0, partition_size < 0 or not a multiple of 16).
  */
 int pa_decode_partition_size(int S, int Hq, int Hkv, int B, int max_context_len,
                              int partition_size);

@@ -406,11 +406,21 @@ int pa_decode_partition_size(int S, int Hq, int Hkv, int B, int max_context_len,
   // beats 512 by 20 %; for 8 sequences of at most 853 tokens x 32 heads one
   // partition takes 19.3 us against 20.6 at 256 tokens; for one sequence of
   // 4000 tokens x 32 heads 512 tokens take 17.5 us against 20.3 at 128.
-  (void)Hq;
+  // When such a call would not split its work evenly and its partitions fill
+  // at least four workgroups per compute unit, P is doubled while they still
+  // fill two: fewer, longer partitions, and none at all to merge once P covers
+  // every sequence. For 16 sequences of 4096 tokens x 32 heads, one partition
+  // per sequence (512 workgroups, no reduce) takes 164.6 us against 168.0 at
+  // 1024 tokens and 167.0 at 2048 (one process alternating the sizes).
   int P = 1024;
   const int64_t units = (int64_t)(S > 0 ? S : 1) * (Hkv > 0 ? Hkv : 1);
   const int maxL = max_context_len > 0 ? max_context_len : 1;
   while (P > 4 * U && units * ceil_div(maxL, P) < pa::kComputeUnits) P /= 2;
+  const int64_t parts = ceil_div(maxL, P);
+  if (!pa::decode_even_split(S, Hq, Hkv, P, parts) && units * parts >= 4 * pa::kComputeUnits) {
+    while (P < maxL && P <= (1 << 29) && units * ceil_div(maxL, 2 * P) >= 2 * pa::kComputeUnits)
+      P *= 2;
+  }
   return P;
 }
 

@@ -163,9 +163,12 @@ def test_workspace_of_the_even_split(lib):
     # groups of 2 and of 1: 3,072 and 12,288 partitions, more than 2,048
     assert ws(128, 16, 8, 128, 16, 2500, 0) == 128 * 16 * 4 * 130 * 4 + 128 * 8 * 4
     assert ws(128, 32, 32, 128, 16, 2500, 0) == 128 * 32 * 4 * 130 * 4 + 128 * 32 * 4
-    # groups of 1 with 1,536 partitions (one round of the vector kernel): no split
-    assert ws(128, 4, 4, 128, 16, 2500, 0) == 128 * 4 * 3 * 130 * 4
-    assert ws(1025, 32, 8, 128, 16, 2500, 0) == 1025 * 32 * 3 * 130 * 4   # over 1024 sequences
+    # groups of 1 with 1,536 partitions (within one round of the vector kernel):
+    # no split, and the default size grows to one partition per sequence
+    assert ws(128, 4, 4, 128, 16, 2500, 0) == 0
+    assert ws(128, 4, 4, 128, 16, 2500, 1024) == 128 * 4 * 3 * 130 * 4
+    assert ws(1025, 32, 8, 128, 16, 2500, 1024) == 1025 * 32 * 3 * 130 * 4  # over 1024 sequences
+    assert ws(1025, 32, 8, 128, 16, 2500, 0) == 0   # ... where the default covers each in one
     assert ws(64, 32, 8, 128, 16, 993, 0) == 0                            # one partition
     # split positions past 32 bits: one piece per partition
     assert ws(1024, 32, 8, 128, 16, 1 << 22, 16) == 1024 * 32 * (1 << 18) * 130 * 4
@@ -185,18 +188,23 @@ def test_workspace_of_the_even_split(lib):
 def test_default_partition_keeps_a_workgroup_per_compute_unit(lib):
     # the library's choice: 1024 tokens, halved while the launch (partitions x
     # sequences x KV heads) would have fewer workgroups than the 256 CUs, down
-    # to 64; these are the measured best choices for each batch shape
+    # to 64; without an even split and with at least 1,024 such workgroups,
+    # doubled while P < L and the doubled size still gives 512; these are the
+    # measured best choices for each batch shape
     ps = lib.pa_decode_partition_size
     shapes = [  # S, Hq, Hkv, max_context_len, chosen P
         (1, 32, 32, 1000, 128), (1, 32, 32, 4000, 512), (1, 32, 32, 16000, 1024),
         (4, 32, 32, 2000, 1024), (8, 32, 32, 853, 1024), (8, 32, 8, 2000, 512),
-        (16, 32, 32, 4096, 1024), (128, 32, 32, 2400, 1024), (2, 4, 4, 48, 64)]
+        (16, 32, 32, 4096, 4096), (128, 32, 32, 2400, 1024), (2, 4, 4, 48, 64),
+        (32, 32, 32, 4096, 1024), (16, 32, 32, 3000, 4096), (1100, 32, 32, 2000, 2048)]
     for S, Hq, Hkv, L, want in shapes:
         P = ps(S, Hq, Hkv, 16, L, 0)
         assert P == want, (S, Hq, Hkv, L, P)
         wgs = lambda p: S * Hkv * -(-L // p)
         assert P == 64 or wgs(P) >= 256
-        assert P == 1024 or wgs(2 * P) < 256
+        assert P >= 1024 or wgs(2 * P) < 256
+        if P > 1024:
+            assert wgs(P) >= 512 and wgs(P // 2) >= 1024
 
 
 def test_append_kv_validation(lib):

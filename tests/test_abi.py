@@ -11,7 +11,8 @@ from conftest import ROOT
 from decode_rules import even_split
 
 HEADER = os.path.join(ROOT, "include", "pa.h")
-LIB = os.path.join(ROOT, "paged_kv_cache_151_amd", "libpa.so")
+# PA_ABI_LIB: another build of the same sources (the host-sanitized one, for example)
+LIB = os.environ.get("PA_ABI_LIB") or os.path.join(ROOT, "paged_kv_cache_151_amd", "libpa.so")
 
 PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_ALIGN, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE = range(6)
 

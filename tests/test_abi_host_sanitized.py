@@ -1,11 +1,13 @@
-"""The library's host code under AddressSanitizer (CPU only).
+"""The library's host code under AddressSanitizer and UBSan (CPU only).
 
 The C-ABI layer (argument checks, size arithmetic, error reporting, the block
 manager) is host code. This test builds the library from the same sources with
-build.py's flags plus AddressSanitizer on the host pass only (the device code
+build.py's flags plus AddressSanitizer and UndefinedBehaviorSanitizer (no
+recovery) on the host pass only (the device code
 is built as always), then runs tests/test_abi.py against that build in a
 child process with the sanitizer runtime preloaded: every entry point's
-refusal paths run under it, and any memory error aborts the child.
+refusal paths run under them, and any memory error or undefined behaviour
+aborts the child.
 """
 import glob
 import importlib.util
@@ -42,7 +44,8 @@ def test_abi_refusals_under_host_address_sanitizer(tmp_path):
     if runtime is None:
         pytest.skip("the clang AddressSanitizer runtime was not found")
     lib = tmp_path / "libpa_host_asan.so"
-    cmd = [hipcc, *b.HIP_FLAGS, "-Xarch_host", "-fsanitize=address", "-Xarch_host",
+    cmd = [hipcc, *b.HIP_FLAGS, "-Xarch_host", "-fsanitize=address,undefined", "-Xarch_host",
+           "-fno-sanitize-recover=all", "-Xarch_host",
            "-fno-omit-frame-pointer", "-shared-libsan", "-I", os.path.join(ROOT, "include"),
            "-I", os.path.join(PKG, "csrc"), *b.sources(), "-o", str(lib)]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -51,6 +54,6 @@ def test_abi_refusals_under_host_address_sanitizer(tmp_path):
     r = subprocess.run([sys.executable, "-m", "pytest", os.path.join(ROOT, "tests", "test_abi.py"),
                         "-q", "-p", "no:cacheprovider"], capture_output=True, text=True, env=env,
                        cwd=ROOT, timeout=600)
-    assert r.returncode == 0 and "AddressSanitizer" not in r.stderr, (r.stdout[-3000:] +
+    assert r.returncode == 0 and "Sanitizer" not in r.stderr and "runtime error" not in r.stderr, (r.stdout[-3000:] +
                                                                       r.stderr[-3000:])
     assert " passed" in r.stdout, r.stdout[-3000:]

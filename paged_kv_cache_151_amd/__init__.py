@@ -151,10 +151,15 @@ def _same_shape(a, b, names):
 _F16, _I32, _I64 = torch.float16, torch.int32, torch.int64
 
 
-def _rows(t, name, n, fn):
+def _rows(t, name, n, fn, ndim=1):
     """The kernels index these arrays by sequence or token: fewer rows than the
-    sizes passed to the library would be read past their end."""
-    if t is not None and (t.dim() == 0 or t.shape[0] != n):
+    sizes passed to the library would be read past their end, and an index
+    vector with extra dimensions would be misread as a flat one."""
+    if t is None:
+        return
+    if t.dim() != ndim:
+        raise ValueError(f"{fn}: {name} must have {ndim} dimension(s), got {tuple(t.shape)}")
+    if t.shape[0] != n:
         raise ValueError(f"{fn}: {name} needs {n} rows, has {tuple(t.shape)}")
 
 
@@ -214,6 +219,7 @@ def pa_debug_bounds_violations():
 def pa_slot_mapping(block_tables, block_size: int, num_blocks: int, context_lens=None,
                     seq_ids=None, positions=None, out=None, stream=None):
     """int64 slots for new tokens (see pa_slot_mapping in include/pa.h)."""
+    _dims(block_tables, 2, "block_tables", "pa_slot_mapping")
     S, MB = block_tables.shape
     T = positions.shape[0] if positions is not None else (
         seq_ids.shape[0] if seq_ids is not None else S)
@@ -233,6 +239,8 @@ def pa_slot_mapping(block_tables, block_size: int, num_blocks: int, context_lens
 
 def pa_write_kv(key, value, k_pool, v_pool, slot_mapping, stream=None):
     """Scatter key/value [T, Hkv, D] into the pools [NB, Hkv, B, D] at their slots."""
+    _dims(key, 3, "key", "pa_write_kv")
+    _dims(k_pool, 4, "k_pool", "pa_write_kv")
     T, Hkv, D = key.shape
     NB, _, B, _ = k_pool.shape
     _same_shape(key, value, "key/value")
@@ -276,6 +284,7 @@ def pa_append_kv(key, value, k_pool, v_pool, block_tables, context_lens=None, se
 
 def pa_copy_blocks(k_pool, v_pool, block_mapping, stream=None):
     """Copy whole blocks src -> dst for each row of block_mapping [n, 2] (int32)."""
+    _dims(k_pool, 4, "k_pool", "pa_copy_blocks")
     NB, Hkv, B, D = k_pool.shape
     _pairs(block_mapping, "pa_copy_blocks")
     n = block_mapping.shape[0]
@@ -289,6 +298,8 @@ def pa_swap_blocks(dst_k_pool, dst_v_pool, src_k_pool, src_v_pool, block_mapping
     """Copy block src of the source pools to block dst of the destination pools for each row
     (src, dst) of block_mapping [n, 2] (int32, on the device). Pools are device tensors or
     pinned host tensors (pin_memory=True)."""
+    _dims(src_k_pool, 4, "src_k_pool", "pa_swap_blocks")
+    _dims(dst_k_pool, 4, "dst_k_pool", "pa_swap_blocks")
     NB_src, Hkv, B, D = src_k_pool.shape
     NB_dst = dst_k_pool.shape[0]
     _pairs(block_mapping, "pa_swap_blocks")
@@ -331,7 +342,7 @@ def pa_decode(query, k_pool, v_pool, block_tables, context_lens, max_context_len
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _same_shape(out, query, "out/query")
     _same_shape(k_pool, v_pool, "k_pool/v_pool")
-    _rows(block_tables, "block_tables", S, "pa_decode")
+    _rows(block_tables, "block_tables", S, "pa_decode", ndim=2)
     _rows(context_lens, "context_lens", S, "pa_decode")
     _check("pa_decode", _lib.pa_decode(
         _arg(out, "out", _F16), _arg(query, "query", _F16), _arg(k_pool, "k_pool", _F16),
@@ -360,7 +371,7 @@ def pa_decode_static(query, k_pool, v_pool, block_tables, context_lens, max_cont
     if out is None:
         out = torch.empty_like(query)
     _same_shape(out, query, "out/query")
-    _rows(block_tables, "block_tables", S, "pa_decode_static")
+    _rows(block_tables, "block_tables", S, "pa_decode_static", ndim=2)
     _rows(context_lens, "context_lens", S, "pa_decode_static")
     _check("pa_decode_static", _lib.pa_decode_static(
         _arg(out, "out", _F16), _arg(query, "query", _F16), _arg(k_pool, "k_pool", _F16),

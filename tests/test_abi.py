@@ -369,6 +369,18 @@ def test_binding_refuses_arrays_shorter_than_the_sizes_it_passes():
                            positions=torch.zeros(5, dtype=i32))
     with pytest.raises(ValueError, match="context_lens needs 2 rows"):
         pa.pa_slot_mapping(tables, 16, 8, context_lens=torch.zeros(1, dtype=i32))
+    # index vectors with extra dimensions would be read as flat arrays
+    with pytest.raises(ValueError, match="context_lens must have 1 dimension"):
+        pa.pa_decode(q, pool, pool, torch.zeros(3, 4, dtype=i32), torch.zeros(3, 2, dtype=i32), 48, 0.1)
+    with pytest.raises(ValueError, match="seq_ids must have 1 dimension"):
+        pa.pa_slot_mapping(tables, 16, 8, seq_ids=torch.zeros(5, 1, dtype=i32),
+                           positions=torch.zeros(5, dtype=i32))
+    with pytest.raises(ValueError, match="k_pool must have 4 dimensions"):
+        pa.pa_copy_blocks(pool[0], pool[0], torch.zeros(2, 2, dtype=i32))
+    with pytest.raises(ValueError, match="key must have 3 dimensions"):
+        pa.pa_write_kv(key[0], key[0], pool, pool, torch.zeros(5, dtype=i64))
+    with pytest.raises(ValueError, match="src_k_pool must have 4 dimensions"):
+        pa.pa_swap_blocks(pool, pool, pool[0], pool[0], torch.zeros(2, 2, dtype=i32))
     buf = torch.zeros(1024, dtype=torch.uint8)
     with pytest.raises(ValueError, match="outside the buffer"):
         pa.pa_stream_read(buf, torch.zeros(1, dtype=i32), nbytes=2048)

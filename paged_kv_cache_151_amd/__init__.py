@@ -429,6 +429,14 @@ def _np_ptr(a):
     return None if a is None else a.ctypes.data
 
 
+def _seq_ids(seq_ids, fn):
+    """Sequence ids as a contiguous int32 vector: the library reads n ints."""
+    ids = _np.ascontiguousarray(seq_ids, dtype=_np.int32)
+    if ids.ndim != 1:
+        raise ValueError(f"{fn}: seq_ids must be a 1-D list of ids, got shape {ids.shape}")
+    return ids
+
+
 class BlockManager:
     """Owner of one native pa_block_manager; every method is one pa_bm_* call."""
 
@@ -463,7 +471,7 @@ class BlockManager:
     def append_tokens(self, seq_ids):
         """One token per listed sequence. Returns (slots int64 [n], copy pairs int32 [k, 2]).
         Raises PaError (with .n_applied) when the pool is exhausted mid-batch."""
-        ids = _np.ascontiguousarray(seq_ids, dtype=_np.int32)
+        ids = _seq_ids(seq_ids, "append_tokens")
         n = len(ids)
         slots = _np.empty(n, dtype=_np.int64)
         pairs = _np.empty((max(n, 1), 2), dtype=_np.int32)
@@ -495,7 +503,7 @@ class BlockManager:
 
     def export(self, seq_ids, MB: int):
         """pa_decode inputs for a batch: (block_tables int32 [n, MB], context_lens int32 [n])."""
-        ids = _np.ascontiguousarray(seq_ids, dtype=_np.int32)
+        ids = _seq_ids(seq_ids, "export")
         tables = _np.empty((len(ids), MB), dtype=_np.int32)
         lens = _np.empty(len(ids), dtype=_np.int32)
         _check("pa_bm_export", _lib.pa_bm_export(self._h, _np_ptr(ids), len(ids), _np_ptr(tables),

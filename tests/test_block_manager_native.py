@@ -104,6 +104,10 @@ def test_exhaustion_applies_a_prefix_and_bad_ids_are_rejected(pa):
     capped.append_tokens([s] * 4)
     with pytest.raises(pa.PaError, match="PA_ERR_STATE"):
         capped.append_tokens([s])
+    with pytest.raises(ValueError, match="1-D list of ids"):   # would be read as a flat list
+        capped.append_tokens([[s, s]])
+    with pytest.raises(ValueError, match="1-D list of ids"):
+        capped.export([[s]], 4)
 
 
 def _run_random(pa, seed, n_ops=400, NB=40, B=4):

@@ -99,3 +99,53 @@ def test_prefill_step_replays_bit_identical(pa):
         out.fill_(7.0)
         g.replay()
         assert np.array_equal(u16(host(out)), u16(eager)), f"replay {r}"
+
+
+def test_static_decode_step_replays_bit_identical(pa):
+    """pa_decode_static inside a captured graph: its partials live in the
+    library's per-GPU scratch array, so the captured step allocates nothing.
+    Before every replay an eager call on other inputs rewrites that scratch;
+    each replay must still equal the eager step bit for bit (the kernels read
+    only partials they wrote in the same call)."""
+    import torch
+    c = _grouped_case()
+    other = W.make_case("graph_static_other", 8101, [1900, 5, 640], Hq=32, Hkv=8, B=16)
+    say(c.name, "static decode step in a graph")
+    P = 256
+    for d in (c, other):
+        need = pa.pa_decode_workspace_bytes(d.S, d.Hq, d.Hkv, d.D, d.B, d.max_context_len, P)
+        assert 0 < need <= pa.pa_decode_static_scratch_bytes()
+    kp, vp = dev(c.k_pool), dev(c.v_pool)
+    tables, lens = dev(c.block_tables), dev(c.context_lens)
+    q, k_new, v_new = dev(c.query), dev(c.key_new), dev(c.value_new)
+    slots = torch.empty(c.S, dtype=torch.int64, device="cuda")
+    out = torch.empty_like(q)
+
+    def step():
+        pa.pa_append_kv(k_new, v_new, kp, vp, tables, context_lens=lens, slot_mapping=slots)
+        pa.pa_decode_static(q, kp, vp, tables, lens, c.max_context_len, c.scale, partition_size=P,
+                            out=out)
+
+    step()
+    eager = host(out).copy()
+    ref_slots = oracle.decode_slots(c.block_tables, c.context_lens, c.B, c.NB)
+    ref = oracle.decode(c.query, *oracle.write_kv(c.k_pool, c.v_pool, c.key_new, c.value_new,
+                                                  ref_slots),
+                        c.block_tables, c.context_lens, c.scale)
+    assert_attention_close(eager, ref, "eager static decode")
+    o_args = (dev(other.query), dev(other.k_pool), dev(other.v_pool), dev(other.block_tables),
+              dev(other.context_lens))
+    o_out = torch.empty_like(o_args[0])
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for r in range(3):
+        out.zero_()
+        slots.fill_(-1)
+        pa.pa_decode_static(*o_args, other.max_context_len, other.scale, partition_size=P,
+                            out=o_out)   # other partials into the same scratch
+        torch.cuda.synchronize()
+        g.replay()
+        assert np.array_equal(u16(host(out)), u16(eager)), f"replay {r}"
+        assert np.array_equal(host(slots), ref_slots)

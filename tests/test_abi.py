@@ -430,3 +430,28 @@ def test_static_decode_refuses_partials_beyond_its_scratch(lib):
     assert b"static scratch" in lib.pa_last_error()
     assert lib.pa_decode_static(None, v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(FAKE), 2, 4, 4, 128,
                                 16, 16, 3, 48, F(0.1), 0, None) == PA_ERR_NULL
+
+
+def test_error_details_are_per_thread(lib):
+    # the library's only state is a thread-local error string: threads whose
+    # calls fail at the same time each read back their own detail (ctypes
+    # releases the interpreter lock around foreign calls, so they interleave)
+    import threading
+    v = ctypes.c_void_p
+    bad = []
+
+    def worker(k):
+        for i in range(3000):
+            T = -(1000 * k + i % 997) - 1
+            st = lib.pa_write_kv(v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(FAKE), T, 2, 128, 16, 8, None)
+            msg = lib.pa_last_error().decode()
+            if st != PA_ERR_SHAPE or f"T={T} " not in msg:
+                bad.append((k, i, st, msg))
+                return
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not bad, bad[:3]

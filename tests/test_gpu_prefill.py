@@ -230,3 +230,25 @@ def test_long_prompt_after_long_cached_prefix_sampled(pa):
             g = h // (c.Hq // c.Hkv)
             want[i, h] = oracle.attend(c.query[j, h], K[g, :p + 1], V[g, :p + 1], c.scale)
     assert_attention_close(got[rows], want, c.name)
+
+
+@pytest.mark.parametrize("G", [1, 4])
+def test_many_short_chunks(pa, G):
+    # 300 sequences of 1-40 new tokens after cached prefixes of 0-600: many
+    # small work items (one row block each) spread over the XCD ranges
+    rng = np.random.default_rng(3500 + G)
+    new = [int(x) for x in rng.integers(1, 41, 300)]
+    cached = [int(x) for x in rng.integers(0, 601, 300)]
+    c = W.make_prefill_case(f"short_chunks_G{G}", 3510 + G, new, cached, Hq=2 * G, Hkv=2, B=16)
+    check(pa, c)
+
+
+def test_one_new_token_per_sequence_is_decode(pa):
+    # prefill with a single new token per sequence attends exactly like decode
+    # over the same cache (the new token at position L - 1)
+    rng = np.random.default_rng(3520)
+    cached = [int(x) for x in rng.integers(0, 900, 200)]
+    c = W.make_prefill_case("one_token_each", 3521, [1] * 200, cached, Hq=8, Hkv=2, B=16)
+    check(pa, c)
+    dec = oracle.decode(c.query, c.k_pool, c.v_pool, c.block_tables, c.context_lens, c.scale)
+    assert_attention_close(run(pa, c), dec, "prefill of one token against decode")

@@ -1,4 +1,4 @@
-// Host-only driver for the native block manager under AddressSanitizer and
+// Host-only test program for the native block manager under AddressSanitizer and
 // UndefinedBehaviorSanitizer (built with g++ by tests/test_block_manager_sanitized.py,
 // together with csrc/block_manager.cpp; no GPU code).
 //
